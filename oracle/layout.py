@@ -1,0 +1,130 @@
+"""Partition of the flat parameter vector over N simulated ranks.
+
+Test infrastructure only (see the package header).
+
+* Stages 0-2 ("The four schemes", ``Base.__init__``; "ZeRO and FSDP",
+  ``ZeroAdam.__init__``): the vector of Psi elements is split into N equal
+  contiguous shards, rank r owning [r*S, (r+1)*S).  The prototype refuses a
+  Psi that N does not divide; ``ZeroAdam`` pads with zeros to N*ceil(Psi/N).
+  Both readings are offered: ``pad=False`` raises, ``pad=True`` pads.
+* Stage 3 ("ZeRO and FSDP", "ZeRO-3 and FSDP"): the model is cut into units
+  (a layer or a few) and each unit is split N ways on its own, with its own
+  zero pad; rank r owns [Q_u + r*S_u, Q_u + (r+1)*S_u) of the padded vector,
+  where Q_u is the padded start of unit u.  Data parallel keeps no shard: the
+  rank's "owned" range is the whole vector.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+
+class IndivisibleError(ValueError):
+    """Psi (or a ZeRO-3 unit) does not divide by N and padding was not asked for."""
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+@dataclass(frozen=True)
+class Layout:
+    numel: int                  # Psi, true parameter count
+    world: int                  # N
+    stage: int                  # 0 = data parallel, 1, 2, 3
+    units: tuple                # true element count of each unit
+    pad: bool
+    shard_u: tuple              # S_u per unit (stage 3); (S,) for stages 1-2; (Psi,) for DP
+    unit_start: tuple           # true start P_u of each unit in [0, Psi)
+    unit_pstart: tuple          # padded start Q_u of each unit
+
+    @property
+    def n_units(self) -> int:
+        return len(self.units)
+
+    @property
+    def padded_numel(self) -> int:
+        if self.stage == 0:
+            return self.numel
+        return sum(self.world * s for s in self.shard_u)
+
+    @property
+    def shard_numel(self) -> int:
+        """Elements of optimizer state each rank keeps."""
+        return sum(self.shard_u)
+
+    def owned(self, rank: int, unit: int = 0):
+        """(padded offset, length) of what ``rank`` owns in ``unit``."""
+        if not 0 <= rank < self.world:
+            raise IndexError(rank)
+        if self.stage == 0:
+            if unit != 0:
+                raise IndexError(unit)
+            return 0, self.numel
+        if self.stage in (1, 2):
+            if unit != 0:
+                raise IndexError(unit)
+            s = self.shard_u[0]
+            return rank * s, s
+        s = self.shard_u[unit]
+        return self.unit_pstart[unit] + rank * s, s
+
+    def local_offset(self, unit: int) -> int:
+        """Offset of ``unit``'s piece inside a rank's concatenated shard."""
+        return sum(self.shard_u[:unit])
+
+    def param_index(self, padded_pos: int) -> Optional[int]:
+        """True parameter index held at a padded position, or None for pad."""
+        if self.stage == 0:
+            return padded_pos if 0 <= padded_pos < self.numel else None
+        if self.stage in (1, 2):
+            return padded_pos if padded_pos < self.numel else None
+        for u in range(self.n_units):
+            q, width = self.unit_pstart[u], self.world * self.shard_u[u]
+            if q <= padded_pos < q + width:
+                k = padded_pos - q
+                return self.unit_start[u] + k if k < self.units[u] else None
+        return None
+
+    def padded_to_param(self, positions) -> "tuple":
+        """Vectorised ``param_index``: (param indices, valid mask) for positions."""
+        import numpy as np
+        pos = np.asarray(positions, dtype=np.int64)
+        if self.stage in (0, 1, 2):
+            return pos.copy(), pos < self.numel
+        par = np.zeros_like(pos)
+        ok = np.zeros(pos.shape, dtype=bool)
+        for u in range(self.n_units):
+            q, width = self.unit_pstart[u], self.world * self.shard_u[u]
+            inside = (pos >= q) & (pos < q + width)
+            k = pos - q
+            hit = inside & (k < self.units[u])
+            par = np.where(hit, self.unit_start[u] + k, par)
+            ok |= hit
+        return par, ok
+
+
+def make_layout(numel: int, world: int, stage: int, units: Optional[Sequence[int]] = None,
+                pad: bool = False) -> Layout:
+    if numel < 1 or world < 1 or stage not in (0, 1, 2, 3):
+        raise ValueError("bad numel/world/stage")
+    unit_list: List[int] = list(units) if units else [numel]
+    if any(u < 1 for u in unit_list) or sum(unit_list) != numel:
+        raise ValueError("unit sizes must be positive and sum to numel")
+    starts = [sum(unit_list[:i]) for i in range(len(unit_list))]
+    if stage == 0:
+        shard_u = (numel,)
+    elif stage in (1, 2):
+        if numel % world and not pad:
+            raise IndivisibleError("parameter count must divide by world size")
+        shard_u = (_ceil_div(numel, world),)
+    else:
+        for u in unit_list:
+            if u % world and not pad:
+                raise IndivisibleError("unit size must divide by world size")
+        shard_u = tuple(_ceil_div(u, world) for u in unit_list)
+    if stage == 3:
+        pstarts = tuple(sum(world * s for s in shard_u[:i]) for i in range(len(shard_u)))
+    else:
+        pstarts = tuple(starts)
+    return Layout(numel, world, stage, tuple(unit_list), pad, shard_u, tuple(starts), pstarts)

@@ -1,0 +1,140 @@
+"""Pins of the oracle's accounting and layout against numbers printed on the pages."""
+import os
+import random
+import shlex
+from decimal import ROUND_HALF_UP, Decimal
+
+import pytest
+
+from oracle import accounting as acc
+from oracle.layout import IndivisibleError, make_layout
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_accounting.txt")
+
+
+def load_pins():
+    pins = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tok = shlex.split(line)
+            pins.append(dict(id=tok[0], numel=int(tok[1]), world=int(tok[2]), stage=int(tok[3]),
+                             units=None if tok[4] == "-" else [int(x) for x in tok[4].split(",")],
+                             pad=bool(int(tok[5])), gather_bytes=int(tok[6]), quantity=tok[7],
+                             printed=Decimal(tok[8]), scale=Decimal(tok[9]), decimals=int(tok[10]),
+                             source=" ".join(tok[11:])))
+    return pins
+
+
+def quantity(pin):
+    lay = make_layout(pin["numel"], pin["world"], pin["stage"], pin["units"], pin["pad"])
+    b = acc.bytes_per_rank(lay, gather_bytes=pin["gather_bytes"])
+    q = pin["quantity"]
+    if q == "resident":
+        return Decimal(b.resident)
+    if q == "peak":
+        return Decimal(b.peak)
+    if q == "opt_state":
+        return Decimal(acc.optimizer_state_bytes(lay))
+    if q == "res_per_param":
+        return Decimal(b.resident) / Decimal(pin["numel"])
+    if q == "peak_per_param":
+        return Decimal(b.peak) / Decimal(pin["numel"])
+    if q == "rs_elems":
+        return Decimal(b.rs_elems)
+    if q == "traffic_bytes_x_n_over_psi":
+        return Decimal(b.traffic_bytes) * pin["world"] / ((pin["world"] - 1) * Decimal(pin["numel"]))
+    raise KeyError(q)
+
+
+PINS = load_pins()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p["id"] for p in PINS])
+def test_page_printed_value(pin):
+    got = quantity(pin) / pin["scale"]
+    q = Decimal(1).scaleb(-pin["decimals"])
+    assert got.quantize(q, rounding=ROUND_HALF_UP) == pin["printed"].quantize(q), pin["source"]
+
+
+def test_sixteen_bytes_per_parameter():
+    # "One Poem Suffices: ZeRO" s3.1: 2 + 2 + 3*4 = 16 bytes per parameter
+    assert acc.B_P16 + acc.B_GRAD + acc.B_MASTER + acc.B_M + acc.B_V == 16
+
+
+@pytest.mark.parametrize("numel,world", [(8, 4), (65536, 4), (124439808, 8), (7_500_000_000, 64),
+                                         (1_558_000_000, 16)])
+def test_closed_forms(numel, world):
+    # "ZeRO and FSDP" three-stage table: 16P, 4P + 12P/N, 2P + 14P/N, 16P/N (N | P)
+    res = [acc.bytes_per_rank(make_layout(numel, world, s)).resident for s in range(4)]
+    assert res == [16 * numel, 4 * numel + 12 * numel // world, 2 * numel + 14 * numel // world,
+                   16 * numel // world]
+
+
+@pytest.mark.parametrize("numel,world", [(8, 4), (65536, 4), (7_500_000_000, 64)])
+def test_traffic_ratio_and_exact_forms(numel, world):
+    # "ZeRO, annotated" s7 / "One Poem Suffices: ZeRO" 4.1.4: DP and stages 1-2 move
+    # 2(N-1)/N * Psi, stage 3 3(N-1)/N * Psi; ratio exactly 1.5
+    t = [acc.bytes_per_rank(make_layout(numel, world, s)).traffic_elems for s in range(4)]
+    s = numel // world
+    assert t[0] == t[1] == t[2] == 2 * (world - 1) * s
+    assert t[3] == 3 * (world - 1) * s
+    assert Decimal(t[3]) / Decimal(t[0]) == Decimal("1.5")
+    # the 7.5B example's approximations 15.0e9 and 22.5e9 numbers per GPU
+    if numel == 7_500_000_000:
+        assert t[0] * world // (world - 1) == 15_000_000_000
+        assert t[3] * world // (world - 1) == 22_500_000_000
+
+
+def test_stage3_peak_is_resident_plus_gathered_unit():
+    # "The four schemes": peak - resident is exactly the gathered copy
+    lay = make_layout(65536, 4, 3, [16384] * 4)
+    b = acc.bytes_per_rank(lay)
+    assert b.peak - b.resident == 2 * 16384
+    one = acc.bytes_per_rank(make_layout(65536, 4, 3))
+    assert one.peak - one.resident == 2 * 65536
+    for s in range(3):
+        bs = acc.bytes_per_rank(make_layout(65536, 4, s))
+        assert bs.peak == bs.resident
+
+
+def test_prefetch_peak_two_live_units():
+    lay = make_layout(10 + 20 + 30 + 5, 5, 3, [10, 20, 30, 5])
+    b2 = acc.bytes_per_rank(lay, max_live=2)
+    assert b2.gathered == 2 * (20 + 30)
+    assert acc.bytes_per_rank(lay, max_live=1).gathered == 2 * 30
+
+
+def test_padding_readings():
+    # the prototype refuses an indivisible count; ZeroAdam pads with ceil(Psi/N)
+    with pytest.raises(IndivisibleError):
+        make_layout(19210, 4, 1)
+    lay = make_layout(19210, 4, 1, pad=True)
+    assert lay.shard_u == (4803,) and lay.padded_numel == 19212
+    b = acc.bytes_per_rank(lay)
+    assert b.res_p16 == 2 * 19210 and b.res_grad == 2 * 19210 and b.res_master == 4 * 4803
+    with pytest.raises(IndivisibleError):
+        make_layout(10, 4, 3, [5, 5])
+    lay3 = make_layout(10, 4, 3, [5, 5], pad=True)
+    assert lay3.shard_u == (2, 2) and lay3.padded_numel == 16
+
+
+def test_layout_owned_ranges_tile_the_padded_vector():
+    rnd = random.Random(7)
+    for _ in range(200):
+        world = rnd.randint(1, 9)
+        units = [rnd.randint(1, 50) for _ in range(rnd.randint(1, 5))]
+        numel = sum(units)
+        for stage in (1, 2, 3):
+            lay = make_layout(numel, world, stage, units, pad=True)
+            seen = []
+            for u in range(lay.n_units if stage == 3 else 1):
+                for r in range(world):
+                    off, n = lay.owned(r, u)
+                    seen.extend(range(off, off + n))
+            assert sorted(seen) == list(range(lay.padded_numel))
+            par, ok = lay.padded_to_param(range(lay.padded_numel))
+            assert sorted(par[ok].tolist()) == list(range(numel))
+            assert int(ok.sum()) == numel
