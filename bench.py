@@ -1,0 +1,221 @@
+"""Benchmark of the ZeRO shard step on one MI355X.
+
+Default workload (share64): one rank's share of a 7.5e9-parameter model on 64
+data-parallel ranks -- the fused reduce + Adam + cast over its 117,187,500
+owned elements with 64 bf16 gradient contributions, then the receive of the
+63 peer slices into the full 7.5e9-element bf16 working copy.  One step is
+one pass of the whole path over one batch of synthetic gradients that are
+resident in HBM before timing starts.
+
+Prints one JSON line: params/s (owned fp32 elements updated per second),
+the roofline of the dominant kernel (algorithmic bytes / average launch time
+from HIP events on the launch stream, against 8 TB/s), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload share64|gpt2s|gpt2xl|llama8b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0
+METRIC = "fused ZeRO shard-step params/sec and achieved HBM GB/s (% of peak), 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_reduce_amd", "csrc", "zsmr_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0):
+    """The oracle, untuned, on a window of the rank's shard (all N
+    contributions, T Adam steps and the same window of the 63 peer slices),
+    repeated until at least ``min_seconds`` of CPU work.  Inputs are made
+    before the clock starts; one gradient set serves every step."""
+    import numpy as np
+    import synth
+    from oracle import numerics as nm
+
+    p = np.arange(window, dtype=np.int64)
+    rows16 = [synth.grad16(w.seed, r, 1, p, w.grad_sigma, w.dtype) for r in range(w.world)]
+    peers = np.stack(rows16[1:])          # 63 slices of 16-bit values to copy
+    theta = synth.theta0(w.seed, p)
+    wc = np.zeros((w.world, window), np.uint16)
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < min_seconds:
+        master, m, v = theta.copy(), np.zeros(window, np.float32), np.zeros(window, np.float32)
+        for t in range(1, w.steps + 1):
+            g = nm.reduce_rank_order([nm.widen16(r, w.dtype) for r in rows16])
+            k = nm.adam_consts(w.lr, w.betas[0], w.betas[1], w.eps, t)
+            master, m, v = nm.adam_update(master, m, v, g, k)
+            wc[0] = nm.cast16(master, w.dtype)
+            wc[1:] = peers
+        reps += 1
+        elapsed = time.perf_counter() - t0
+    params = reps * w.steps * window
+    return {"value": params / elapsed, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"window of {window} owned elements of rank 0 (of {117_187_500}), all "
+                      f"{w.world} bf16 contributions, {w.steps} Adam steps + cast + the same "
+                      f"window of the {w.world - 1} peer slices, repeated {reps}x "
+                      f"({elapsed:.1f} s); NumPy single-threaded"}
+
+
+def bench_share64(args, w):
+    import torch
+    import workloads as wl
+    import zero_sharded_mixed_reduce_amd as z
+
+    if args.blocks_per_cu:
+        z.zsmr_set_blocks_per_cu(args.blocks_per_cu)
+    share = wl.RankShare(w, rank=0)
+    share.gen_grads(1)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for t in range(1, args.warmup + 1):
+        share.step(t)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        t = args.warmup + 1 + i
+        ev[i][0].record(stream)
+        share.fused(t)
+        ev[i][1].record(stream)
+        share.receive()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    recv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    S, N = share.S, w.world
+    fused_bytes = S * (2 * N + 26)              # N x 2 B grads, 24 B master/m/v r+w, 2 B cast
+    recv_bytes = (share.P - S) * 4              # 2 B read + 2 B written per peer element
+    parts = {
+        "fused_step": {"ms": round(fused_ms, 4), "bytes": fused_bytes,
+                       "GBps": round(fused_bytes / fused_ms / 1e6, 1),
+                       "frac": round(fused_bytes / fused_ms / 1e6 / PEAK_HBM_GBPS, 4)},
+        "peer_receive": {"ms": round(recv_ms, 4), "bytes": recv_bytes,
+                         "GBps": round(recv_bytes / recv_ms / 1e6, 1),
+                         "frac": round(recv_bytes / recv_ms / 1e6 / PEAK_HBM_GBPS, 4)},
+        "step_GBps": round((fused_bytes + recv_bytes) / ms_step / 1e6, 1),
+    }
+    dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
+    kname = {"fused_step": "step_vec8_kernel", "peer_receive": "copy16_kernel"}[dom]
+    roof = {"bound": "hbm", "achieved": parts[dom]["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": parts[dom]["frac"], "traffic": read_traffic(kname, w.key),
+            "kernel": kname, "algorithmic_bytes_per_launch": parts[dom]["bytes"]}
+    # the hot path's own kernel, reported beside the dominant one
+    roof_fused = {"bound": "hbm", "achieved": parts["fused_step"]["GBps"], "peak": PEAK_HBM_GBPS,
+                  "unit": "GB/s", "frac": parts["fused_step"]["frac"],
+                  "traffic": read_traffic("step_vec8_kernel", w.key)}
+    return S / (ms_step / 1e3), ms_step, roof, roof_fused, parts, {
+        "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "owned_shard": S,
+        "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
+        "rank": 0, "blocks_per_cu": args.blocks_per_cu or 8}
+
+
+def bench_world(args, w):
+    """Simulated-world workloads (all N ranks on the GPU): one step = N fused
+    launches (stages 1-2) or the ZeRO-3 unit schedule (stage 3)."""
+    import torch
+    import workloads as wl
+    import zero_sharded_mixed_reduce_amd as z
+
+    if args.blocks_per_cu:
+        z.zsmr_set_blocks_per_cu(args.blocks_per_cu)
+    stream = torch.cuda.current_stream()
+    if w.stage == 3:
+        world = wl.Stage3World(w)
+    else:
+        world = wl.ShardedWorld(w)
+        world.gen_grads(1)
+    timer = wl.Timer(stream)
+    for t in range(1, args.warmup + 1):
+        world.step(t)
+    torch.cuda.synchronize()
+    timer.reset()
+    for i in range(args.steps):
+        world.step(args.warmup + 1 + i, timer)
+    ms_step = timer.ms() / args.steps
+    N = w.world
+    byts = w.numel * (2 * N + 26) + (8 * w.numel if w.stage == 3 else 0)
+    gbps = byts / ms_step / 1e6
+    roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": read_traffic("step_vec8_kernel", w.key),
+            "kernel": "step_vec8_kernel", "algorithmic_bytes_per_step": byts}
+    return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, {
+        "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
+        "steps_T": w.steps, "lr": w.lr}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="share64")
+    ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the N ranks of the ZeRO world are simulated in "
+              "that GPU's HBM, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = wl.WORKLOADS[args.workload]
+    if args.workload == "share64":
+        value, ms, roof, roof_fused, parts, cfg = bench_share64(args, w)
+    else:
+        value, ms, roof, roof_fused, parts, cfg = bench_world(args, w)
+    torch.cuda.synchronize()
+    line = {"metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": cfg, "roofline": roof}
+    if roof_fused is not None:
+        line["roofline_fused_step"] = roof_fused
+    if parts:
+        line["parts"] = parts
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,238 @@
+/*
+ * zsmr.h -- C ABI of libzsmr.so, the ZeRO shard step on one MI355X (gfx950).
+ *
+ * The library runs the per-rank step of ZeRO data parallelism over a flat
+ * parameter vector of Psi elements for a world of N ranks that is simulated in
+ * one GPU's HBM:
+ *   1. the arithmetic of the gradient reduce-scatter: N 16-bit gradient rows
+ *      summed in fp32 in rank order 0..N-1, then divided by N;
+ *   2. mixed-precision Adam on the rank's fp32 master, m and v shard;
+ *   3. the all-gather side: the updated master cast (round to nearest even)
+ *      into the 16-bit working copy, and copies of peers' 16-bit slices;
+ *   4. ZeRO-3's per-unit gather -> use -> release -> re-gather schedule,
+ *      with exact per-band byte and per-rank traffic accounting for data
+ *      parallel and ZeRO stages 1-3.
+ * Sources: "The four schemes" (the scheme flags table, Base._adam, the
+ * accounting methods and the resident-vs-peak table), "ZeRO and FSDP" (the
+ * three-stage table, ZeroAdam, "ZeRO-3 and FSDP"), "ZeRO, annotated"
+ * (sections 3.1, 5.1-5.3 and 7), "One Poem Suffices: ZeRO" (sections 3.1 and
+ * 4.1, Appendix B) and "Sharding the States.".
+ *
+ * Conventions for every entry point:
+ *  - Return value: ZSMR_OK (0) or one of the ZSMR_ERR_* codes below; no C++
+ *    exception crosses the ABI.  zsmr_strerror() names a code.
+ *  - Device pointers are owned by the caller (the library never allocates
+ *    device memory).  The library allocates only the host-side context.
+ *  - Every device operation is enqueued asynchronously on the caller's
+ *    hipStream_t (0 = the null stream).  Launch failures are returned at once
+ *    (ZSMR_ERR_HIP, text in zsmr_last_hip_error()); faults during execution
+ *    surface at the caller's next synchronisation.
+ *  - Arguments are checked before anything is launched or counted; a call
+ *    that returns an error has no effect.  The caller guarantees that every
+ *    buffer covers the elements the call touches (the library cannot see
+ *    allocation sizes through raw pointers).
+ *  - A context is not thread-safe; calls on one context must be serialised.
+ *  - Element counts and offsets are int64 (the 7.5e9-element working copy and
+ *    the 2.5e10-element gradient set exceed 2^32).
+ *  - fp32 buffers (master, m, v, g, theta0) must be 4-byte aligned; the fast
+ *    path wants 16 bytes.  16-bit buffers must be 2-byte aligned.  Any legal
+ *    alignment works; the kernel variant is chosen from the pointers.
+ */
+#ifndef ZSMR_H
+#define ZSMR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ZSMR_OK              0
+#define ZSMR_ERR_ARG         1  /* null/negative/out-of-range argument        */
+#define ZSMR_ERR_INDIVISIBLE 2  /* Psi or a unit not divisible by N, pad == 0 */
+#define ZSMR_ERR_STATE       3  /* ZeRO-3 gather/release out of order         */
+#define ZSMR_ERR_DTYPE       4  /* unknown 16-bit format code                 */
+#define ZSMR_ERR_ALIGN       5  /* pointer not aligned to its element size    */
+#define ZSMR_ERR_HIP         6  /* a HIP runtime call or launch failed        */
+
+/* 16-bit formats of gradients and of the working copy */
+#define ZSMR_FP16 1
+#define ZSMR_BF16 2
+
+/* schemes ("The four schemes", the three-flag table) */
+#define ZSMR_DP    0  /* nothing sharded; one all-reduce per step          */
+#define ZSMR_ZERO1 1  /* optimizer state sharded                            */
+#define ZSMR_ZERO2 2  /* + gradients sharded                                */
+#define ZSMR_ZERO3 3  /* + parameters sharded, gathered per unit            */
+
+typedef struct zsmr_ctx zsmr_ctx;
+
+/* Adam hyper-parameters, in double; the library rounds each constant of a
+ * step (beta1, 1-beta1, beta2, 1-beta2, 1-beta1^t, 1-beta2^t, lr, eps) to
+ * fp32 once, as the prototype's Python scalars are ("The four schemes",
+ * Base._adam).  Requires lr >= 0, 0 <= beta < 1, eps >= 0, all finite. */
+typedef struct zsmr_adam {
+    double lr, beta1, beta2, eps;
+} zsmr_adam;
+
+/* The partition a context describes. */
+typedef struct zsmr_layout_info {
+    int64_t numel;         /* Psi                                               */
+    int64_t padded_numel;  /* flat length including the zero pad (DP: Psi)      */
+    int64_t shard_numel;   /* elements of optimizer state one rank keeps        */
+    int64_t max_unit_numel;/* largest padded unit N*S_u (stage 3), else padded  */
+    int32_t world, stage, n_units, grad_dtype, param_dtype, pad;
+} zsmr_layout_info;
+
+/* Accounting, bytes per rank ("The four schemes": bytes_per_param and
+ * peak_bytes_per_param; "ZeRO and FSDP": the three-stage table).  Sharded
+ * bands count the padded shard, unsharded bands the true Psi.  Traffic is
+ * the elements one rank sends per step: DP one all-reduce of 2(N-1)
+ * chunks of ceil(Psi/N); stages 1-2 a reduce-scatter plus an all-gather of
+ * (N-1)*S each; stage 3 a reduce-scatter plus two all-gathers of
+ * (N-1)*sum(S_u) each ("ZeRO, annotated" section 7).  Bytes = elements x 2. */
+typedef struct zsmr_bytes {
+    int64_t res_p16, res_grad, res_master, res_m, res_v;
+    int64_t resident;      /* sum of the five bands                             */
+    int64_t gathered;      /* stage 3: bytes of the gathered unit(s) live at once */
+    int64_t peak;          /* resident + gathered                               */
+    int64_t unit_grad;     /* stage 3: full 16-bit gradient of the largest unit */
+    int64_t rs_elems, ag_elems, ar_elems;
+    int64_t traffic_elems, traffic_bytes;
+} zsmr_bytes;
+
+/* What the calls made on a context actually did, for one rank: elements that
+ * rank received through each simulated collective, plus the ZeRO-3 schedule. */
+typedef struct zsmr_counters {
+    int64_t rs_elems, ag_elems, ar_elems;
+    int64_t traffic_elems, traffic_bytes;
+    int64_t stage3_gathers, stage3_releases;   /* summed over units           */
+    int64_t live_units, live_bytes, peak_live_bytes;
+} zsmr_counters;
+
+/* Name of a status code (static storage). */
+const char* zsmr_strerror(int32_t status);
+
+/* Text of the last HIP error seen by this thread, or "" (thread-local). */
+const char* zsmr_last_hip_error(void);
+
+/* Build the partition of Psi = numel elements over `world` ranks (host only).
+ * stage: ZSMR_DP..ZSMR_ZERO3.  grad_dtype/param_dtype: ZSMR_FP16 or ZSMR_BF16.
+ * units: n_units sizes summing to numel (ZeRO-3 splits each unit N ways with
+ * its own pad, "ZeRO and FSDP", "ZeRO-3 and FSDP"); n_units == 0 with
+ * unit_numel == NULL means one unit of numel.  Stages 0-2 ignore the unit
+ * split.  pad == 0: Psi (stage 3: every unit) must divide by world, else
+ * ZSMR_ERR_INDIVISIBLE (the prototype's assertion in "The four schemes");
+ * pad == 1: shards are ceil(./N) and the tail is zero (ZeroAdam in "ZeRO and
+ * FSDP").  Rank r of stages 1-2 owns [r*S, (r+1)*S); of stage 3 owns
+ * [Q_u + r*S_u, Q_u + (r+1)*S_u) of unit u, Q_u its padded start; a data
+ * parallel rank "owns" [0, Psi).  *out receives a context to free with
+ * zero_destroy(). */
+int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
+                         int32_t grad_dtype, int32_t param_dtype, int32_t pad,
+                         const int64_t* unit_numel, int32_t n_units);
+
+/* Free a context (NULL is ignored). */
+void zero_destroy(zsmr_ctx* ctx);
+
+/* Copy the partition's sizes into *out (host only). */
+int32_t zero_layout_info(const zsmr_ctx* ctx, zsmr_layout_info* out);
+
+/* Index map (host only): padded flat offset and length of what `rank` owns
+ * in `unit` (stages 0-2: unit must be 0), and the offset of that piece inside
+ * the rank's own concatenated shard.  Any output pointer may be NULL. */
+int32_t zero_layout(const zsmr_ctx* ctx, int32_t rank, int32_t unit,
+                    int64_t* offset, int64_t* len, int64_t* local_offset);
+
+/* Accounting for one rank (pure, host only).  gather_bytes: bytes per
+ * gathered element of the stage-3 peak (0 = the 16-bit working copy's 2; the
+ * prototype's fp32 gather is 4).  max_live: units gathered at once (0 = 1;
+ * 2 = prefetch of the next unit). */
+int32_t zero_bytes_per_rank(const zsmr_ctx* ctx, int32_t gather_bytes, int32_t max_live,
+                            zsmr_bytes* out);
+
+/* Counters of `rank` accumulated by the calls below since creation or the
+ * last zero_reset_counters() (host only). */
+int32_t zero_counters(const zsmr_ctx* ctx, int32_t rank, zsmr_counters* out);
+int32_t zero_reset_counters(zsmr_ctx* ctx);
+
+/* Device-side init of one (rank, unit) piece of length len = layout len:
+ * master = theta0, m = v = 0, p16 = RNE16(theta0).  theta0 points at the
+ * piece's initial values (fp32, len), p16 at where its 16-bit copy lives. */
+int32_t zero_init_state(const zsmr_ctx* ctx, int32_t rank, int32_t unit, const float* theta0,
+                        float* master, float* m, float* v, void* p16, hipStream_t stream);
+
+/* Gradient layout shared by the reduce entry points: row r (rank r's
+ * 16-bit gradient) starts at grads + r*row_stride elements, and the piece
+ * owned by (rank, unit) starts at column base_elem of every row; the call
+ * reads N rows x len elements.  In a simulated world of full gradient
+ * vectors row_stride is the padded length and base_elem the layout offset;
+ * for one rank's received contributions base_elem is 0. */
+
+/* Reduce only: g_out[j] = (sum over r in order of fp32(G_r[base+j])) / N, or
+ * the raw sum if mean == 0 ("The four schemes", reduce_scatter_mean; "ZeRO
+ * and FSDP", ZeroAdam.step).  fp32 output of len elements. */
+int32_t zero_reduce_shard(zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* grads,
+                          int64_t row_stride, int64_t base_elem, int32_t mean, float* g_out,
+                          hipStream_t stream);
+
+/* Adam only, on n elements ("The four schemes", Base._adam):
+ *   m = b1*m + (1-b1)*g;  v = b2*v + ((1-b2)*g)*g;
+ *   master -= (lr * (m/(1-b1^t))) / (sqrt(v/(1-b2^t)) + eps)
+ * every operation rounded to fp32, no fused multiply-add.  t >= 1. */
+int32_t zero_adam_step(float* master, float* m, float* v, const float* g, int64_t n, int32_t t,
+                       const zsmr_adam* hp, hipStream_t stream);
+
+/* Cast only: p16_dst[j] = RNE16(master[j]) for the (rank, unit) piece -- the
+ * all-gather side of stages 1-2 (into slot r of the working copy) and the
+ * rank's own 16-bit shard at stage 3. */
+int32_t zero_gather_cast(zsmr_ctx* ctx, int32_t rank, int32_t unit, const float* master,
+                         void* p16_dst, hipStream_t stream);
+
+/* The hot path: reduce + Adam + cast in one pass over the (rank, unit)
+ * piece, reading each gradient row, master, m and v once and writing master,
+ * m, v and the 16-bit copy once.  Bit-identical to zero_reduce_shard(mean=1)
+ * + zero_adam_step + zero_gather_cast.  t >= 1 is the step number (the same
+ * for every rank and unit of a step). */
+int32_t zero_fused_step(zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* grads,
+                        int64_t row_stride, int64_t base_elem, float* master, float* m,
+                        float* v, void* p16_dst, int32_t t, const zsmr_adam* hp,
+                        hipStream_t stream);
+
+/* All-gather receive: copy n 16-bit elements src -> dst (peers' slices into
+ * the working copy of recv_rank); counted as all-gather traffic received by
+ * recv_rank.  Overlapping src and dst is not allowed. */
+int32_t zero_gather_copy(zsmr_ctx* ctx, int32_t recv_rank, const void* src, void* dst,
+                         int64_t n, hipStream_t stream);
+
+/* ZeRO-3 schedule ("The four schemes", where the third P comes from; "ZeRO
+ * and FSDP", "ZeRO-3 and FSDP").  Units gathered at once may not exceed
+ * max_live (default 1, i.e. no prefetch; 2 allows gathering unit i+1 while
+ * unit i is live).  Fails with ZSMR_ERR_STATE if units are live. */
+int32_t zero_stage3_set_max_live(zsmr_ctx* ctx, int32_t max_live);
+
+/* Gather unit `unit`: copy the N 16-bit shards shard_ptrs[0..N-1] (a host
+ * array of N device pointers, shard r of S_u elements) into unit_buf (N*S_u
+ * elements, shard r at r*S_u).  ZSMR_ERR_STATE if the unit is already live or
+ * max_live units are live.  Counts one all-gather of (N-1)*S_u elements
+ * received by every rank, and the live/peak gathered bytes. */
+int32_t zero_stage3_unit_gather(zsmr_ctx* ctx, int32_t unit, const void* const* shard_ptrs,
+                                void* unit_buf, hipStream_t stream);
+
+/* Release unit `unit` (host only).  ZSMR_ERR_STATE if it is not live. */
+int32_t zero_stage3_unit_release(zsmr_ctx* ctx, int32_t unit);
+
+/* Schedule state of one unit (host only); any output pointer may be NULL. */
+int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
+                               int64_t* gathers, int64_t* releases);
+
+/* Launch shape of the streaming kernels: workgroups per compute unit for the
+ * grid-stride loops (default 8; 1..64).  Affects speed only, never results. */
+int32_t zsmr_set_blocks_per_cu(int32_t blocks_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZSMR_H */

@@ -1,0 +1,170 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol its headers declare, and its host-only parts (layout, accounting,
+argument checks, the ZeRO-3 state checks) agree with the oracle.  No call
+here launches a kernel."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import zero_sharded_mixed_reduce_amd as z
+from oracle import accounting as acc
+from oracle.layout import make_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(z.LIB_PATH)
+    names = declared("zsmr.h")
+    assert "zero_fused_step" in names and "zero_bytes_per_rank" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(z.SIGNATURES), "binding and header disagree"
+    import synth.gpu as sg
+    slib = ctypes.CDLL(sg.LIB_PATH)
+    snames = declared("zsmr_synth.h")
+    assert snames == ["zsmr_synth_fill16", "zsmr_synth_fill32"]
+    for n in snames:
+        assert hasattr(slib, n), n
+
+
+CONFIGS = [
+    (65536, 4, st, [16384] * 4 if st == 3 else None) for st in range(4)
+] + [
+    (124_439_808, 8, 2, None), (1_558_000_000, 16, 1, None), (7_500_000_000, 64, 2, None),
+    (8_030_261_248, 8, 3, [1_050_677_248] + [218_112_000] * 32),
+]
+
+
+def _cmp_bytes(ctx, lay, gb=2, ml=1):
+    got = z.zero_bytes_per_rank(ctx, gb, ml)
+    want = acc.bytes_per_rank(lay, gather_bytes=gb, max_live=ml)
+    for k, v in got.items():
+        assert v == getattr(want, k), k
+
+
+@pytest.mark.parametrize("numel,world,stage,units", CONFIGS)
+def test_layout_and_accounting_match_oracle(numel, world, stage, units):
+    ctx = z.zero_init_shards(numel, world, stage, "bf16", units=units)
+    lay = make_layout(numel, world, stage, units)
+    info = ctx.info()
+    assert info["padded_numel"] == lay.padded_numel and info["shard_numel"] == lay.shard_numel
+    for u in range(lay.n_units if stage == 3 else 1):
+        for r in range(world):
+            off, ln, loc = z.zero_layout(ctx, r, u)
+            assert (off, ln) == lay.owned(r, u)
+            assert loc == (lay.local_offset(u) if stage == 3 else 0)
+    _cmp_bytes(ctx, lay)
+    _cmp_bytes(ctx, lay, gb=4, ml=2)
+
+
+def test_random_layouts_match_oracle():
+    rnd = random.Random(1234)
+    for _ in range(300):
+        world = rnd.randint(1, 70)
+        units = [rnd.randint(1, 10 ** rnd.randint(1, 7)) for _ in range(rnd.randint(1, 6))]
+        numel = sum(units)
+        stage = rnd.randint(0, 3)
+        ctx = z.zero_init_shards(numel, world, stage, "fp16", pad=True,
+                                 units=units if stage == 3 else None)
+        lay = make_layout(numel, world, stage, units if stage == 3 else None, pad=True)
+        r = rnd.randrange(world)
+        u = rnd.randrange(lay.n_units) if stage == 3 else 0
+        assert z.zero_layout(ctx, r, u)[:2] == lay.owned(r, u)
+        _cmp_bytes(ctx, lay, gb=rnd.choice([2, 4]), ml=rnd.randint(1, 3))
+
+
+def test_page_pins_through_the_c_library():
+    # the tiny model of "ZeRO, annotated" and the 7.5B/64 Figure-1 case
+    tiny = [z.zero_bytes_per_rank(z.zero_init_shards(8, 4, s, "fp16"))["resident"] for s in range(4)]
+    assert tiny == [128, 56, 44, 32]
+    big = [z.zero_bytes_per_rank(z.zero_init_shards(7_500_000_000, 64, s, "bf16"))["resident"]
+           for s in range(4)]
+    assert big == [120_000_000_000, 31_406_250_000, 16_640_625_000, 1_875_000_000]
+    assert z.zero_bytes_per_rank(z.zero_init_shards(8, 4, 1, "fp16"))["rs_elems"] == 6
+    # zero_check: 57,636 bytes of optimizer state with ceil(19,210 / 4) = 4,803
+    b = z.zero_bytes_per_rank(z.zero_init_shards(19210, 4, 1, "bf16", pad=True))
+    assert b["res_master"] + b["res_m"] + b["res_v"] == 57636
+
+
+def test_init_errors():
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_init_shards(1001, 4, 2, "bf16")
+    assert e.value.code == z.ZSMR_ERR_INDIVISIBLE
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_init_shards(10, 4, 3, "bf16", units=[5, 5])
+    assert e.value.code == z.ZSMR_ERR_INDIVISIBLE
+    for bad in [dict(numel=0, world=1, stage=0), dict(numel=8, world=0, stage=0),
+                dict(numel=8, world=2, stage=4), dict(numel=8, world=2, stage=3, units=[4, 5])]:
+        with pytest.raises(z.ZsmrError) as e:
+            z.zero_init_shards(bad["numel"], bad["world"], bad["stage"], "bf16", units=bad.get("units"))
+        assert e.value.code == z.ZSMR_ERR_ARG
+    h = ctypes.c_void_p()
+    assert z.load().zero_init_shards(ctypes.byref(h), 8, 2, 1, 3, 2, 0, None, 0) == z.ZSMR_ERR_DTYPE
+
+
+def test_argument_errors_return_before_any_launch():
+    ctx = z.zero_init_shards(64, 4, 2, "bf16")
+    ok = 1 << 20                          # an aligned, never-dereferenced address
+    with pytest.raises(z.ZsmrError) as e:     # rank out of range
+        z.zero_fused_step(ctx, 4, 0, ok, 64, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # t < 1
+        z.zero_fused_step(ctx, 0, 0, ok, 64, 0, ok, ok, ok, ok, 0, 1e-3, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # beta1 >= 1
+        z.zero_fused_step(ctx, 0, 0, ok, 64, 0, ok, ok, ok, ok, 1, 1e-3, betas=(1.0, 0.999), stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # rows overlap (stride < shard)
+        z.zero_fused_step(ctx, 0, 0, ok, 8, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # odd address for a 16-bit row
+        z.zero_fused_step(ctx, 0, 0, ok + 1, 64, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ALIGN
+    with pytest.raises(z.ZsmrError) as e:     # fp32 master not 4-byte aligned
+        z.zero_fused_step(ctx, 0, 0, ok, 64, 0, ok + 2, ok, ok, ok, 1, 1e-3, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ALIGN
+    with pytest.raises(z.ZsmrError) as e:     # null g_out
+        z.zero_reduce_shard(ctx, 0, 0, ok, 64, 0, True, 0, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # overlapping copy
+        z.zero_gather_copy(ctx, 0, ok, ok + 8, 100, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    z.zero_adam_step(ok, ok, ok, ok, 0, 1, 1e-3, stream=0)       # n = 0 is a no-op
+    z.zero_gather_copy(ctx, 0, ok, ok, 0, stream=0)
+    for rank in range(4):                                          # nothing was counted
+        assert z.zero_counters(ctx, rank)["traffic_elems"] == 0
+
+
+def test_stage3_state_errors_on_the_host():
+    ctx = z.zero_init_shards(64, 4, 3, "bf16", units=[32, 32])
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_stage3_unit_release(ctx, 0)
+    assert e.value.code == z.ZSMR_ERR_STATE
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_stage3_unit_release(ctx, 2)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # a null shard pointer is refused before launching
+        z.zero_stage3_unit_gather(ctx, 0, [1 << 20, 0, 1 << 20, 1 << 20], 1 << 21, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    assert z.zero_stage3_unit_state(ctx, 0) == (False, 0, 0)
+    z.zero_stage3_set_max_live(ctx, 2)
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_stage3_set_max_live(ctx, 0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    nz = z.zero_init_shards(64, 4, 2, "bf16")
+    with pytest.raises(z.ZsmrError) as e:     # not a stage-3 context
+        z.zero_stage3_unit_release(nz, 0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:
+        z.zsmr_set_blocks_per_cu(0)
+    assert e.value.code == z.ZSMR_ERR_ARG

@@ -1,0 +1,335 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, at
+sizes the oracle finishes in seconds: all four schemes on the 65,536-element
+/ 4-rank / fp16 workload, ragged and padded sizes, every alignment variant of
+the kernels, mixed 16-bit formats, fused against unfused, and the counters
+against the accounting."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import zero_sharded_mixed_reduce_amd as z
+from oracle import accounting as acc
+from oracle import numerics as nm
+from oracle import schemes as sc
+from oracle.layout import make_layout
+from tests.gpu_helpers import compare, dev16, host16, host32, param_map, say
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def gpu_scheme(stage, numel, world, dt, T, lr, units=None, pad=False, fused=True, gsig=1e-2,
+               check_gathers=True, seed=0):
+    """Run a scheme over N simulated ranks through the C ABI only."""
+    say(f"[gpu_scheme] stage={stage} numel={numel} world={world} dt={dt} T={T} units={units} "
+        f"pad={pad} fused={fused}")
+    units3 = list(units) if (units and stage == 3) else None
+    ctx = z.zero_init_shards(numel, world, stage, dt, pad=pad, units=units3)
+    info = ctx.info()
+    P = info["padded_numel"]
+    pm = param_map(ctx, units3)
+    ok = pm >= 0
+    p = np.arange(numel)
+    theta = synth.theta0(seed, p)
+
+    def padded(x, fill=0):
+        out = np.full(P, fill, dtype=x.dtype)
+        out[ok] = x[pm[ok]]
+        return out
+
+    def grads_dev(t):
+        rows = np.stack([padded(synth.grad16(seed, r, t, p, gsig, dt)) for r in range(world)])
+        return dev16(rows.ravel())
+
+    reps = world if stage == 0 else 1                 # DP: one full replica per rank
+    th = torch.from_numpy(padded(theta)).cuda()
+    master = [torch.empty(P, dtype=torch.float32, device="cuda") for _ in range(reps)]
+    m = [torch.empty_like(master[0]) for _ in range(reps)]
+    v = [torch.empty_like(master[0]) for _ in range(reps)]
+    p16 = [torch.empty(P, dtype=TDT[dt], device="cuda") for _ in range(reps)]
+    pieces = []
+    for u in range(info["n_units"] if stage == 3 else 1):
+        for r in range(world):
+            off, ln, _ = z.zero_layout(ctx, r, u)
+            pieces.append((r, u, off, ln))
+    for (r, u, off, ln) in pieces:
+        i = r if stage == 0 else 0
+        z.zero_init_state(ctx, r, u, th[off:], master[i][off:], m[i][off:], v[i][off:], p16[i][off:])
+    g_tmp = torch.empty(max(pc[3] for pc in pieces), dtype=torch.float32, device="cuda")
+    unit_buf = torch.empty(info["max_unit_numel"], dtype=TDT[dt], device="cuda")
+    gather_bad = 0
+
+    def update(t, G, r, u, off, ln):
+        i = r if stage == 0 else 0
+        if fused:
+            z.zero_fused_step(ctx, r, u, G, P, off, master[i][off:], m[i][off:], v[i][off:],
+                              p16[i][off:], t, lr)
+        else:
+            z.zero_reduce_shard(ctx, r, u, G, P, off, True, g_tmp)
+            z.zero_adam_step(master[i][off:], m[i][off:], v[i][off:], g_tmp, ln, t, lr)
+            z.zero_gather_cast(ctx, r, u, master[i][off:], p16[i][off:])
+
+    def gather(u):
+        nonlocal gather_bad
+        offs = [z.zero_layout(ctx, r, u) for r in range(world)]
+        z.zero_stage3_unit_gather(ctx, u, [p16[0][o:] for (o, _, _) in offs], unit_buf)
+        if check_gathers:
+            q0, su = offs[0][0], offs[0][1]
+            gather_bad += not torch.equal(unit_buf[:world * su].view(torch.int16),
+                                          p16[0][q0:q0 + world * su].view(torch.int16))
+
+    for t in range(1, T + 1):
+        G = grads_dev(t)
+        if stage != 3:
+            for (r, u, off, ln) in pieces:
+                update(t, G, r, u, off, ln)
+        else:
+            U = info["n_units"]
+            for u in range(U):
+                gather(u)
+                z.zero_stage3_unit_release(ctx, u)
+            for u in reversed(range(U)):
+                gather(u)
+                for (r, uu, off, ln) in pieces:
+                    if uu == u:
+                        update(t, G, r, u, off, ln)
+                z.zero_stage3_unit_release(ctx, u)
+    torch.cuda.synchronize()
+    assert gather_bad == 0, "a gathered unit differs from its shards"
+
+    res = {"ctx": ctx, "P": P, "pm": pm}
+    res["reps"] = [{"master": _unpad(host32(master[i]), pm, ok, numel),
+                    "m": _unpad(host32(m[i]), pm, ok, numel),
+                    "v": _unpad(host32(v[i]), pm, ok, numel),
+                    "p16": _unpad(host16(p16[i]), pm, ok, numel),
+                    "pad_master": host32(master[i])[~ok], "pad_p16": host16(p16[i])[~ok]}
+                   for i in range(reps)]
+    return res
+
+
+def _unpad(x, pm, ok, numel):
+    out = np.empty(numel, dtype=x.dtype)
+    out[pm[ok]] = x[ok]
+    return out
+
+
+def oracle_scheme(stage, numel, world, dt, T, lr, units=None, pad=False, gsig=1e-2, seed=0):
+    p = np.arange(numel)
+    theta = synth.theta0(seed, p)
+
+    def g(t):
+        return [synth.grad16(seed, r, t, p, gsig, dt) for r in range(world)]
+    return sc.run(stage, numel, world, theta, g, T, dt, lr, units=units if stage == 3 else None,
+                  pad=pad)
+
+
+def check_against_oracle(res, ref, what):
+    for i, rep in enumerate(res["reps"]):
+        compare({"master": rep["master"], "m": rep["m"], "v": rep["v"]},
+                {"master": ref.full_master(), "m": ref.full_m(), "v": ref.full_v()},
+                rep["p16"], ref.working_copy(), f"{what} replica {i}")
+        assert not rep["pad_master"].any() and not rep["pad_p16"].any(), "pad is not zero"
+
+
+def check_counters(res, stage, numel, world, units, pad, T):
+    lay = make_layout(numel, world, stage, units if stage == 3 else None, pad)
+    want = acc.bytes_per_rank(lay)
+    for r in range(world):
+        c = z.zero_counters(res["ctx"], r)
+        assert c["rs_elems"] == T * want.rs_elems
+        assert c["ag_elems"] == T * want.ag_elems
+        assert c["ar_elems"] == T * want.ar_elems
+        assert c["traffic_bytes"] == T * want.traffic_bytes
+    c = z.zero_counters(res["ctx"], 0)
+    if stage == 3:
+        U = lay.n_units
+        assert c["stage3_gathers"] == 2 * U * T and c["stage3_releases"] == 2 * U * T
+        assert c["live_units"] == 0 and c["peak_live_bytes"] == want.gathered
+        for u in range(U):
+            assert z.zero_stage3_unit_state(res["ctx"], u) == (False, 2 * T, 2 * T)
+
+
+# --------------------------------------------- the 65,536 / N = 4 workload --
+@pytest.mark.parametrize("stage", [0, 1, 2, 3])
+@pytest.mark.parametrize("fused", [True, False])
+def test_psi65k_all_schemes(stage, fused):
+    numel, world, dt, T, lr, units = 65536, 4, "fp16", 5, 1e-2, [16384] * 4
+    res = gpu_scheme(stage, numel, world, dt, T, lr, units, fused=fused)
+    ref = oracle_scheme(stage, numel, world, dt, T, lr, units)
+    check_against_oracle(res, ref, f"psi65k stage {stage} fused={fused}")
+    check_counters(res, stage, numel, world, units, False, T)
+
+
+def test_psi65k_stage3_one_unit_is_whole_vector_gather():
+    res = gpu_scheme(3, 65536, 4, "fp16", 5, 1e-2, [65536])
+    ref = oracle_scheme(3, 65536, 4, "fp16", 5, 1e-2, [65536])
+    check_against_oracle(res, ref, "psi65k stage 3, one unit")
+    check_counters(res, 3, 65536, 4, [65536], False, 5)
+
+
+# ------------------------------------------------ ragged and padded sizes --
+@pytest.mark.parametrize("numel,world,stage,units,dt", [
+    (1001, 4, 1, None, "bf16"),                 # pad: S = 251, rows not 16-byte aligned
+    (1001, 3, 2, None, "fp16"),
+    (40_003, 5, 2, None, "bf16"),               # several tiles, ragged tail, odd world
+    (40_003, 7, 3, [10_001, 7, 29_991, 1, 2, 1], "bf16"),   # tiny units, all padded
+    (123_457, 8, 3, [100_000, 23_457], "fp16"),
+    (777, 1, 2, None, "bf16"),                  # a world of one
+    (7, 1, 1, None, "bf16"),                    # fewer elements than one vector
+    (9, 3, 3, [9], "fp16"),                     # padding inside a single unit
+    (65_544, 8, 0, None, "bf16"),               # data parallel, not a multiple of 64
+])
+def test_ragged_and_padded(numel, world, stage, units, dt):
+    pad = True
+    for fused in (True, False):
+        res = gpu_scheme(stage, numel, world, dt, 3, 1e-3, units, pad=pad, fused=fused, gsig=1e-2)
+        ref = oracle_scheme(stage, numel, world, dt, 3, 1e-3, units, pad=pad)
+        check_against_oracle(res, ref, f"ragged {numel}/{world}/stage {stage} fused={fused}")
+        check_counters(res, stage, numel, world, units, pad, 3)
+
+
+# -------------------------------------------------- single-piece variants --
+def _piece_inputs(n, world, gdt, seed=0, step=1, sigma=1e-2, outlier=0):
+    p = np.arange(n)
+    rows = np.stack([synth.grad16(seed, r, step, p, sigma, gdt, outlier) for r in range(world)])
+    theta = synth.theta0(seed, p)
+    return rows, theta
+
+
+def _oracle_piece(rows, theta, gdt, pdt, T, lr, steps_rows=None):
+    master, m, v = theta.copy(), np.zeros_like(theta), np.zeros_like(theta)
+    for t in range(1, T + 1):
+        r16 = rows if steps_rows is None else steps_rows[t]
+        g = nm.reduce_rank_order([nm.widen16(r, gdt) for r in r16])
+        master, m, v = nm.adam_update(master, m, v, g, nm.adam_consts(lr, 0.9, 0.999, 1e-8, t))
+    return master, m, v, nm.cast16(master, pdt)
+
+
+@pytest.mark.parametrize("shift16,shift32,gshift", [
+    (0, 0, 0),      # 128-bit everywhere
+    (4, 0, 0),      # 16-bit destination 8-byte aligned: 64-bit stores
+    (2, 0, 0),      # 4-byte aligned: 32-bit stores
+    (1, 0, 0),      # 2-byte aligned: 16-bit stores
+    (3, 0, 0),
+    (0, 1, 0),      # fp32 state not 16-byte aligned: one element per lane
+    (0, 0, 1),      # gradient rows not 16-byte aligned: one element per lane
+    (5, 3, 2),
+])
+@pytest.mark.parametrize("n", [8 * 256 * 3 + 5, 1, 7, 8, 9])
+def test_alignment_variants(shift16, shift32, gshift, n):
+    world, gdt, pdt, T, lr = 4, "bf16", "bf16", 2, 1e-3
+    ctx = z.zero_init_shards(n * world, world, 2, gdt, pdt)
+    rows, theta = _piece_inputs(n, world, gdt)
+    stride = n + 8 + (8 - n % 8) % 8                       # rows 16-byte aligned apart
+    gbuf = np.zeros(gshift + world * stride, np.uint16)
+    for r in range(world):
+        gbuf[gshift + r * stride: gshift + r * stride + n] = rows[r]
+    G = dev16(gbuf)
+    mk32 = lambda: torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    mb, mm, vb = mk32(), mk32(), mk32()
+    pb = torch.zeros(n + 16, dtype=torch.bfloat16, device="cuda")
+    th = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    th[shift32:shift32 + n] = torch.from_numpy(theta).cuda()
+    s, s16 = shift32, shift16
+    z.zero_init_state(ctx, 0, 0, th[s:], mb[s:], mm[s:], vb[s:], pb[s16:])
+    for t in range(1, T + 1):
+        z.zero_fused_step(ctx, 0, 0, G[gshift:], stride, 0, mb[s:], mm[s:], vb[s:], pb[s16:], t, lr)
+    torch.cuda.synchronize()
+    master, m, v, p16 = _oracle_piece(rows, theta, gdt, pdt, T, lr)
+    got16 = host16(pb)
+    compare({"master": host32(mb)[s:s + n], "m": host32(mm)[s:s + n], "v": host32(vb)[s:s + n]},
+            {"master": master, "m": m, "v": v}, got16[s16:s16 + n], p16,
+            f"alignment shift16={shift16} shift32={shift32} gshift={gshift} n={n}")
+    # nothing outside the piece was written
+    assert not got16[:s16].any() and not got16[s16 + n:].any()
+    assert not host32(mb)[:s].any() and not host32(mb)[s + n:].any()
+
+
+@pytest.mark.parametrize("gdt,pdt", [("fp16", "bf16"), ("bf16", "fp16"), ("fp16", "fp16")])
+def test_mixed_formats(gdt, pdt):
+    n, world, T, lr = 3 * 2048 + 3, 8, 3, 1e-2
+    ctx = z.zero_init_shards(n * world, world, 1, gdt, pdt)
+    steps_rows = {t: _piece_inputs(n, world, gdt, step=t)[0] for t in range(1, T + 1)}
+    theta = synth.theta0(0, np.arange(n))
+    th = torch.from_numpy(theta).cuda()
+    mb = torch.empty(n, dtype=torch.float32, device="cuda")
+    mm, vb = torch.empty_like(mb), torch.empty_like(mb)
+    pb = torch.empty(n, dtype=TDT[pdt], device="cuda")
+    z.zero_init_state(ctx, 0, 0, th, mb, mm, vb, pb)
+    for t in range(1, T + 1):
+        z.zero_fused_step(ctx, 0, 0, dev16(steps_rows[t].ravel()), n, 0, mb, mm, vb, pb, t, lr)
+    torch.cuda.synchronize()
+    master, m, v, p16 = _oracle_piece(None, theta, gdt, pdt, T, lr, steps_rows)
+    compare({"master": host32(mb), "m": host32(mm), "v": host32(vb)},
+            {"master": master, "m": m, "v": v}, host16(pb), p16, f"mixed {gdt}->{pdt}")
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "fp16"])
+def test_reduce_sum_and_mean(gdt):
+    n, world = 10_000 + 3, 16
+    ctx = z.zero_init_shards(n * world, world, 2, gdt)
+    rows, _ = _piece_inputs(n, world, gdt, sigma=1e-1, outlier=100)
+    G = dev16(rows.ravel())
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    for mean in (False, True):
+        z.zero_reduce_shard(ctx, 0, 0, G, n, 0, mean, out)
+        torch.cuda.synchronize()
+        want = nm.reduce_rank_order([nm.widen16(r, gdt) for r in rows], mean=mean)
+        assert np.array_equal(host32(out).view(np.uint32), want.view(np.uint32)), f"mean={mean}"
+
+
+def test_zero_gradient_leaves_master_and_adam_only_matches():
+    n = 5000
+    theta = synth.theta0(0, np.arange(n))
+    g = np.zeros(n, np.float32)
+    mb = torch.from_numpy(theta.copy()).cuda()
+    mm, vb = torch.zeros_like(mb), torch.zeros_like(mb)
+    for t in range(1, 4):
+        z.zero_adam_step(mb, mm, vb, torch.from_numpy(g).cuda(), n, t, 1e-2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host32(mb).view(np.uint32), theta.view(np.uint32))
+    assert not host32(mm).any() and not host32(vb).any()
+    # Adam alone against the oracle on a wide range of magnitudes
+    rng = np.random.default_rng(2)
+    gg = (rng.normal(0, 1, n) * 10.0 ** rng.uniform(-9, 1, n)).astype(np.float32)
+    mb = torch.from_numpy(theta.copy()).cuda()
+    mm, vb = torch.zeros_like(mb), torch.zeros_like(mb)
+    master, m, v = theta.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 6):
+        z.zero_adam_step(mb, mm, vb, torch.from_numpy(gg).cuda(), n, t, 3e-3, (0.8, 0.95), 1e-6)
+        master, m, v = nm.adam_update(master, m, v, gg, nm.adam_consts(3e-3, 0.8, 0.95, 1e-6, t))
+    torch.cuda.synchronize()
+    for got, want in ((mb, master), (mm, m), (vb, v)):
+        assert np.array_equal(host32(got).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_cast_special_values(dt):
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65520.0, 1e30, -1e30, np.inf, -np.inf, 6e-8,
+                     3e-45, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+                     3.4e38, 5.96e-8, 2.98e-8, 1.5e-38], np.float32)
+    rng = np.random.default_rng(9)
+    rand = rng.integers(0, 1 << 32, 1 << 16, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = np.concatenate([vals, rand[np.isfinite(rand)]]).astype(np.float32)
+    ctx = z.zero_init_shards(x.size, 1, 2, dt)
+    out = torch.empty(x.size, dtype=TDT[dt], device="cuda")
+    z.zero_gather_cast(ctx, 0, 0, torch.from_numpy(x).cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(out), nm.cast16(x, dt))
+
+
+def test_gather_copy_alignments():
+    n = 100_003
+    src = np.arange(n + 32, dtype=np.uint16)
+    ctx = z.zero_init_shards(64, 2, 2, "bf16")
+    for so, do in [(0, 0), (4, 4), (1, 1), (2, 6), (3, 0), (0, 5)]:
+        S = dev16(src)
+        D = torch.zeros(n + 32, dtype=torch.int16, device="cuda")
+        z.zero_gather_copy(ctx, 1, S[so:], D[do:], n)
+        torch.cuda.synchronize()
+        got = host16(D)
+        assert np.array_equal(got[do:do + n], src[so:so + n])
+        assert not got[:do].any() and not got[do + n:].any()
+    assert z.zero_counters(ctx, 1)["ag_elems"] == 6 * n

@@ -1,0 +1,274 @@
+"""Python binding of libzsmr.so, the ZeRO shard step on one MI355X (gfx950).
+
+Argument marshalling only: every function here has the name of a C entry
+point of ``include/zsmr.h`` and passes pointers (``tensor.data_ptr()`` or a
+plain int), sizes and a HIP stream (default: torch's current stream) to it.
+All arithmetic runs in the library's HIP kernels.  There is no fallback: if
+``libzsmr.so`` has not been built, importing the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_DIR, "libzsmr.so")
+
+ZSMR_OK, ZSMR_ERR_ARG, ZSMR_ERR_INDIVISIBLE, ZSMR_ERR_STATE = 0, 1, 2, 3
+ZSMR_ERR_DTYPE, ZSMR_ERR_ALIGN, ZSMR_ERR_HIP = 4, 5, 6
+ZSMR_FP16, ZSMR_BF16 = 1, 2
+ZSMR_DP, ZSMR_ZERO1, ZSMR_ZERO2, ZSMR_ZERO3 = 0, 1, 2, 3
+DTYPES = {"fp16": ZSMR_FP16, "bf16": ZSMR_BF16}
+
+_i32, _i64, _vp, _f32p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+
+
+class ZsmrError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = f"{where}: {_lib().zsmr_strerror(code).decode()} (code {code})"
+        if code == ZSMR_ERR_HIP:
+            msg += f": {_lib().zsmr_last_hip_error().decode()}"
+        super().__init__(msg)
+        self.code = code
+
+
+class zsmr_adam(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+class zsmr_layout_info(ctypes.Structure):
+    _fields_ = [("numel", _i64), ("padded_numel", _i64), ("shard_numel", _i64),
+                ("max_unit_numel", _i64), ("world", _i32), ("stage", _i32), ("n_units", _i32),
+                ("grad_dtype", _i32), ("param_dtype", _i32), ("pad", _i32)]
+
+
+class zsmr_bytes(ctypes.Structure):
+    _fields_ = [(n, _i64) for n in ("res_p16", "res_grad", "res_master", "res_m", "res_v",
+                                    "resident", "gathered", "peak", "unit_grad", "rs_elems",
+                                    "ag_elems", "ar_elems", "traffic_elems", "traffic_bytes")]
+
+
+class zsmr_counters(ctypes.Structure):
+    _fields_ = [(n, _i64) for n in ("rs_elems", "ag_elems", "ar_elems", "traffic_elems",
+                                    "traffic_bytes", "stage3_gathers", "stage3_releases",
+                                    "live_units", "live_bytes", "peak_live_bytes")]
+
+
+# name -> (restype, argtypes); the list is the ABI of include/zsmr.h
+SIGNATURES = {
+    "zsmr_strerror": (ctypes.c_char_p, [_i32]),
+    "zsmr_last_hip_error": (ctypes.c_char_p, []),
+    "zero_init_shards": (_i32, [ctypes.POINTER(_vp), _i64, _i32, _i32, _i32, _i32, _i32,
+                                ctypes.POINTER(_i64), _i32]),
+    "zero_destroy": (None, [_vp]),
+    "zero_layout_info": (_i32, [_vp, ctypes.POINTER(zsmr_layout_info)]),
+    "zero_layout": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                           ctypes.POINTER(_i64)]),
+    "zero_bytes_per_rank": (_i32, [_vp, _i32, _i32, ctypes.POINTER(zsmr_bytes)]),
+    "zero_counters": (_i32, [_vp, _i32, ctypes.POINTER(zsmr_counters)]),
+    "zero_reset_counters": (_i32, [_vp]),
+    "zero_init_state": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "zero_reduce_shard": (_i32, [_vp, _i32, _i32, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "zero_adam_step": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, ctypes.POINTER(zsmr_adam), _vp]),
+    "zero_gather_cast": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "zero_fused_step": (_i32, [_vp, _i32, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32,
+                               ctypes.POINTER(zsmr_adam), _vp]),
+    "zero_gather_copy": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
+    "zero_stage3_set_max_live": (_i32, [_vp, _i32]),
+    "zero_stage3_unit_gather": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _vp, _vp]),
+    "zero_stage3_unit_release": (_i32, [_vp, _i32]),
+    "zero_stage3_unit_state": (_i32, [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
+                                      ctypes.POINTER(_i64)]),
+    "zsmr_set_blocks_per_cu": (_i32, [_i32]),
+}
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m zero_sharded_mixed_reduce_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def load():
+    """Load libzsmr.so (raises ImportError if it has not been built)."""
+    return _lib()
+
+
+def _check(code: int, where: str) -> None:
+    if code != ZSMR_OK:
+        raise ZsmrError(code, where)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _hp(lr: float, betas=(0.9, 0.999), eps: float = 1e-8) -> zsmr_adam:
+    return zsmr_adam(float(lr), float(betas[0]), float(betas[1]), float(eps))
+
+
+class Ctx:
+    """Owner of a ``zsmr_ctx*`` (freed with ``zero_destroy`` on close/GC)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def close(self):
+        if self.handle:
+            _lib().zero_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def _as_param(self):
+        return self.handle
+
+    def info(self) -> dict:
+        return zero_layout_info(self)
+
+    def layout(self, rank: int, unit: int = 0):
+        return zero_layout(self, rank, unit)
+
+
+def zero_init_shards(numel: int, world: int, stage: int, grad_dtype: str = "bf16",
+                     param_dtype: Optional[str] = None, pad: bool = False,
+                     units: Optional[Sequence[int]] = None) -> Ctx:
+    h = _vp()
+    arr = None
+    n_units = 0
+    if units:
+        arr = (_i64 * len(units))(*[int(u) for u in units])
+        n_units = len(units)
+    code = _lib().zero_init_shards(ctypes.byref(h), int(numel), int(world), int(stage),
+                                   DTYPES[grad_dtype], DTYPES[param_dtype or grad_dtype],
+                                   int(bool(pad)), arr, n_units)
+    _check(code, "zero_init_shards")
+    return Ctx(h.value)
+
+
+def zero_destroy(ctx: Ctx) -> None:
+    ctx.close()
+
+
+def zero_layout_info(ctx: Ctx) -> dict:
+    out = zsmr_layout_info()
+    _check(_lib().zero_layout_info(ctx.handle, ctypes.byref(out)), "zero_layout_info")
+    return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def zero_layout(ctx: Ctx, rank: int, unit: int = 0):
+    off, ln, loc = _i64(), _i64(), _i64()
+    _check(_lib().zero_layout(ctx.handle, rank, unit, ctypes.byref(off), ctypes.byref(ln),
+                              ctypes.byref(loc)), "zero_layout")
+    return off.value, ln.value, loc.value
+
+
+def zero_bytes_per_rank(ctx: Ctx, gather_bytes: int = 0, max_live: int = 0) -> dict:
+    out = zsmr_bytes()
+    _check(_lib().zero_bytes_per_rank(ctx.handle, gather_bytes, max_live, ctypes.byref(out)),
+           "zero_bytes_per_rank")
+    return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def zero_counters(ctx: Ctx, rank: int) -> dict:
+    out = zsmr_counters()
+    _check(_lib().zero_counters(ctx.handle, rank, ctypes.byref(out)), "zero_counters")
+    return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def zero_reset_counters(ctx: Ctx) -> None:
+    _check(_lib().zero_reset_counters(ctx.handle), "zero_reset_counters")
+
+
+def zero_init_state(ctx: Ctx, rank: int, unit: int, theta0, master, m, v, p16, stream=None):
+    _check(_lib().zero_init_state(ctx.handle, rank, unit, _ptr(theta0), _ptr(master), _ptr(m),
+                                  _ptr(v), _ptr(p16), _stream(stream)), "zero_init_state")
+
+
+def zero_reduce_shard(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base_elem: int,
+                      mean: bool, g_out, stream=None):
+    _check(_lib().zero_reduce_shard(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
+                                    int(base_elem), int(bool(mean)), _ptr(g_out), _stream(stream)),
+           "zero_reduce_shard")
+
+
+def zero_adam_step(master, m, v, g, n: int, t: int, lr: float, betas=(0.9, 0.999),
+                   eps: float = 1e-8, stream=None):
+    hp = _hp(lr, betas, eps)
+    _check(_lib().zero_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(g), int(n), int(t),
+                                 ctypes.byref(hp), _stream(stream)), "zero_adam_step")
+
+
+def zero_gather_cast(ctx: Ctx, rank: int, unit: int, master, p16_dst, stream=None):
+    _check(_lib().zero_gather_cast(ctx.handle, rank, unit, _ptr(master), _ptr(p16_dst),
+                                   _stream(stream)), "zero_gather_cast")
+
+
+def zero_fused_step(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base_elem: int,
+                    master, m, v, p16_dst, t: int, lr: float, betas=(0.9, 0.999),
+                    eps: float = 1e-8, stream=None):
+    hp = _hp(lr, betas, eps)
+    _check(_lib().zero_fused_step(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
+                                  int(base_elem), _ptr(master), _ptr(m), _ptr(v), _ptr(p16_dst),
+                                  int(t), ctypes.byref(hp), _stream(stream)), "zero_fused_step")
+
+
+def zero_gather_copy(ctx: Ctx, recv_rank: int, src, dst, n: int, stream=None):
+    _check(_lib().zero_gather_copy(ctx.handle, recv_rank, _ptr(src), _ptr(dst), int(n),
+                                   _stream(stream)), "zero_gather_copy")
+
+
+def zero_stage3_set_max_live(ctx: Ctx, max_live: int) -> None:
+    _check(_lib().zero_stage3_set_max_live(ctx.handle, max_live), "zero_stage3_set_max_live")
+
+
+def zero_stage3_unit_gather(ctx: Ctx, unit: int, shard_ptrs: Sequence, unit_buf, stream=None):
+    arr = (_vp * len(shard_ptrs))(*[_ptr(p) for p in shard_ptrs])
+    _check(_lib().zero_stage3_unit_gather(ctx.handle, unit, arr, _ptr(unit_buf), _stream(stream)),
+           "zero_stage3_unit_gather")
+
+
+def zero_stage3_unit_release(ctx: Ctx, unit: int) -> None:
+    _check(_lib().zero_stage3_unit_release(ctx.handle, unit), "zero_stage3_unit_release")
+
+
+def zero_stage3_unit_state(ctx: Ctx, unit: int):
+    live, g, r = _i32(), _i64(), _i64()
+    _check(_lib().zero_stage3_unit_state(ctx.handle, unit, ctypes.byref(live), ctypes.byref(g),
+                                         ctypes.byref(r)), "zero_stage3_unit_state")
+    return bool(live.value), g.value, r.value
+
+
+def zsmr_set_blocks_per_cu(bpc: int) -> None:
+    _check(_lib().zsmr_set_blocks_per_cu(int(bpc)), "zsmr_set_blocks_per_cu")

@@ -1,0 +1,513 @@
+// Host side of libzsmr.so: the C ABI declared in include/zsmr.h.
+//
+// Layout and accounting are integer host code (no HIP call), so they work on
+// a machine without a GPU.  Device entry points validate every argument,
+// compute the fp32 Adam constants, launch through zsmr_launch.h on the
+// caller's stream and only then update the per-rank counters.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zsmr.h"
+#include "zsmr_launch.h"
+
+struct zsmr_ctx {
+    int64_t numel = 0;
+    int32_t world = 0, stage = 0, gdt = 0, pdt = 0, pad = 0;
+    std::vector<int64_t> units;        // true unit sizes
+    std::vector<int64_t> shard_u;      // S_u (stage 3); {S} stages 1-2; {Psi} DP
+    std::vector<int64_t> unit_pstart;  // padded start Q_u (stage 3); {0} otherwise
+    std::vector<int64_t> local_off;    // offset of unit u's piece in a rank's shard
+    int64_t padded = 0, shard_total = 0;
+    // counters: elements received per rank
+    std::vector<int64_t> rs, ag, ar;
+    // ZeRO-3 schedule
+    std::vector<int64_t> gathers, releases;
+    std::vector<char> live;
+    int32_t max_live = 1, live_units = 0;
+    int64_t live_bytes = 0, peak_live_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_hip_error;
+
+int32_t hip_fail(hipError_t e) {
+    g_hip_error = hipGetErrorString(e);
+    return ZSMR_ERR_HIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dtype_ok(int32_t d) { return d == ZSMR_FP16 || d == ZSMR_BF16; }
+
+int n_pieces(const zsmr_ctx* c) { return c->stage == ZSMR_ZERO3 ? (int)c->units.size() : 1; }
+
+int32_t check_piece(const zsmr_ctx* c, int32_t rank, int32_t unit) {
+    if (!c) return ZSMR_ERR_ARG;
+    if (rank < 0 || rank >= c->world) return ZSMR_ERR_ARG;
+    if (unit < 0 || unit >= n_pieces(c)) return ZSMR_ERR_ARG;
+    return ZSMR_OK;
+}
+
+void piece(const zsmr_ctx* c, int32_t rank, int32_t unit, int64_t* off, int64_t* len, int64_t* loc) {
+    int64_t o, l, lo;
+    if (c->stage == ZSMR_DP) {
+        o = 0;
+        l = c->numel;
+        lo = 0;
+    } else if (c->stage != ZSMR_ZERO3) {
+        l = c->shard_u[0];
+        o = (int64_t)rank * l;
+        lo = 0;
+    } else {
+        l = c->shard_u[unit];
+        o = c->unit_pstart[unit] + (int64_t)rank * l;
+        lo = c->local_off[unit];
+    }
+    if (off) *off = o;
+    if (len) *len = l;
+    if (loc) *loc = lo;
+}
+
+bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int32_t check_adam(const zsmr_adam* hp, int32_t t, zsmr::AdamK* k) {
+    if (!hp || t < 1) return ZSMR_ERR_ARG;
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps;
+    if (!std::isfinite(lr) || !std::isfinite(b1) || !std::isfinite(b2) || !std::isfinite(eps))
+        return ZSMR_ERR_ARG;
+    if (lr < 0 || b1 < 0 || b1 >= 1 || b2 < 0 || b2 >= 1 || eps < 0) return ZSMR_ERR_ARG;
+    // Each constant is a double expression rounded to fp32 once ("The four
+    // schemes", Base._adam uses Python scalars against fp32 arrays).
+    k->c1 = (float)b1;
+    k->c1m = (float)(1.0 - b1);
+    k->c2 = (float)b2;
+    k->c2m = (float)(1.0 - b2);
+    k->bc1 = (float)(1.0 - std::pow(b1, (double)t));
+    k->bc2 = (float)(1.0 - std::pow(b2, (double)t));
+    k->lr = (float)lr;
+    k->eps = (float)eps;
+    return ZSMR_OK;
+}
+
+// Counting of one reduce over (rank, unit) of `len` elements: a data-parallel
+// replica takes part in one all-reduce of the whole vector; a sharded rank
+// receives (N-1) peers' contributions to its piece.
+void count_reduce(zsmr_ctx* c, int32_t rank, int64_t len) {
+    const int64_t w = c->world;
+    if (c->stage == ZSMR_DP)
+        c->ar[rank] += 2 * (w - 1) * ceil_div(c->numel, w);
+    else
+        c->rs[rank] += (w - 1) * len;
+}
+
+// Counting of one cast of (rank, unit): at stages 1-2 the all-gather delivers
+// the rank's slot to every other rank; DP and stage 3 cast locally.
+void count_cast(zsmr_ctx* c, int32_t rank, int64_t len) {
+    if (c->stage == ZSMR_ZERO1 || c->stage == ZSMR_ZERO2)
+        for (int32_t q = 0; q < c->world; ++q)
+            if (q != rank) c->ag[q] += len;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zsmr_strerror(int32_t s) {
+    switch (s) {
+        case ZSMR_OK: return "ok";
+        case ZSMR_ERR_ARG: return "invalid argument";
+        case ZSMR_ERR_INDIVISIBLE: return "parameter count (or unit) not divisible by world size";
+        case ZSMR_ERR_STATE: return "ZeRO-3 gather/release out of order";
+        case ZSMR_ERR_DTYPE: return "unknown 16-bit format";
+        case ZSMR_ERR_ALIGN: return "pointer not aligned to its element size";
+        case ZSMR_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* zsmr_last_hip_error(void) { return g_hip_error.c_str(); }
+
+int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
+                         int32_t grad_dtype, int32_t param_dtype, int32_t pad,
+                         const int64_t* unit_numel, int32_t n_units) {
+    if (!out) return ZSMR_ERR_ARG;
+    *out = nullptr;
+    if (numel < 1 || world < 1 || stage < ZSMR_DP || stage > ZSMR_ZERO3 || (pad != 0 && pad != 1))
+        return ZSMR_ERR_ARG;
+    if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZSMR_ERR_DTYPE;
+    if (n_units < 0 || (n_units > 0 && !unit_numel) || (n_units == 0 && unit_numel))
+        return ZSMR_ERR_ARG;
+    std::vector<int64_t> units;
+    if (n_units == 0) {
+        units.push_back(numel);
+    } else {
+        int64_t sum = 0;
+        for (int32_t i = 0; i < n_units; ++i) {
+            if (unit_numel[i] < 1 || unit_numel[i] > numel - sum) return ZSMR_ERR_ARG;
+            sum += unit_numel[i];
+            units.push_back(unit_numel[i]);
+        }
+        if (sum != numel) return ZSMR_ERR_ARG;
+    }
+    zsmr_ctx* c = new (std::nothrow) zsmr_ctx;
+    if (!c) return ZSMR_ERR_ARG;
+    c->numel = numel;
+    c->world = world;
+    c->stage = stage;
+    c->gdt = grad_dtype;
+    c->pdt = param_dtype;
+    c->pad = pad;
+    c->units = units;
+    if (stage == ZSMR_DP) {
+        c->shard_u = {numel};
+        c->unit_pstart = {0};
+        c->local_off = {0};
+        c->padded = numel;
+        c->shard_total = numel;
+    } else if (stage != ZSMR_ZERO3) {
+        if (numel % world && !pad) {
+            delete c;
+            return ZSMR_ERR_INDIVISIBLE;
+        }
+        const int64_t s = ceil_div(numel, world);
+        c->shard_u = {s};
+        c->unit_pstart = {0};
+        c->local_off = {0};
+        c->padded = s * world;
+        c->shard_total = s;
+    } else {
+        int64_t q = 0, loc = 0;
+        for (int64_t u : units) {
+            if (u % world && !pad) {
+                delete c;
+                return ZSMR_ERR_INDIVISIBLE;
+            }
+            const int64_t s = ceil_div(u, world);
+            c->shard_u.push_back(s);
+            c->unit_pstart.push_back(q);
+            c->local_off.push_back(loc);
+            q += s * world;
+            loc += s;
+        }
+        c->padded = q;
+        c->shard_total = loc;
+    }
+    c->rs.assign(world, 0);
+    c->ag.assign(world, 0);
+    c->ar.assign(world, 0);
+    c->gathers.assign(units.size(), 0);
+    c->releases.assign(units.size(), 0);
+    c->live.assign(units.size(), 0);
+    *out = c;
+    return ZSMR_OK;
+}
+
+void zero_destroy(zsmr_ctx* ctx) { delete ctx; }
+
+int32_t zero_layout_info(const zsmr_ctx* c, zsmr_layout_info* out) {
+    if (!c || !out) return ZSMR_ERR_ARG;
+    out->numel = c->numel;
+    out->padded_numel = c->padded;
+    out->shard_numel = c->shard_total;
+    int64_t mx = 0;
+    if (c->stage == ZSMR_ZERO3) {
+        for (int64_t s : c->shard_u) mx = s * c->world > mx ? s * c->world : mx;
+    } else {
+        mx = c->padded;
+    }
+    out->max_unit_numel = mx;
+    out->world = c->world;
+    out->stage = c->stage;
+    out->n_units = (int32_t)c->units.size();
+    out->grad_dtype = c->gdt;
+    out->param_dtype = c->pdt;
+    out->pad = c->pad;
+    return ZSMR_OK;
+}
+
+int32_t zero_layout(const zsmr_ctx* c, int32_t rank, int32_t unit, int64_t* offset, int64_t* len,
+                    int64_t* local_offset) {
+    const int32_t st = check_piece(c, rank, unit);
+    if (st) return st;
+    piece(c, rank, unit, offset, len, local_offset);
+    return ZSMR_OK;
+}
+
+int32_t zero_bytes_per_rank(const zsmr_ctx* c, int32_t gather_bytes, int32_t max_live,
+                            zsmr_bytes* o) {
+    if (!c || !o || gather_bytes < 0 || max_live < 0) return ZSMR_ERR_ARG;
+    if (gather_bytes == 0) gather_bytes = 2;
+    if (max_live == 0) max_live = 1;
+    const int64_t n = c->numel, w = c->world;
+    const bool shard_opt = c->stage >= ZSMR_ZERO1, shard_grad = c->stage >= ZSMR_ZERO2,
+               shard_param = c->stage >= ZSMR_ZERO3;
+    const int64_t s = c->shard_total;
+    std::memset(o, 0, sizeof(*o));
+    // bytes per element of each band: 2 + 2 + 4 + 4 + 4 = 16 ("One Poem
+    // Suffices: ZeRO" section 3.1; "The four schemes", per-band constants)
+    o->res_p16 = 2 * (shard_param ? s : n);
+    o->res_grad = 2 * (shard_grad ? s : n);
+    const int64_t opt = shard_opt ? s : n;
+    o->res_master = 4 * opt;
+    o->res_m = 4 * opt;
+    o->res_v = 4 * opt;
+    o->resident = o->res_p16 + o->res_grad + o->res_master + o->res_m + o->res_v;
+    if (c->stage == ZSMR_ZERO3) {
+        const int64_t nu = (int64_t)c->shard_u.size();
+        const int64_t k = max_live < nu ? max_live : nu;
+        int64_t best = 0, widest = 0;
+        for (int64_t i = 0; i + k <= nu; ++i) {
+            int64_t sum = 0;
+            for (int64_t j = i; j < i + k; ++j) sum += w * c->shard_u[j];
+            best = sum > best ? sum : best;
+        }
+        for (int64_t su : c->shard_u) widest = w * su > widest ? w * su : widest;
+        o->gathered = gather_bytes * best;
+        o->unit_grad = 2 * widest;
+    }
+    o->peak = o->resident + o->gathered;
+    if (c->stage == ZSMR_DP) {
+        o->ar_elems = 2 * (w - 1) * ceil_div(n, w);
+    } else if (c->stage != ZSMR_ZERO3) {
+        o->rs_elems = (w - 1) * s;
+        o->ag_elems = (w - 1) * s;
+    } else {
+        o->rs_elems = (w - 1) * s;
+        o->ag_elems = 2 * (w - 1) * s;
+    }
+    o->traffic_elems = o->rs_elems + o->ag_elems + o->ar_elems;
+    o->traffic_bytes = 2 * o->traffic_elems;
+    return ZSMR_OK;
+}
+
+int32_t zero_counters(const zsmr_ctx* c, int32_t rank, zsmr_counters* o) {
+    if (!c || !o || rank < 0 || rank >= c->world) return ZSMR_ERR_ARG;
+    std::memset(o, 0, sizeof(*o));
+    o->rs_elems = c->rs[rank];
+    o->ag_elems = c->ag[rank];
+    o->ar_elems = c->ar[rank];
+    o->traffic_elems = o->rs_elems + o->ag_elems + o->ar_elems;
+    o->traffic_bytes = 2 * o->traffic_elems;
+    for (size_t u = 0; u < c->gathers.size(); ++u) {
+        o->stage3_gathers += c->gathers[u];
+        o->stage3_releases += c->releases[u];
+    }
+    o->live_units = c->live_units;
+    o->live_bytes = c->live_bytes;
+    o->peak_live_bytes = c->peak_live_bytes;
+    return ZSMR_OK;
+}
+
+int32_t zero_reset_counters(zsmr_ctx* c) {
+    if (!c) return ZSMR_ERR_ARG;
+    std::fill(c->rs.begin(), c->rs.end(), 0);
+    std::fill(c->ag.begin(), c->ag.end(), 0);
+    std::fill(c->ar.begin(), c->ar.end(), 0);
+    std::fill(c->gathers.begin(), c->gathers.end(), 0);
+    std::fill(c->releases.begin(), c->releases.end(), 0);
+    c->peak_live_bytes = c->live_bytes;
+    return ZSMR_OK;
+}
+
+int32_t zero_init_state(const zsmr_ctx* c, int32_t rank, int32_t unit, const float* theta0,
+                        float* master, float* m, float* v, void* p16, hipStream_t stream) {
+    int32_t st = check_piece(c, rank, unit);
+    if (st) return st;
+    if (!theta0 || !master || !m || !v || !p16) return ZSMR_ERR_ARG;
+    if (!al(theta0, 4) || !al(master, 4) || !al(m, 4) || !al(v, 4) || !al(p16, 2))
+        return ZSMR_ERR_ALIGN;
+    int64_t len = 0;
+    piece(c, rank, unit, nullptr, &len, nullptr);
+    zsmr::StepArgs a{};
+    a.g_in = theta0;
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.p16 = static_cast<uint16_t*>(p16);
+    a.n = len;
+    const hipError_t e = zsmr::launch_step(zsmr::M_INIT | zsmr::M_CAST, c->gdt, c->pdt, a, stream);
+    return e == hipSuccess ? ZSMR_OK : hip_fail(e);
+}
+
+static int32_t check_grads(const zsmr_ctx* c, const void* grads, int64_t row_stride,
+                           int64_t base, int64_t len) {
+    if (!grads || base < 0 || row_stride < 0) return ZSMR_ERR_ARG;
+    if (c->world > 1 && row_stride < len) return ZSMR_ERR_ARG;   // rows may not overlap
+    if (!al(grads, 2)) return ZSMR_ERR_ALIGN;
+    return ZSMR_OK;
+}
+
+int32_t zero_reduce_shard(zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
+                          int64_t row_stride, int64_t base, int32_t mean, float* g_out,
+                          hipStream_t stream) {
+    int32_t st = check_piece(c, rank, unit);
+    if (st) return st;
+    int64_t len = 0;
+    piece(c, rank, unit, nullptr, &len, nullptr);
+    if ((st = check_grads(c, grads, row_stride, base, len))) return st;
+    if (!g_out || (mean != 0 && mean != 1)) return ZSMR_ERR_ARG;
+    if (!al(g_out, 4)) return ZSMR_ERR_ALIGN;
+    zsmr::StepArgs a{};
+    a.grads = static_cast<const uint16_t*>(grads) + base;
+    a.row_stride = row_stride;
+    a.nrows = c->world;
+    a.mean = mean;
+    a.nf = (float)c->world;
+    a.g_out = g_out;
+    a.n = len;
+    const hipError_t e = zsmr::launch_step(zsmr::M_REDUCE | zsmr::M_GOUT, c->gdt, c->pdt, a, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    count_reduce(c, rank, len);
+    return ZSMR_OK;
+}
+
+int32_t zero_adam_step(float* master, float* m, float* v, const float* g, int64_t n, int32_t t,
+                       const zsmr_adam* hp, hipStream_t stream) {
+    zsmr::AdamK k{};
+    int32_t st = check_adam(hp, t, &k);
+    if (st) return st;
+    if (n < 0) return ZSMR_ERR_ARG;
+    if (n == 0) return ZSMR_OK;
+    if (!master || !m || !v || !g) return ZSMR_ERR_ARG;
+    if (!al(master, 4) || !al(m, 4) || !al(v, 4) || !al(g, 4)) return ZSMR_ERR_ALIGN;
+    zsmr::StepArgs a{};
+    a.g_in = g;
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.n = n;
+    a.k = k;
+    const hipError_t e = zsmr::launch_step(zsmr::M_ADAM, ZSMR_BF16, ZSMR_BF16, a, stream);
+    return e == hipSuccess ? ZSMR_OK : hip_fail(e);
+}
+
+int32_t zero_gather_cast(zsmr_ctx* c, int32_t rank, int32_t unit, const float* master,
+                         void* p16_dst, hipStream_t stream) {
+    int32_t st = check_piece(c, rank, unit);
+    if (st) return st;
+    if (!master || !p16_dst) return ZSMR_ERR_ARG;
+    if (!al(master, 4) || !al(p16_dst, 2)) return ZSMR_ERR_ALIGN;
+    int64_t len = 0;
+    piece(c, rank, unit, nullptr, &len, nullptr);
+    zsmr::StepArgs a{};
+    a.master = const_cast<float*>(master);
+    a.p16 = static_cast<uint16_t*>(p16_dst);
+    a.n = len;
+    const hipError_t e = zsmr::launch_step(zsmr::M_CAST, c->gdt, c->pdt, a, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    count_cast(c, rank, len);
+    return ZSMR_OK;
+}
+
+int32_t zero_fused_step(zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
+                        int64_t row_stride, int64_t base, float* master, float* m, float* v,
+                        void* p16_dst, int32_t t, const zsmr_adam* hp, hipStream_t stream) {
+    int32_t st = check_piece(c, rank, unit);
+    if (st) return st;
+    int64_t len = 0;
+    piece(c, rank, unit, nullptr, &len, nullptr);
+    if ((st = check_grads(c, grads, row_stride, base, len))) return st;
+    zsmr::AdamK k{};
+    if ((st = check_adam(hp, t, &k))) return st;
+    if (!master || !m || !v || !p16_dst) return ZSMR_ERR_ARG;
+    if (!al(master, 4) || !al(m, 4) || !al(v, 4) || !al(p16_dst, 2)) return ZSMR_ERR_ALIGN;
+    zsmr::StepArgs a{};
+    a.grads = static_cast<const uint16_t*>(grads) + base;
+    a.row_stride = row_stride;
+    a.nrows = c->world;
+    a.mean = 1;
+    a.nf = (float)c->world;
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.p16 = static_cast<uint16_t*>(p16_dst);
+    a.n = len;
+    a.k = k;
+    const hipError_t e =
+        zsmr::launch_step(zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST, c->gdt, c->pdt, a, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    count_reduce(c, rank, len);
+    count_cast(c, rank, len);
+    return ZSMR_OK;
+}
+
+int32_t zero_gather_copy(zsmr_ctx* c, int32_t recv_rank, const void* src, void* dst, int64_t n,
+                         hipStream_t stream) {
+    if (!c || recv_rank < 0 || recv_rank >= c->world || n < 0) return ZSMR_ERR_ARG;
+    if (n == 0) return ZSMR_OK;
+    if (!src || !dst) return ZSMR_ERR_ARG;
+    if (!al(src, 2) || !al(dst, 2)) return ZSMR_ERR_ALIGN;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t bytes = static_cast<uintptr_t>(n) * 2;
+    if (s < d + bytes && d < s + bytes) return ZSMR_ERR_ARG;
+    const hipError_t e = zsmr::launch_copy16(static_cast<const uint16_t*>(src),
+                                             static_cast<uint16_t*>(dst), n, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c->ag[recv_rank] += n;
+    return ZSMR_OK;
+}
+
+int32_t zero_stage3_set_max_live(zsmr_ctx* c, int32_t max_live) {
+    if (!c || c->stage != ZSMR_ZERO3 || max_live < 1) return ZSMR_ERR_ARG;
+    if (c->live_units) return ZSMR_ERR_STATE;
+    c->max_live = max_live;
+    return ZSMR_OK;
+}
+
+int32_t zero_stage3_unit_gather(zsmr_ctx* c, int32_t unit, const void* const* shard_ptrs,
+                                void* unit_buf, hipStream_t stream) {
+    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
+        return ZSMR_ERR_ARG;
+    if (!shard_ptrs || !unit_buf) return ZSMR_ERR_ARG;
+    for (int32_t r = 0; r < c->world; ++r)
+        if (!shard_ptrs[r]) return ZSMR_ERR_ARG;
+    for (int32_t r = 0; r < c->world; ++r)
+        if (!al(shard_ptrs[r], 2)) return ZSMR_ERR_ALIGN;
+    if (!al(unit_buf, 2)) return ZSMR_ERR_ALIGN;
+    if (c->live[unit] || c->live_units >= c->max_live) return ZSMR_ERR_STATE;
+    const int64_t su = c->shard_u[unit];
+    const hipError_t e = zsmr::launch_gather16(reinterpret_cast<const uint16_t* const*>(shard_ptrs),
+                                               c->world, su, static_cast<uint16_t*>(unit_buf), stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c->live[unit] = 1;
+    c->live_units += 1;
+    c->gathers[unit] += 1;
+    for (int32_t r = 0; r < c->world; ++r) c->ag[r] += (int64_t)(c->world - 1) * su;
+    c->live_bytes += 2 * (int64_t)c->world * su;
+    if (c->live_bytes > c->peak_live_bytes) c->peak_live_bytes = c->live_bytes;
+    return ZSMR_OK;
+}
+
+int32_t zero_stage3_unit_release(zsmr_ctx* c, int32_t unit) {
+    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
+        return ZSMR_ERR_ARG;
+    if (!c->live[unit]) return ZSMR_ERR_STATE;
+    c->live[unit] = 0;
+    c->live_units -= 1;
+    c->releases[unit] += 1;
+    c->live_bytes -= 2 * (int64_t)c->world * c->shard_u[unit];
+    return ZSMR_OK;
+}
+
+int32_t zero_stage3_unit_state(const zsmr_ctx* c, int32_t unit, int32_t* live, int64_t* gathers,
+                               int64_t* releases) {
+    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
+        return ZSMR_ERR_ARG;
+    if (live) *live = c->live[unit];
+    if (gathers) *gathers = c->gathers[unit];
+    if (releases) *releases = c->releases[unit];
+    return ZSMR_OK;
+}
+
+int32_t zsmr_set_blocks_per_cu(int32_t bpc) {
+    if (bpc < 1 || bpc > 64) return ZSMR_ERR_ARG;
+    zsmr::set_blocks_per_cu(bpc);
+    return ZSMR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// gfx950 kernels of the ZeRO shard step.
+//
+// One streaming pass per launch.  The path is bound by HBM bandwidth (about
+// 0.3-0.6 flop per byte), so there is no MFMA and no LDS: every lane owns 8
+// consecutive elements, reads each 16-bit gradient row with one 128-bit load,
+// the fp32 master/m/v with two 128-bit loads each, and writes each output
+// once.  The same device code, selected by the MODE bits, gives the fused
+// step and the unfused reduce-only, Adam-only, cast-only and init launches,
+// so the fused and unfused results are the same bits.
+//
+// Arithmetic (the pages: "The four schemes", Base._adam and the schemes'
+// reduce_scatter_mean / astype casts; "ZeRO and FSDP", ZeroAdam.step):
+//  - reduce: fp32 accumulation strictly in rank order 0..N-1, then / N;
+//  - Adam: one IEEE fp32 rounding per operation, no contraction into FMA
+//    (the file is compiled with contraction off and the pragma below),
+//    correctly rounded division and square root;
+//  - cast: round to nearest even (bf16 by the integer carry rule; fp16 by
+//    v_cvt_f16_f32 in the default round-to-nearest-even mode).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zsmr.h"
+#include "zsmr_launch.h"
+
+#pragma clang fp contract(off)
+
+#ifndef ZSMR_NONTEMPORAL
+#define ZSMR_NONTEMPORAL 1
+#endif
+
+namespace zsmr {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kRowBatch = 8;   // gradient rows in flight per lane
+int g_blocks_per_cu = 8;
+
+// Streamed data is touched once per step: non-temporal loads and stores keep
+// it from displacing anything useful in L2 and the MALL.
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) {
+#if ZSMR_NONTEMPORAL
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+#if ZSMR_NONTEMPORAL
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// ---------------------------------------------------------------- formats --
+template <int DT>
+__device__ __forceinline__ float widen(uint32_t h);
+template <>
+__device__ __forceinline__ float widen<ZSMR_BF16>(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+template <>
+__device__ __forceinline__ float widen<ZSMR_FP16>(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t narrow(float x);
+template <>
+__device__ __forceinline__ uint32_t narrow<ZSMR_BF16>(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+template <>
+__device__ __forceinline__ uint32_t narrow<ZSMR_FP16>(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = widen<DT>(w[i] & 0xffffu);
+        f[2 * i + 1] = widen<DT>(w[i] >> 16);
+    }
+}
+
+// ------------------------------------------------------------------- Adam --
+__device__ __forceinline__ void adam1(const AdamK& k, float g, float& w, float& m, float& v) {
+    m = k.c1 * m + k.c1m * g;
+    v = k.c2 * v + (k.c2m * g) * g;
+    const float mh = m / k.bc1;
+    const float vh = v / k.bc2;
+    const float d = __builtin_sqrtf(vh) + k.eps;
+    const float u = (k.lr * mh) / d;
+    w = w - u;
+}
+
+// ------------------------------------------------------------ 16-bit store --
+template <int DV>
+__device__ __forceinline__ void store8x16(uint16_t* p, const uint32_t* h) {
+    if constexpr (DV == 8) {
+        u32x4 w;
+        w[0] = h[0] | (h[1] << 16);
+        w[1] = h[2] | (h[3] << 16);
+        w[2] = h[4] | (h[5] << 16);
+        w[3] = h[6] | (h[7] << 16);
+        st(reinterpret_cast<u32x4*>(p), w);
+    } else if constexpr (DV == 4) {
+        u32x2 a, b;
+        a[0] = h[0] | (h[1] << 16);
+        a[1] = h[2] | (h[3] << 16);
+        b[0] = h[4] | (h[5] << 16);
+        b[1] = h[6] | (h[7] << 16);
+        st(reinterpret_cast<u32x2*>(p), a);
+        st(reinterpret_cast<u32x2*>(p + 4), b);
+    } else if constexpr (DV == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st(reinterpret_cast<uint32_t*>(p + 2 * i), h[2 * i] | (h[2 * i + 1] << 16));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st(p + i, static_cast<uint16_t>(h[i]));
+    }
+}
+
+__device__ __forceinline__ void load8f(const float* p, float* f) {
+    const f32x4 a = ld(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = ld(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = a[i];
+        f[4 + i] = b[i];
+    }
+}
+
+__device__ __forceinline__ void store8f(float* p, const float* f) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = f[i];
+        b[i] = f[4 + i];
+    }
+    st(reinterpret_cast<f32x4*>(p), a);
+    st(reinterpret_cast<f32x4*>(p + 4), b);
+}
+
+// --------------------------------------------------- 8 elements per lane --
+template <int GDT, int PDT, int MODE, int DV>
+__device__ __forceinline__ void body8(const StepArgs& a, int64_t e) {
+    float g[8];
+    if constexpr ((MODE & M_REDUCE) != 0) {
+        const uint16_t* p = a.grads + e;
+        unpack8<GDT>(ld(reinterpret_cast<const u32x4*>(p)), g);
+        for (int r = 1; r < a.nrows; r += kRowBatch) {
+            u32x4 buf[kRowBatch];
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k)
+                if (r + k < a.nrows)
+                    buf[k] = ld(reinterpret_cast<const u32x4*>(p + (int64_t)(r + k) * a.row_stride));
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) {
+                if (r + k < a.nrows) {
+                    float t[8];
+                    unpack8<GDT>(buf[k], t);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) g[j] = g[j] + t[j];
+                }
+            }
+        }
+        if (a.mean) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g[j] = g[j] / a.nf;
+        }
+        if constexpr ((MODE & M_GOUT) != 0) store8f(a.g_out + e, g);
+    } else if constexpr ((MODE & (M_ADAM | M_INIT)) != 0) {
+        load8f(a.g_in + e, g);
+    }
+
+    float w[8];
+    if constexpr ((MODE & M_ADAM) != 0) {
+        float m[8], v[8];
+        load8f(a.master + e, w);
+        load8f(a.m + e, m);
+        load8f(a.v + e, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) adam1(a.k, g[j], w[j], m[j], v[j]);
+        store8f(a.master + e, w);
+        store8f(a.m + e, m);
+        store8f(a.v + e, v);
+    } else if constexpr ((MODE & M_INIT) != 0) {
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = g[j];
+        store8f(a.master + e, w);
+        store8f(a.m + e, z);
+        store8f(a.v + e, z);
+    } else if constexpr ((MODE & M_CAST) != 0) {
+        load8f(a.master + e, w);
+    }
+
+    if constexpr ((MODE & M_CAST) != 0) {
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = narrow<PDT>(w[j]);
+        store8x16<DV>(a.p16 + e, h);
+    }
+}
+
+// ------------------------------------------------------- one element -----
+template <int GDT, int PDT, int MODE>
+__device__ __forceinline__ void body1(const StepArgs& a, int64_t e) {
+    float g = 0.f;
+    if constexpr ((MODE & M_REDUCE) != 0) {
+        const uint16_t* p = a.grads + e;
+        g = widen<GDT>(p[0]);
+        for (int r = 1; r < a.nrows; ++r) g = g + widen<GDT>(p[(int64_t)r * a.row_stride]);
+        if (a.mean) g = g / a.nf;
+        if constexpr ((MODE & M_GOUT) != 0) a.g_out[e] = g;
+    } else if constexpr ((MODE & (M_ADAM | M_INIT)) != 0) {
+        g = a.g_in[e];
+    }
+    float w = 0.f;
+    if constexpr ((MODE & M_ADAM) != 0) {
+        float m = a.m[e], v = a.v[e];
+        w = a.master[e];
+        adam1(a.k, g, w, m, v);
+        a.master[e] = w;
+        a.m[e] = m;
+        a.v[e] = v;
+    } else if constexpr ((MODE & M_INIT) != 0) {
+        w = g;
+        a.master[e] = w;
+        a.m[e] = 0.f;
+        a.v[e] = 0.f;
+    } else if constexpr ((MODE & M_CAST) != 0) {
+        w = a.master[e];
+    }
+    if constexpr ((MODE & M_CAST) != 0) a.p16[e] = static_cast<uint16_t>(narrow<PDT>(w));
+}
+
+// ---------------------------------------------------------------- kernels --
+// Aligned path: grid-stride over 8-element vectors; the last n % 8 elements
+// go to the first lanes of workgroup 0.
+template <int GDT, int PDT, int MODE, int DV>
+__global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
+    const int64_t nvec = a.n >> 3;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+        body8<GDT, PDT, MODE, DV>(a, i << 3);
+    const int tail = static_cast<int>(a.n & 7);
+    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail)
+        body1<GDT, PDT, MODE>(a, (nvec << 3) + threadIdx.x);
+}
+
+// Any-alignment path: one element per lane.
+template <int GDT, int PDT, int MODE>
+__global__ __launch_bounds__(kThreads) void step_scalar_kernel(StepArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < a.n; e += stride)
+        body1<GDT, PDT, MODE>(a, e);
+}
+
+// ------------------------------------------------------------ 16-bit copy --
+template <int W>
+struct VecOf;
+template <>
+struct VecOf<16> { typedef u32x4 T; };
+template <>
+struct VecOf<8> { typedef u32x2 T; };
+template <>
+struct VecOf<4> { typedef uint32_t T; };
+template <>
+struct VecOf<2> { typedef uint16_t T; };
+
+// Copy n elements: `head` scalar elements bring dst (and src, which has the
+// same alignment modulo W) to a W-byte boundary, then W-byte vectors, then
+// the scalar tail.  Lanes of workgroup `part` of `parts` stride the body.
+template <int W>
+__device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, int64_t n,
+                                           int64_t head, int64_t part, int64_t parts) {
+    typedef typename VecOf<W>::T V;
+    constexpr int E = W / 2;
+    const int64_t nb = (n - head) / E;
+    const int64_t body_end = head + nb * E;
+    const V* s = reinterpret_cast<const V*>(src + head);
+    V* d = reinterpret_cast<V*>(dst + head);
+    const int64_t stride = parts * kThreads;
+    for (int64_t i = part * kThreads + threadIdx.x; i < nb; i += stride) st(d + i, ld(s + i));
+    if (part == 0) {
+        const int t = static_cast<int>(threadIdx.x);
+        if (t < head) dst[t] = src[t];
+        const int64_t tail = n - body_end;
+        if (t >= 64 && t - 64 < tail) dst[body_end + (t - 64)] = src[body_end + (t - 64)];
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void copy16_kernel(const uint16_t* src, uint16_t* dst,
+                                                          int64_t n, int64_t head) {
+    copy_range<W>(src, dst, n, head, blockIdx.x, gridDim.x);
+}
+
+constexpr int kMaxGather = 64;
+struct GatherArgs {
+    const uint16_t* src[kMaxGather];
+    int64_t head[kMaxGather];
+    uint16_t* dst;
+    int64_t each;
+};
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void gather16_kernel(GatherArgs g) {
+    const int r = blockIdx.y;
+    copy_range<W>(g.src[r], g.dst + (int64_t)r * g.each, g.each, g.head[r], blockIdx.x, gridDim.x);
+}
+
+// ------------------------------------------------------------------ host --
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+unsigned grid_for(int64_t work_items) {
+    const int64_t cap = (int64_t)cu_count() * g_blocks_per_cu;
+    int64_t blocks = (work_items + kThreads - 1) / kThreads;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return static_cast<unsigned>(blocks);
+}
+
+inline bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int dst_vec(const void* p) {
+    if (al(p, 16)) return 8;
+    if (al(p, 8)) return 4;
+    if (al(p, 4)) return 2;
+    return 1;
+}
+
+template <int GDT, int PDT, int MODE>
+hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
+    if (!vec) {
+        hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n)), dim3(kThreads),
+                           0, s, a);
+        return hipGetLastError();
+    }
+    const dim3 grid(grid_for((a.n + 7) >> 3));
+    switch (dv) {
+        case 8: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 8>), grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, bool vec, int dv, hipStream_t s) {
+    const bool gb = gdt == ZSMR_BF16, pb = pdt == ZSMR_BF16;
+    if (gb && pb) return launch_mode<ZSMR_BF16, ZSMR_BF16, MODE>(a, vec, dv, s);
+    if (gb) return launch_mode<ZSMR_BF16, ZSMR_FP16, MODE>(a, vec, dv, s);
+    if (pb) return launch_mode<ZSMR_FP16, ZSMR_BF16, MODE>(a, vec, dv, s);
+    return launch_mode<ZSMR_FP16, ZSMR_FP16, MODE>(a, vec, dv, s);
+}
+
+}  // namespace
+
+void set_blocks_per_cu(int32_t bpc) { g_blocks_per_cu = bpc; }
+
+hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
+    if (a.n <= 0) return hipSuccess;
+    bool vec = true;
+    if (mode & M_REDUCE) vec = vec && al(a.grads, 16) && (a.row_stride % 8) == 0;
+    if (mode & (M_ADAM | M_CAST | M_INIT)) vec = vec && al(a.master, 16);
+    if (mode & (M_ADAM | M_INIT)) vec = vec && al(a.m, 16) && al(a.v, 16);
+    if ((mode & M_INIT) || ((mode & M_ADAM) && !(mode & M_REDUCE))) vec = vec && al(a.g_in, 16);
+    if (mode & M_GOUT) vec = vec && al(a.g_out, 16);
+    const int dv = (mode & M_CAST) ? dst_vec(a.p16) : 8;
+    switch (mode) {
+        case M_REDUCE | M_ADAM | M_CAST: return launch_dt<M_REDUCE | M_ADAM | M_CAST>(gdt, pdt, a, vec, dv, s);
+        case M_REDUCE | M_GOUT: return launch_dt<M_REDUCE | M_GOUT>(gdt, ZSMR_BF16, a, vec, 8, s);
+        case M_ADAM: return launch_mode<ZSMR_BF16, ZSMR_BF16, M_ADAM>(a, vec, 8, s);
+        case M_CAST: return launch_dt<M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
+        case M_INIT | M_CAST: return launch_dt<M_INIT | M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+static int copy_width(uintptr_t a, uintptr_t b) {
+    const uintptr_t d = a > b ? a - b : b - a;
+    if (d % 16 == 0) return 16;
+    if (d % 8 == 0) return 8;
+    if (d % 4 == 0) return 4;
+    return 2;
+}
+
+static int64_t head_for(const void* dst, int w, int64_t n) {
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(dst) % static_cast<uintptr_t>(w);
+    int64_t h = mis ? static_cast<int64_t>((w - mis) / 2) : 0;
+    return h < n ? h : n;
+}
+
+hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
+    const int64_t head = head_for(dst, w, n);
+    const dim3 grid(grid_for((n - head) / (w / 2) + 1));
+    switch (w) {
+        case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
+        case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
+        case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
+        default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t each, uint16_t* dst,
+                           hipStream_t s) {
+    if (each <= 0 || nsrc <= 0) return hipSuccess;
+    for (int32_t r0 = 0; r0 < nsrc; r0 += kMaxGather) {
+        const int32_t cnt = nsrc - r0 < kMaxGather ? nsrc - r0 : kMaxGather;
+        GatherArgs g{};
+        g.dst = dst + (int64_t)r0 * each;
+        g.each = each;
+        int w = 16;
+        for (int32_t i = 0; i < cnt; ++i) {
+            const int wi = copy_width(reinterpret_cast<uintptr_t>(srcs[r0 + i]),
+                                      reinterpret_cast<uintptr_t>(g.dst + (int64_t)i * each));
+            if (wi < w) w = wi;
+        }
+        for (int32_t i = 0; i < cnt; ++i) {
+            g.src[i] = srcs[r0 + i];
+            g.head[i] = head_for(g.dst + (int64_t)i * each, w, each);
+        }
+        const int64_t per = each / (w / 2) + 1;
+        const int64_t cap = (int64_t)cu_count() * g_blocks_per_cu;
+        int64_t bx = (per + kThreads - 1) / kThreads;
+        const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
+        if (bx > lim) bx = lim;
+        if (bx < 1) bx = 1;
+        const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(cnt));
+        switch (w) {
+            case 16: hipLaunchKernelGGL(gather16_kernel<16>, grid, dim3(kThreads), 0, s, g); break;
+            case 8: hipLaunchKernelGGL(gather16_kernel<8>, grid, dim3(kThreads), 0, s, g); break;
+            case 4: hipLaunchKernelGGL(gather16_kernel<4>, grid, dim3(kThreads), 0, s, g); break;
+            default: hipLaunchKernelGGL(gather16_kernel<2>, grid, dim3(kThreads), 0, s, g); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace zsmr
