@@ -88,20 +88,50 @@ def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0):
                       f"({elapsed:.1f} s); NumPy single-threaded"}
 
 
+def warm(step, warmup: int, min_seconds: float = 1.0) -> None:
+    """The W untimed warm-up steps, continued until the GPU has been busy for
+    at least ``min_seconds`` (its clocks start from an idle state)."""
+    import torch
+    t, t0 = 0, time.perf_counter()
+    while t < warmup or time.perf_counter() - t0 < min_seconds:
+        t += 1
+        step(t)
+        torch.cuda.synchronize()
+
+
+def copy_ceiling(z, nbytes: int = 4 << 30, reps: int = 10) -> float:
+    """GB/s of the library's own 128-bit copy kernel between two aligned
+    buffers of ``nbytes`` (read + write), measured in the same process."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ctx = z.zero_init_shards(2, 2, 2, "bf16")
+    stream = torch.cuda.current_stream()
+    z.zero_gather_copy(ctx, 0, src, dst, src.numel())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        z.zero_gather_copy(ctx, 0, src, dst, src.numel())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / ms / 1e6
+
+
 def bench_share64(args, w):
     import torch
     import workloads as wl
     import zero_sharded_mixed_reduce_amd as z
 
-    if args.blocks_per_cu:
-        z.zsmr_set_blocks_per_cu(args.blocks_per_cu)
+    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc)
     share = wl.RankShare(w, rank=0)
     share.gen_grads(1)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    for t in range(1, args.warmup + 1):
-        share.step(t)
-    torch.cuda.synchronize()
+    warm(lambda t: share.step(t), args.warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -141,7 +171,8 @@ def bench_share64(args, w):
     return S / (ms_step / 1e3), ms_step, roof, roof_fused, parts, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "owned_shard": S,
         "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
-        "rank": 0, "blocks_per_cu": args.blocks_per_cu or 8}
+        "rank": 0, "step_workgroups_per_cu": args.step_bpc,
+        "copy_workgroups_per_cu": args.copy_bpc}
 
 
 def bench_world(args, w):
@@ -151,8 +182,7 @@ def bench_world(args, w):
     import workloads as wl
     import zero_sharded_mixed_reduce_amd as z
 
-    if args.blocks_per_cu:
-        z.zsmr_set_blocks_per_cu(args.blocks_per_cu)
+    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
         world = wl.Stage3World(w)
@@ -160,9 +190,7 @@ def bench_world(args, w):
         world = wl.ShardedWorld(w)
         world.gen_grads(1)
     timer = wl.Timer(stream)
-    for t in range(1, args.warmup + 1):
-        world.step(t)
-    torch.cuda.synchronize()
+    warm(lambda t: world.step(t), args.warmup)
     timer.reset()
     for i in range(args.steps):
         world.step(args.warmup + 1 + i, timer)
@@ -184,7 +212,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="share64")
-    ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
+    ap.add_argument("--copy-bpc", type=int, default=4, help="workgroups per CU, copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -212,6 +241,11 @@ def main():
         line["roofline_fused_step"] = roof_fused
     if parts:
         line["parts"] = parts
+    import zero_sharded_mixed_reduce_amd as z
+    ceil = copy_ceiling(z)
+    line["copy_ceiling_GBps"] = round(ceil, 1)
+    if "peer_receive" in parts:
+        parts["peer_receive"]["frac_of_copy_ceiling"] = round(parts["peer_receive"]["GBps"] / ceil, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -228,9 +228,11 @@ int32_t zero_stage3_unit_release(zsmr_ctx* ctx, int32_t unit);
 int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
                                int64_t* gathers, int64_t* releases);
 
-/* Launch shape of the streaming kernels: workgroups per compute unit for the
- * grid-stride loops (default 8; 1..64).  Affects speed only, never results. */
-int32_t zsmr_set_blocks_per_cu(int32_t blocks_per_cu);
+/* Launch shape: workgroups per compute unit of the step kernels (reduce,
+ * Adam, cast, fused; default 2) and of the copies (receive and ZeRO-3
+ * gather; default 4); each 1..64.  Process-wide.  Affects speed only, never
+ * results. */
+int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc);
 
 #ifdef __cplusplus
 }

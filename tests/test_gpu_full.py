@@ -1,0 +1,151 @@
+"""Parity at the workloads' full sizes, run exactly as bench.py runs them
+(same drivers, same launch shape).  The oracle recomputes sampled elements
+one by one from regenerated inputs (boundary windows of every shard and unit,
+the ends of each launch's vector range, and random indices); every element is
+also checked against properties that hold at any size: the 16-bit working
+copy is torch's round-to-nearest-even cast of the fp32 master, received peer
+slots equal what was staged, and the counters equal the accounting."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+import zero_sharded_mixed_reduce_amd as z
+from oracle import accounting as acc
+from oracle import sampled
+from oracle.layout import make_layout
+from tests.gpu_helpers import compare, host16, say
+
+pytestmark = pytest.mark.gpu
+
+WINDOW = 2048
+
+
+def windows(starts_ends, lo, hi, n_random, seed):
+    """Positions in [lo, hi): WINDOW-wide windows at each listed position and
+    n_random uniform ones."""
+    pos = []
+    for p in starts_ends:
+        a = max(lo, min(p, hi) - WINDOW // 2)
+        b = min(hi, a + WINDOW)
+        pos.append(np.arange(a, b, dtype=np.int64))
+    rng = np.random.default_rng(seed)
+    pos.append(rng.integers(lo, hi, n_random, dtype=np.int64))
+    return np.unique(np.concatenate(pos))
+
+
+def gather_at(t: torch.Tensor, pos: np.ndarray) -> torch.Tensor:
+    return t[torch.from_numpy(pos).to(t.device)]
+
+
+def cast_matches(master: torch.Tensor, p16: torch.Tensor, dtype: str, chunk=1 << 27) -> int:
+    """Elements where p16 differs from torch's RNE cast of master (on the GPU)."""
+    bad = 0
+    for lo in range(0, master.numel(), chunk):
+        ref = master[lo:lo + chunk].to(wl.TORCH16[dtype]).view(torch.int16)
+        bad += int((ref != p16[lo:lo + chunk].view(torch.int16)).sum().item())
+    return bad
+
+
+def free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check_sampled(w, par_idx, master, m, v, p16, what):
+    want = sampled.trajectory(par_idx, w.world, w.steps, w.dtype, w.grad_sigma, w.lr, w.betas, w.eps,
+                              w.seed, w.outlier_permyriad, w.theta_sigma)
+    return compare({"master": master, "m": m, "v": v}, {"master": want[0], "m": want[1], "v": want[2]},
+                   p16, want[3], what)
+
+
+@pytest.mark.parametrize("key", ["gpt2s", "gpt2xl"])
+def test_sharded_world_full_size(key):
+    w = wl.WORKLOADS[key]
+    say(f"[full] {key}: numel={w.numel} world={w.world} stage={w.stage} T={w.steps}")
+    world = wl.ShardedWorld(w)
+    world.run(w.steps)
+    torch.cuda.synchronize()
+    S, P = world.S, world.P
+    marks = []
+    for r in range(w.world):
+        marks += [r * S, (r + 1) * S - 1]
+    # fp32 byte offsets 2^31 and 2^32 (elements 2^29, 2^30) where they exist
+    marks += [P - 1, P // 2] + [e for e in (1 << 29, 1 << 30) if e < w.numel]
+    pos = windows(marks, 0, w.numel, 1 << 16, seed=len(key))
+    check_sampled(w, pos, gather_at(world.master, pos).cpu().numpy(), gather_at(world.m, pos).cpu().numpy(),
+                  gather_at(world.v, pos).cpu().numpy(), host16(gather_at(world.wc, pos)), f"{key} sampled")
+    assert cast_matches(world.master, world.wc, w.dtype) == 0
+    if P > w.numel:
+        assert not world.master[w.numel:].any() and not world.wc[w.numel:].view(torch.int16).any()
+    lay = make_layout(w.numel, w.world, w.stage, pad=w.pad)
+    want = acc.bytes_per_rank(lay)
+    for r in range(w.world):
+        c = z.zero_counters(world.ctx, r)
+        assert (c["rs_elems"], c["ag_elems"]) == (w.steps * want.rs_elems, w.steps * want.ag_elems)
+    del world
+    free()
+
+
+@pytest.mark.parametrize("rank", [0, 63])
+def test_rank_share_full_size(rank):
+    """One rank of the 7.5e9 / 64 world: S = 117,187,500 is 4 modulo 8, so an
+    odd rank's slot in the working copy is only 8-byte aligned."""
+    w = wl.WORKLOADS["share64"]
+    say(f"[full] share64 rank={rank}")
+    share = wl.RankShare(w, rank=rank)
+    share.run(w.steps)
+    torch.cuda.synchronize()
+    S, off, P = share.S, share.off, share.P
+    pos = windows([0, S - 1, S // 2, (S // 512) * 512, S - 600], 0, S, 1 << 16, seed=rank)
+    check_sampled(w, off + pos, gather_at(share.master, pos).cpu().numpy(),
+                  gather_at(share.m, pos).cpu().numpy(), gather_at(share.v, pos).cpu().numpy(),
+                  host16(gather_at(share.wc, off + pos)), f"share64 rank {rank} sampled")
+    own = share.wc[off:off + S]
+    assert cast_matches(share.master, own, w.dtype) == 0
+    # every peer slot of the 7.5e9-element working copy was received intact
+    # (positions past 2^31 and 2^32 included)
+    for lo, hi in ((0, off), (off + S, P)):
+        for c in range(lo, hi, 1 << 28):
+            e = min(hi, c + (1 << 28))
+            assert torch.equal(share.wc[c:e].view(torch.int16), share.staged[c:e].view(torch.int16))
+    lay = make_layout(w.numel, w.world, w.stage)
+    want = acc.bytes_per_rank(lay)
+    c = z.zero_counters(share.ctx, rank)
+    assert (c["rs_elems"], c["ag_elems"]) == (w.steps * want.rs_elems, w.steps * want.ag_elems)
+    del share, own
+    free()
+
+
+def test_stage3_llama8b_full_size():
+    w = wl.WORKLOADS["llama8b"]
+    say(f"[full] llama8b: units={len(w.units)} numel={w.numel}")
+    s3 = wl.Stage3World(w, check_gathers=True)
+    s3.run(w.steps)
+    torch.cuda.synchronize()
+    assert s3.gather_mismatch == 0
+    lay = make_layout(w.numel, w.world, 3, list(w.units))
+    marks = []
+    for u in range(lay.n_units):
+        for r in range(w.world):
+            off, n = lay.owned(r, u)
+            marks += [off, off + n - 1]
+    marks += [(1 << 31), (1 << 32), lay.padded_numel - 1]
+    pos = windows(marks, 0, lay.padded_numel, 1 << 16, seed=8)
+    par, ok = lay.padded_to_param(pos)
+    assert ok.all()                                   # every unit divides by 8: no pad
+    check_sampled(w, par, gather_at(s3.master, pos).cpu().numpy(), gather_at(s3.m, pos).cpu().numpy(),
+                  gather_at(s3.v, pos).cpu().numpy(), host16(gather_at(s3.p16, pos)), "llama8b sampled")
+    assert cast_matches(s3.master, s3.p16, w.dtype) == 0
+    want = acc.bytes_per_rank(lay)
+    for r in range(w.world):
+        c = z.zero_counters(s3.ctx, r)
+        assert (c["rs_elems"], c["ag_elems"]) == (w.steps * want.rs_elems, w.steps * want.ag_elems)
+    c = z.zero_counters(s3.ctx, 0)
+    assert c["stage3_gathers"] == 2 * lay.n_units * w.steps == c["stage3_releases"]
+    assert c["peak_live_bytes"] == want.gathered and c["live_units"] == 0
+    del s3
+    free()

@@ -504,9 +504,9 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* c, int32_t unit, int32_t* live, i
     return ZSMR_OK;
 }
 
-int32_t zsmr_set_blocks_per_cu(int32_t bpc) {
-    if (bpc < 1 || bpc > 64) return ZSMR_ERR_ARG;
-    zsmr::set_blocks_per_cu(bpc);
+int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc) {
+    if (step_bpc < 1 || step_bpc > 64 || copy_bpc < 1 || copy_bpc > 64) return ZSMR_ERR_ARG;
+    zsmr::set_launch_shape(step_bpc, copy_bpc);
     return ZSMR_OK;
 }
 

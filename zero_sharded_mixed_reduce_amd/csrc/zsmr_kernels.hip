@@ -24,8 +24,31 @@
 
 #pragma clang fp contract(off)
 
-#ifndef ZSMR_NONTEMPORAL
-#define ZSMR_NONTEMPORAL 1
+// Compile-time shape of the streaming loops (tuned on MI355X; results never
+// depend on them).
+#ifndef ZSMR_NT_LOAD
+#define ZSMR_NT_LOAD 1          // non-temporal loads of streamed data
+#endif
+#ifndef ZSMR_NT_STORE
+#define ZSMR_NT_STORE 1         // non-temporal stores
+#endif
+#ifndef ZSMR_ROW_BATCH
+#define ZSMR_ROW_BATCH 8        // gradient rows in flight per lane
+#endif
+#ifndef ZSMR_EARLY_STATE
+#define ZSMR_EARLY_STATE 0      // issue master/m/v loads before the reduce
+#endif
+#ifndef ZSMR_COPY_UNROLL
+#define ZSMR_COPY_UNROLL 1      // 16-byte vectors in flight per lane in copies
+#endif
+#ifndef ZSMR_STEP_CHUNKED
+#define ZSMR_STEP_CHUNKED 0     // step kernel: one contiguous chunk per workgroup
+#endif
+#ifndef ZSMR_COPY_CHUNKED
+#define ZSMR_COPY_CHUNKED 1     // copies: one contiguous chunk per workgroup
+#endif
+#ifndef ZSMR_SPLIT
+#define ZSMR_SPLIT 1            // wave-contiguous element map (see Groups)
 #endif
 
 namespace zsmr {
@@ -36,14 +59,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowBatch = 8;   // gradient rows in flight per lane
-int g_blocks_per_cu = 8;
+constexpr int kRowBatch = ZSMR_ROW_BATCH;
+constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
+// workgroups per compute unit of the grid-stride launches (measured on
+// MI355X: the step kernel streams best with 2, the copies with 4)
+int g_step_bpc = 2;
+int g_copy_bpc = 4;
 
 // Streamed data is touched once per step: non-temporal loads and stores keep
 // it from displacing anything useful in L2 and the MALL.
 template <typename T>
 __device__ __forceinline__ T ld(const T* p) {
-#if ZSMR_NONTEMPORAL
+#if ZSMR_NT_LOAD
     return __builtin_nontemporal_load(p);
 #else
     return *p;
@@ -51,7 +78,7 @@ __device__ __forceinline__ T ld(const T* p) {
 }
 template <typename T>
 __device__ __forceinline__ void st(T* p, T v) {
-#if ZSMR_NONTEMPORAL
+#if ZSMR_NT_STORE
     __builtin_nontemporal_store(v, p);
 #else
     *p = v;
@@ -103,114 +130,179 @@ __device__ __forceinline__ void adam1(const AdamK& k, float g, float& w, float& 
     w = w - u;
 }
 
-// ------------------------------------------------------------ 16-bit store --
+// -------------------------------------------------- 16-bit group store --
+// Four 16-bit results at p (DV: widest store the address allows).
 template <int DV>
-__device__ __forceinline__ void store8x16(uint16_t* p, const uint32_t* h) {
-    if constexpr (DV == 8) {
-        u32x4 w;
+__device__ __forceinline__ void store4x16(uint16_t* p, const uint32_t* h) {
+    if constexpr (DV >= 4) {
+        u32x2 w;
         w[0] = h[0] | (h[1] << 16);
         w[1] = h[2] | (h[3] << 16);
-        w[2] = h[4] | (h[5] << 16);
-        w[3] = h[6] | (h[7] << 16);
-        st(reinterpret_cast<u32x4*>(p), w);
-    } else if constexpr (DV == 4) {
-        u32x2 a, b;
-        a[0] = h[0] | (h[1] << 16);
-        a[1] = h[2] | (h[3] << 16);
-        b[0] = h[4] | (h[5] << 16);
-        b[1] = h[6] | (h[7] << 16);
-        st(reinterpret_cast<u32x2*>(p), a);
-        st(reinterpret_cast<u32x2*>(p + 4), b);
+        st(reinterpret_cast<u32x2*>(p), w);
     } else if constexpr (DV == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st(reinterpret_cast<uint32_t*>(p + 2 * i), h[2 * i] | (h[2 * i + 1] << 16));
+        st(reinterpret_cast<uint32_t*>(p), h[0] | (h[1] << 16));
+        st(reinterpret_cast<uint32_t*>(p + 2), h[2] | (h[3] << 16));
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st(p + i, static_cast<uint16_t>(h[i]));
+        for (int i = 0; i < 4; ++i) st(p + i, static_cast<uint16_t>(h[i]));
     }
 }
 
-__device__ __forceinline__ void load8f(const float* p, float* f) {
-    const f32x4 a = ld(reinterpret_cast<const f32x4*>(p));
-    const f32x4 b = ld(reinterpret_cast<const f32x4*>(p + 4));
+// ------------------------------------------- two 4-element groups per lane --
+// A lane owns elements e0..e0+3 and e1..e1+3.  SPLIT: a wave owns 512
+// consecutive elements, lane l the groups at 4l and 256+4l, so every load
+// and store instruction of the wave covers one contiguous run (1 KB of fp32,
+// 512 B of 16-bit data).  Otherwise e1 = e0 + 4 (8 consecutive elements, one
+// 16-byte load per gradient row).
+template <bool SPLIT>
+struct Groups {
+    // the 8 raw 16-bit words of one row, packed two per dword
+    __device__ static __forceinline__ u32x4 load16raw(const uint16_t* p, uint32_t e0, uint32_t e1) {
+        if constexpr (SPLIT) {
+            const u32x2 a = ld(reinterpret_cast<const u32x2*>(p + e0));
+            const u32x2 b = ld(reinterpret_cast<const u32x2*>(p + e1));
+            u32x4 r;
+            r[0] = a[0];
+            r[1] = a[1];
+            r[2] = b[0];
+            r[3] = b[1];
+            return r;
+        } else {
+            return ld(reinterpret_cast<const u32x4*>(p + e0));
+        }
+    }
+    template <int DV>
+    __device__ static __forceinline__ void store16(uint16_t* p, uint32_t e0, uint32_t e1, const uint32_t* h) {
+        if constexpr (!SPLIT && DV == 8) {
+            u32x4 w;
+            w[0] = h[0] | (h[1] << 16);
+            w[1] = h[2] | (h[3] << 16);
+            w[2] = h[4] | (h[5] << 16);
+            w[3] = h[6] | (h[7] << 16);
+            st(reinterpret_cast<u32x4*>(p + e0), w);
+        } else {
+            store4x16<DV>(p + e0, h);
+            store4x16<DV>(p + e1, h + 4);
+        }
+    }
+    __device__ static __forceinline__ void load32(const float* p, uint32_t e0, uint32_t e1, float* f) {
+        const f32x4 a = ld(reinterpret_cast<const f32x4*>(p + e0));
+        const f32x4 b = ld(reinterpret_cast<const f32x4*>(p + e1));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = a[i];
-        f[4 + i] = b[i];
+        for (int i = 0; i < 4; ++i) {
+            f[i] = a[i];
+            f[4 + i] = b[i];
+        }
     }
-}
-
-__device__ __forceinline__ void store8f(float* p, const float* f) {
-    f32x4 a, b;
+    __device__ static __forceinline__ void store32(float* p, uint32_t e0, uint32_t e1, const float* f) {
+        f32x4 a, b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = f[i];
-        b[i] = f[4 + i];
+        for (int i = 0; i < 4; ++i) {
+            a[i] = f[i];
+            b[i] = f[4 + i];
+        }
+        st(reinterpret_cast<f32x4*>(p + e0), a);
+        st(reinterpret_cast<f32x4*>(p + e1), b);
     }
-    st(reinterpret_cast<f32x4*>(p), a);
-    st(reinterpret_cast<f32x4*>(p + 4), b);
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ void load_rows(const StepArgs& a, int r, uint32_t e0, uint32_t e1, u32x4* buf) {
+    // rows past the last one are clamped to it: every load is issued
+    // unconditionally (so the compiler can count them) and the re-read row
+    // comes from cache; add_rows() skips it
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+        const int rr = r + k < a.nrows ? r + k : a.nrows - 1;
+        buf[k] = Groups<SPLIT>::load16raw(a.grads + (int64_t)rr * a.row_stride, e0, e1);
+    }
 }
 
-// --------------------------------------------------- 8 elements per lane --
-template <int GDT, int PDT, int MODE, int DV>
-__device__ __forceinline__ void body8(const StepArgs& a, int64_t e) {
+template <int GDT>
+__device__ __forceinline__ void add_rows(const StepArgs& a, int r, const u32x4* buf, float* g) {
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+        if (r + k < a.nrows) {
+            float t[8];
+            unpack8<GDT>(buf[k], t);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g[j] = g[j] + t[j];
+        }
+    }
+}
+
+template <bool SPLIT, int GDT, int PDT, int MODE, int DV>
+__device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1) {
+    typedef Groups<SPLIT> G;
     float g[8];
+    float w[8], m[8], v[8];
+    constexpr bool early = ZSMR_EARLY_STATE && (MODE & M_ADAM) && (MODE & M_REDUCE);
+    if constexpr (early) {
+        G::load32(a.master, e0, e1, w);
+        G::load32(a.m, e0, e1, m);
+        G::load32(a.v, e0, e1, v);
+    }
     if constexpr ((MODE & M_REDUCE) != 0) {
-        const uint16_t* p = a.grads + e;
-        unpack8<GDT>(ld(reinterpret_cast<const u32x4*>(p)), g);
-        for (int r = 1; r < a.nrows; r += kRowBatch) {
-            u32x4 buf[kRowBatch];
-#pragma unroll
-            for (int k = 0; k < kRowBatch; ++k)
-                if (r + k < a.nrows)
-                    buf[k] = ld(reinterpret_cast<const u32x4*>(p + (int64_t)(r + k) * a.row_stride));
-#pragma unroll
-            for (int k = 0; k < kRowBatch; ++k) {
-                if (r + k < a.nrows) {
-                    float t[8];
-                    unpack8<GDT>(buf[k], t);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) g[j] = g[j] + t[j];
-                }
+        // rows 1..N-1 in batches, double-buffered so that one batch is in
+        // flight while the previous one is added; the sum itself runs
+        // strictly in rank order 0, 1, ..., N-1
+        u32x4 bufA[kRowBatch], bufB[kRowBatch];
+        const u32x4 row0 = G::load16raw(a.grads, e0, e1);
+        int r = 1;
+        if (a.nrows > 1) load_rows<SPLIT>(a, r, e0, e1, bufA);
+        unpack8<GDT>(row0, g);
+        while (r < a.nrows) {
+            if (r + kRowBatch >= a.nrows) {
+                add_rows<GDT>(a, r, bufA, g);
+                break;
             }
+            load_rows<SPLIT>(a, r + kRowBatch, e0, e1, bufB);
+            add_rows<GDT>(a, r, bufA, g);
+            r += kRowBatch;
+            if (r + kRowBatch >= a.nrows) {
+                add_rows<GDT>(a, r, bufB, g);
+                break;
+            }
+            load_rows<SPLIT>(a, r + kRowBatch, e0, e1, bufA);
+            add_rows<GDT>(a, r, bufB, g);
+            r += kRowBatch;
         }
         if (a.mean) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) g[j] = g[j] / a.nf;
         }
-        if constexpr ((MODE & M_GOUT) != 0) store8f(a.g_out + e, g);
+        if constexpr ((MODE & M_GOUT) != 0) G::store32(a.g_out, e0, e1, g);
     } else if constexpr ((MODE & (M_ADAM | M_INIT)) != 0) {
-        load8f(a.g_in + e, g);
+        G::load32(a.g_in, e0, e1, g);
     }
 
-    float w[8];
     if constexpr ((MODE & M_ADAM) != 0) {
-        float m[8], v[8];
-        load8f(a.master + e, w);
-        load8f(a.m + e, m);
-        load8f(a.v + e, v);
+        if constexpr (!early) {
+            G::load32(a.master, e0, e1, w);
+            G::load32(a.m, e0, e1, m);
+            G::load32(a.v, e0, e1, v);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) adam1(a.k, g[j], w[j], m[j], v[j]);
-        store8f(a.master + e, w);
-        store8f(a.m + e, m);
-        store8f(a.v + e, v);
+        G::store32(a.master, e0, e1, w);
+        G::store32(a.m, e0, e1, m);
+        G::store32(a.v, e0, e1, v);
     } else if constexpr ((MODE & M_INIT) != 0) {
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) w[j] = g[j];
-        store8f(a.master + e, w);
-        store8f(a.m + e, z);
-        store8f(a.v + e, z);
+        G::store32(a.master, e0, e1, w);
+        G::store32(a.m, e0, e1, z);
+        G::store32(a.v, e0, e1, z);
     } else if constexpr ((MODE & M_CAST) != 0) {
-        load8f(a.master + e, w);
+        G::load32(a.master, e0, e1, w);
     }
 
     if constexpr ((MODE & M_CAST) != 0) {
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = narrow<PDT>(w[j]);
-        store8x16<DV>(a.p16 + e, h);
+        G::template store16<DV>(a.p16, e0, e1, h);
     }
 }
 
@@ -247,17 +339,43 @@ __device__ __forceinline__ void body1(const StepArgs& a, int64_t e) {
 }
 
 // ---------------------------------------------------------------- kernels --
-// Aligned path: grid-stride over 8-element vectors; the last n % 8 elements
-// go to the first lanes of workgroup 0.
+constexpr bool kSplit = ZSMR_SPLIT != 0;
+// elements the vector path covers: whole wave tiles (split) or whole 8s
+__host__ __device__ constexpr int64_t vec_elems(int64_t n) { return kSplit ? n / 512 * 512 : n / 8 * 8; }
+
+// Aligned path over vector index i (8 elements each); the elements past the
+// last whole tile go one per lane to workgroup 0.
 template <int GDT, int PDT, int MODE, int DV>
 __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
-    const int64_t nvec = a.n >> 3;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
-        body8<GDT, PDT, MODE, DV>(a, i << 3);
-    const int tail = static_cast<int>(a.n & 7);
-    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail)
-        body1<GDT, PDT, MODE>(a, (nvec << 3) + threadIdx.x);
+    const int64_t n_main = vec_elems(a.n);
+    const int64_t nvec = n_main >> 3;
+    // a launch covers fewer than 2^31 elements (the host splits larger
+    // pieces), so in-launch offsets are 32-bit
+    auto run = [&](uint32_t i) {
+        uint32_t e0, e1;
+        if constexpr (kSplit) {
+            e0 = (i >> 6) * 512u + (i & 63u) * 4u;   // wave tile, lane group
+            e1 = e0 + 256u;
+        } else {
+            e0 = i << 3;
+            e1 = e0 + 4u;
+        }
+        body8<kSplit, GDT, PDT, MODE, DV>(a, e0, e1);
+    };
+    const uint32_t nv = static_cast<uint32_t>(nvec);
+#if ZSMR_STEP_CHUNKED
+    // workgroup b streams vectors [b*chunk, (b+1)*chunk): each row, band and
+    // output is one sequential run per workgroup
+    const uint32_t chunk = ((nv + gridDim.x - 1) / gridDim.x + kThreads - 1) / kThreads * kThreads;
+    const uint32_t lo = blockIdx.x * chunk;
+    const uint32_t hi = lo + chunk < nv ? lo + chunk : nv;
+    for (uint32_t i = lo + threadIdx.x; i < hi; i += kThreads) run(i);
+#else
+    const uint32_t stride = gridDim.x * kThreads;
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) run(i);
+#endif
+    if (blockIdx.x == 0)
+        for (int64_t e = n_main + threadIdx.x; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
 }
 
 // Any-alignment path: one element per lane.
@@ -292,8 +410,35 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
     const int64_t body_end = head + nb * E;
     const V* s = reinterpret_cast<const V*>(src + head);
     V* d = reinterpret_cast<V*>(dst + head);
+#if ZSMR_COPY_CHUNKED
+    // one contiguous chunk per workgroup; kCopyUnroll consecutive groups of
+    // kThreads vectors are loaded before any is stored
+    constexpr int64_t group = (int64_t)kThreads * kCopyUnroll;
+    const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
+    const int64_t lo = part * chunk;
+    const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += group) {
+        V tmp[kCopyUnroll];
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            if (i + k * kThreads < hi) tmp[k] = ld(s + i + k * kThreads);
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            if (i + k * kThreads < hi) st(d + i + k * kThreads, tmp[k]);
+    }
+#else
     const int64_t stride = parts * kThreads;
-    for (int64_t i = part * kThreads + threadIdx.x; i < nb; i += stride) st(d + i, ld(s + i));
+    // kCopyUnroll independent vectors per lane are loaded before any is stored
+    for (int64_t i = part * kThreads + threadIdx.x; i < nb; i += stride * kCopyUnroll) {
+        V tmp[kCopyUnroll];
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            if (i + k * stride < nb) tmp[k] = ld(s + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            if (i + k * stride < nb) st(d + i + k * stride, tmp[k]);
+    }
+#endif
     if (part == 0) {
         const int t = static_cast<int>(threadIdx.x);
         if (t < head) dst[t] = src[t];
@@ -336,8 +481,8 @@ int cu_count() {
     return cus;
 }
 
-unsigned grid_for(int64_t work_items) {
-    const int64_t cap = (int64_t)cu_count() * g_blocks_per_cu;
+unsigned grid_for(int64_t work_items, int bpc) {
+    const int64_t cap = (int64_t)cu_count() * bpc;
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
@@ -347,7 +492,7 @@ unsigned grid_for(int64_t work_items) {
 inline bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 int dst_vec(const void* p) {
-    if (al(p, 16)) return 8;
+    if (al(p, 16) && !kSplit) return 8;
     if (al(p, 8)) return 4;
     if (al(p, 4)) return 2;
     return 1;
@@ -356,11 +501,11 @@ int dst_vec(const void* p) {
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
     if (!vec) {
-        hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n)), dim3(kThreads),
+        hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n, g_step_bpc)), dim3(kThreads),
                            0, s, a);
         return hipGetLastError();
     }
-    const dim3 grid(grid_for((a.n + 7) >> 3));
+    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc));
     switch (dv) {
         case 8: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 8>), grid, dim3(kThreads), 0, s, a); break;
         case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
@@ -381,12 +526,17 @@ hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, bool vec, int dv, hipS
 
 }  // namespace
 
-void set_blocks_per_cu(int32_t bpc) { g_blocks_per_cu = bpc; }
+void set_launch_shape(int32_t step_bpc, int32_t copy_bpc) {
+    g_step_bpc = step_bpc;
+    g_copy_bpc = copy_bpc;
+}
 
-hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
-    if (a.n <= 0) return hipSuccess;
+namespace {
+hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
     bool vec = true;
-    if (mode & M_REDUCE) vec = vec && al(a.grads, 16) && (a.row_stride % 8) == 0;
+    if (mode & M_REDUCE)
+        vec = vec && (kSplit ? al(a.grads, 8) && (a.row_stride % 4) == 0
+                             : al(a.grads, 16) && (a.row_stride % 8) == 0);
     if (mode & (M_ADAM | M_CAST | M_INIT)) vec = vec && al(a.master, 16);
     if (mode & (M_ADAM | M_INIT)) vec = vec && al(a.m, 16) && al(a.v, 16);
     if ((mode & M_INIT) || ((mode & M_ADAM) && !(mode & M_REDUCE))) vec = vec && al(a.g_in, 16);
@@ -400,6 +550,27 @@ hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a, hipStream_
         case M_INIT | M_CAST: return launch_dt<M_INIT | M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
         default: return hipErrorInvalidValue;
     }
+}
+}  // namespace
+
+// Pieces of 2^30 elements or more are cut into launches of at most 2^30
+// (a multiple of every vector width, so alignment is kept).
+hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream_t s) {
+    constexpr int64_t kMaxLaunch = int64_t(1) << 30;
+    for (int64_t c = 0; c < a0.n; c += kMaxLaunch) {
+        StepArgs a = a0;
+        a.n = a0.n - c < kMaxLaunch ? a0.n - c : kMaxLaunch;
+        if (a.grads) a.grads += c;
+        if (a.g_in) a.g_in += c;
+        if (a.g_out) a.g_out += c;
+        if (a.master) a.master += c;
+        if (a.m) a.m += c;
+        if (a.v) a.v += c;
+        if (a.p16) a.p16 += c;
+        const hipError_t e = launch_step_one(mode, gdt, pdt, a, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 static int copy_width(uintptr_t a, uintptr_t b) {
@@ -420,7 +591,7 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     if (n <= 0) return hipSuccess;
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
     const int64_t head = head_for(dst, w, n);
-    const dim3 grid(grid_for((n - head) / (w / 2) + 1));
+    const dim3 grid(grid_for((n - head) / (w / 2) + 1, g_copy_bpc));
     switch (w) {
         case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
         case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
@@ -449,7 +620,7 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
             g.head[i] = head_for(g.dst + (int64_t)i * each, w, each);
         }
         const int64_t per = each / (w / 2) + 1;
-        const int64_t cap = (int64_t)cu_count() * g_blocks_per_cu;
+        const int64_t cap = (int64_t)cu_count() * g_copy_bpc;
         int64_t bx = (per + kThreads - 1) / kThreads;
         const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
         if (bx > lim) bx = lim;
