@@ -126,7 +126,7 @@ def bench_share64(args, w):
     import workloads as wl
     import zero_sharded_mixed_reduce_amd as z
 
-    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc)
+    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
     share = wl.RankShare(w, rank=0)
     share.gen_grads(1)
     stream = torch.cuda.current_stream()
@@ -172,7 +172,8 @@ def bench_share64(args, w):
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "owned_shard": S,
         "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
         "rank": 0, "step_workgroups_per_cu": args.step_bpc,
-        "copy_workgroups_per_cu": args.copy_bpc}
+        "copy_workgroups_per_cu": args.copy_bpc, "fused_defer_tiles": args.defer_tiles,
+        "fused_defer_min_rows": args.defer_min_rows}
 
 
 def bench_world(args, w):
@@ -182,7 +183,7 @@ def bench_world(args, w):
     import workloads as wl
     import zero_sharded_mixed_reduce_amd as z
 
-    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc)
+    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
         world = wl.Stage3World(w)
@@ -214,6 +215,9 @@ def main():
     ap.add_argument("--workload", default="share64")
     ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
     ap.add_argument("--copy-bpc", type=int, default=4, help="workgroups per CU, copies")
+    ap.add_argument("--defer-tiles", type=int, default=5, help="fused-step tiles kept in LDS (0-5)")
+    ap.add_argument("--defer-min-rows", type=int, default=32,
+                    help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -229,10 +229,15 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
                                int64_t* gathers, int64_t* releases);
 
 /* Launch shape: workgroups per compute unit of the step kernels (reduce,
- * Adam, cast, fused; default 2) and of the copies (receive and ZeRO-3
- * gather; default 4); each 1..64.  Process-wide.  Affects speed only, never
+ * Adam, cast, and the fused step when it writes at once; default 2) and of
+ * the copies (receive and ZeRO-3 gather; default 4), each 1..64; defer_tiles,
+ * 0..5 (default 5): how many wave tiles of fused-step results a workgroup
+ * keeps in LDS before writing them in one burst (0 = write at once); and
+ * defer_min_rows >= 1 (default 32): the fewest gradient rows for which the
+ * fused step defers its writes.  Process-wide.  Affects speed only, never
  * results. */
-int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc);
+int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
+                              int32_t defer_min_rows);
 
 #ifdef __cplusplus
 }

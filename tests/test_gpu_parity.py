@@ -20,6 +20,15 @@ pytestmark = pytest.mark.gpu
 TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
 
+@pytest.fixture(params=[5, 0], ids=["deferred", "direct"])
+def fused_path(request):
+    """Run a test with the fused step's deferred-write kernel (default) and
+    with the kernel that writes at once; both must give the same bits."""
+    z.zsmr_set_launch_shape(2, 4, request.param, 1)
+    yield request.param
+    z.zsmr_set_launch_shape()
+
+
 def gpu_scheme(stage, numel, world, dt, T, lr, units=None, pad=False, fused=True, gsig=1e-2,
                check_gathers=True, seed=0):
     """Run a scheme over N simulated ranks through the C ABI only."""
@@ -154,7 +163,7 @@ def check_counters(res, stage, numel, world, units, pad, T):
 # --------------------------------------------- the 65,536 / N = 4 workload --
 @pytest.mark.parametrize("stage", [0, 1, 2, 3])
 @pytest.mark.parametrize("fused", [True, False])
-def test_psi65k_all_schemes(stage, fused):
+def test_psi65k_all_schemes(stage, fused, fused_path):
     numel, world, dt, T, lr, units = 65536, 4, "fp16", 5, 1e-2, [16384] * 4
     res = gpu_scheme(stage, numel, world, dt, T, lr, units, fused=fused)
     ref = oracle_scheme(stage, numel, world, dt, T, lr, units)
@@ -181,7 +190,7 @@ def test_psi65k_stage3_one_unit_is_whole_vector_gather():
     (9, 3, 3, [9], "fp16"),                     # padding inside a single unit
     (65_544, 8, 0, None, "bf16"),               # data parallel, not a multiple of 64
 ])
-def test_ragged_and_padded(numel, world, stage, units, dt):
+def test_ragged_and_padded(numel, world, stage, units, dt, fused_path):
     pad = True
     for fused in (True, False):
         res = gpu_scheme(stage, numel, world, dt, 3, 1e-3, units, pad=pad, fused=fused, gsig=1e-2)
@@ -218,7 +227,7 @@ def _oracle_piece(rows, theta, gdt, pdt, T, lr, steps_rows=None):
     (5, 3, 2),
 ])
 @pytest.mark.parametrize("n", [8 * 256 * 3 + 5, 1, 7, 8, 9])
-def test_alignment_variants(shift16, shift32, gshift, n):
+def test_alignment_variants(shift16, shift32, gshift, n, fused_path):
     world, gdt, pdt, T, lr = 4, "bf16", "bf16", 2, 1e-3
     ctx = z.zero_init_shards(n * world, world, 2, gdt, pdt)
     rows, theta = _piece_inputs(n, world, gdt)
@@ -248,7 +257,7 @@ def test_alignment_variants(shift16, shift32, gshift, n):
 
 
 @pytest.mark.parametrize("gdt,pdt", [("fp16", "bf16"), ("bf16", "fp16"), ("fp16", "fp16")])
-def test_mixed_formats(gdt, pdt):
+def test_mixed_formats(gdt, pdt, fused_path):
     n, world, T, lr = 3 * 2048 + 3, 8, 3, 1e-2
     ctx = z.zero_init_shards(n * world, world, 1, gdt, pdt)
     steps_rows = {t: _piece_inputs(n, world, gdt, step=t)[0] for t in range(1, T + 1)}
@@ -264,6 +273,31 @@ def test_mixed_formats(gdt, pdt):
     master, m, v, p16 = _oracle_piece(None, theta, gdt, pdt, T, lr, steps_rows)
     compare({"master": host32(mb), "m": host32(mm), "v": host32(vb)},
             {"master": master, "m": m, "v": v}, host16(pb), p16, f"mixed {gdt}->{pdt}")
+
+
+@pytest.mark.parametrize("tiles", [5, 3, 1])
+def test_deferred_kernel_many_rounds(tiles):
+    """Several rounds of the deferred-write kernel (each round covers 256
+    workgroups x tiles x 256 lanes x 8 elements) and a ragged tail."""
+    z.zsmr_set_launch_shape(2, 4, tiles, 1)
+    try:
+        n = 2 * 256 * tiles * 256 * 8 + 3 * 512 + 77
+        world, T, lr = 4, 2, 1e-3
+        ctx = z.zero_init_shards(n * world, world, 2, "bf16")
+        steps_rows = {t: _piece_inputs(n, world, "bf16", step=t)[0] for t in range(1, T + 1)}
+        theta = synth.theta0(0, np.arange(n))
+        mb = torch.from_numpy(theta.copy()).cuda()
+        mm, vb = torch.empty_like(mb), torch.empty_like(mb)
+        pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        z.zero_init_state(ctx, 0, 0, mb.clone(), mb, mm, vb, pb)
+        for t in range(1, T + 1):
+            z.zero_fused_step(ctx, 0, 0, dev16(steps_rows[t].ravel()), n, 0, mb, mm, vb, pb, t, lr)
+        torch.cuda.synchronize()
+        master, m, v, p16 = _oracle_piece(None, theta, "bf16", "bf16", T, lr, steps_rows)
+        compare({"master": host32(mb), "m": host32(mm), "v": host32(vb)},
+                {"master": master, "m": m, "v": v}, host16(pb), p16, f"deferred tiles={tiles} n={n}")
+    finally:
+        z.zsmr_set_launch_shape()
 
 
 @pytest.mark.parametrize("gdt", ["bf16", "fp16"])

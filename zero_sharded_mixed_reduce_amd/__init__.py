@@ -81,7 +81,7 @@ SIGNATURES = {
     "zero_stage3_unit_release": (_i32, [_vp, _i32]),
     "zero_stage3_unit_state": (_i32, [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
                                       ctypes.POINTER(_i64)]),
-    "zsmr_set_launch_shape": (_i32, [_i32, _i32]),
+    "zsmr_set_launch_shape": (_i32, [_i32, _i32, _i32, _i32]),
 }
 
 _LIB = None
@@ -270,5 +270,7 @@ def zero_stage3_unit_state(ctx: Ctx, unit: int):
     return bool(live.value), g.value, r.value
 
 
-def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 4) -> None:
-    _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc)), "zsmr_set_launch_shape")
+def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 4, defer_tiles: int = 5,
+                          defer_min_rows: int = 32) -> None:
+    _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc), int(defer_tiles),
+                                        int(defer_min_rows)), "zsmr_set_launch_shape")

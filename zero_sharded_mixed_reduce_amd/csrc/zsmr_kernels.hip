@@ -65,6 +65,13 @@ constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // MI355X: the step kernel streams best with 2, the copies with 4)
 int g_step_bpc = 2;
 int g_copy_bpc = 4;
+// the fused step's deferred-write kernel: tiles kept in LDS per workgroup
+// (0 = write at once with step_vec8_kernel) and workgroups per CU
+int g_defer_tiles = 5;
+int g_defer_bpc = 1;
+// ... used when a step reduces at least this many rows (below it the
+// read:write ratio is low and one workgroup per CU streams too little)
+int g_defer_min_rows = 32;
 
 // Streamed data is touched once per step: non-temporal loads and stores keep
 // it from displacing anything useful in L2 and the MALL.
@@ -231,8 +238,16 @@ __device__ __forceinline__ void add_rows(const StepArgs& a, int r, const u32x4* 
     }
 }
 
-template <bool SPLIT, int GDT, int PDT, int MODE, int DV>
-__device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1) {
+// Results of the fused step for one lane's 8 elements, when they are kept on
+// chip instead of being stored at once (the deferred-write kernel).
+struct Out8 {
+    float w[8], m[8], v[8];
+    uint32_t h[8];
+};
+
+template <bool SPLIT, int GDT, int PDT, int MODE, int DV, bool DEFER = false>
+__device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1, Out8* out = nullptr) {
+    static_assert(!DEFER || MODE == (M_REDUCE | M_ADAM | M_CAST), "only the fused step defers");
     typedef Groups<SPLIT> G;
     float g[8];
     float w[8], m[8], v[8];
@@ -284,9 +299,18 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) adam1(a.k, g[j], w[j], m[j], v[j]);
-        G::store32(a.master, e0, e1, w);
-        G::store32(a.m, e0, e1, m);
-        G::store32(a.v, e0, e1, v);
+        if constexpr (DEFER) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                out->w[j] = w[j];
+                out->m[j] = m[j];
+                out->v[j] = v[j];
+            }
+        } else {
+            G::store32(a.master, e0, e1, w);
+            G::store32(a.m, e0, e1, m);
+            G::store32(a.v, e0, e1, v);
+        }
     } else if constexpr ((MODE & M_INIT) != 0) {
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -302,7 +326,12 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = narrow<PDT>(w[j]);
-        G::template store16<DV>(a.p16, e0, e1, h);
+        if constexpr (DEFER) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) out->h[j] = h[j];
+        } else {
+            G::template store16<DV>(a.p16, e0, e1, h);
+        }
     }
 }
 
@@ -376,6 +405,78 @@ __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
 #endif
     if (blockIdx.x == 0)
         for (int64_t e = n_main + threadIdx.x; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
+}
+
+// The fused step with deferred writes.  Mixing a write stream into the
+// 2N-row read stream costs HBM throughput out of proportion to the bytes
+// written; a workgroup therefore computes KD wave tiles, keeps their results
+// (master, m, v and the 16-bit copy: 112 B per lane per tile) in LDS, and
+// only then writes them in one burst.  Each lane reads back only what it
+// wrote itself, so the barriers only line the workgroup's waves up; results
+// are the same bits as step_vec8_kernel's.  KD = 5 fills 140 KB of LDS, one
+// workgroup per CU.
+template <int GDT, int PDT, int DV, int KD>
+__global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a) {
+    static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
+    constexpr int MODE = M_REDUCE | M_ADAM | M_CAST;
+    __shared__ float s_w[KD][8][kThreads];
+    __shared__ float s_m[KD][8][kThreads];
+    __shared__ float s_v[KD][8][kThreads];
+    __shared__ uint32_t s_h[KD][4][kThreads];
+    const int t = threadIdx.x;
+    const uint32_t nv = static_cast<uint32_t>(vec_elems(a.n) >> 3);
+    const uint32_t per_block = KD * kThreads;
+    const uint32_t per_round = gridDim.x * per_block;
+    const uint32_t rounds = (nv + per_round - 1) / per_round;
+    for (uint32_t rd = 0; rd < rounds; ++rd) {
+        const uint32_t base = rd * per_round + blockIdx.x * per_block;
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            const uint32_t i = base + k * kThreads + t;
+            if (i < nv) {
+                const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;
+                Out8 o;
+                body8<true, GDT, PDT, MODE, DV, true>(a, e0, e0 + 256u, &o);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    s_w[k][j][t] = o.w[j];
+                    s_m[k][j][t] = o.m[j];
+                    s_v[k][j][t] = o.v[j];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_h[k][j][t] = o.h[2 * j] | (o.h[2 * j + 1] << 16);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            const uint32_t i = base + k * kThreads + t;
+            if (i < nv) {
+                const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;
+                const uint32_t e1 = e0 + 256u;
+                float w[8], m[8], v[8];
+                uint32_t h[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    w[j] = s_w[k][j][t];
+                    m[j] = s_m[k][j][t];
+                    v[j] = s_v[k][j][t];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h[2 * j] = s_h[k][j][t] & 0xffffu;
+                    h[2 * j + 1] = s_h[k][j][t] >> 16;
+                }
+                Groups<true>::store32(a.master, e0, e1, w);
+                Groups<true>::store32(a.m, e0, e1, m);
+                Groups<true>::store32(a.v, e0, e1, v);
+                Groups<true>::template store16<DV>(a.p16, e0, e1, h);
+            }
+        }
+        __syncthreads();
+    }
+    if (blockIdx.x == 0)
+        for (int64_t e = vec_elems(a.n) + t; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
 }
 
 // Any-alignment path: one element per lane.
@@ -498,8 +599,31 @@ int dst_vec(const void* p) {
     return 1;
 }
 
+template <int GDT, int PDT, int DV>
+hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
+    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_defer_bpc));
+    switch (g_defer_tiles) {
+        case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 2>), grid, dim3(kThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 3>), grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 4>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 5>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
+    if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST) && kSplit) {
+        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows) {
+            switch (dv) {
+                case 8:
+                case 4: return launch_deferred<GDT, PDT, 4>(a, s);
+                case 2: return launch_deferred<GDT, PDT, 2>(a, s);
+                default: return launch_deferred<GDT, PDT, 1>(a, s);
+            }
+        }
+    }
     if (!vec) {
         hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n, g_step_bpc)), dim3(kThreads),
                            0, s, a);
@@ -526,9 +650,12 @@ hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, bool vec, int dv, hipS
 
 }  // namespace
 
-void set_launch_shape(int32_t step_bpc, int32_t copy_bpc) {
+void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
+                      int32_t defer_min_rows) {
     g_step_bpc = step_bpc;
     g_copy_bpc = copy_bpc;
+    g_defer_tiles = defer_tiles;
+    g_defer_min_rows = defer_min_rows;
 }
 
 namespace {

@@ -42,6 +42,7 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
 // dst[r*each + j] = srcs[r][j], r < nsrc
 hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t each,
                            uint16_t* dst, hipStream_t stream);
-void set_launch_shape(int32_t step_bpc, int32_t copy_bpc);
+void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
+                      int32_t defer_min_rows);
 
 }  // namespace zsmr
