@@ -160,14 +160,17 @@ def bench_share64(args, w):
         "step_GBps": round((fused_bytes + recv_bytes) / ms_step / 1e6, 1),
     }
     dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
-    kname = {"fused_step": "step_vec8_kernel", "peer_receive": "copy16_kernel"}[dom]
+    fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
+                    else "step_vec8_kernel")
+    kname = {"fused_step": fused_kernel, "peer_receive": "copy16_kernel"}[dom]
     roof = {"bound": "hbm", "achieved": parts[dom]["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": parts[dom]["frac"], "traffic": read_traffic(kname, w.key),
             "kernel": kname, "algorithmic_bytes_per_launch": parts[dom]["bytes"]}
     # the hot path's own kernel, reported beside the dominant one
     roof_fused = {"bound": "hbm", "achieved": parts["fused_step"]["GBps"], "peak": PEAK_HBM_GBPS,
                   "unit": "GB/s", "frac": parts["fused_step"]["frac"],
-                  "traffic": read_traffic("step_vec8_kernel", w.key)}
+                  "traffic": read_traffic(fused_kernel, w.key), "kernel": fused_kernel,
+                  "algorithmic_bytes_per_launch": fused_bytes}
     return S / (ms_step / 1e3), ms_step, roof, roof_fused, parts, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "owned_shard": S,
         "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
