@@ -149,3 +149,62 @@ def test_stage3_llama8b_full_size():
     assert c["peak_live_bytes"] == want.gathered and c["live_units"] == 0
     del s3
     free()
+
+
+@pytest.mark.parametrize("defer", [0, 5])
+def test_piece_larger_than_one_launch(defer):
+    """A piece of 2^30 + 1,029 elements: the host cuts it into a launch of
+    2^30 elements and one of the rest (a partial wave tile plus a ragged
+    tail); checked around the cut and at the ends."""
+    import synth
+    import synth.gpu as sgpu
+    z.zsmr_set_launch_shape(2, 4, defer, 1)
+    try:
+        n, world, T, lr = (1 << 30) + 1029, 2, 2, 1e-3
+        say(f"[full] piece over 2^30: n={n} defer={defer}")
+        ctx = z.zero_init_shards(n * world, world, 2, "bf16")
+        grads = torch.empty(world * n, dtype=torch.bfloat16, device="cuda")
+        theta = torch.empty(n, dtype=torch.float32, device="cuda")
+        sgpu.fill32(theta, n, 0, n, 0, synth.TAG_THETA, 0, 0, 0.02)
+        master, m, v = torch.empty_like(theta), torch.empty_like(theta), torch.empty_like(theta)
+        p16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        z.zero_init_state(ctx, 0, 0, theta, master, m, v, p16)
+        del theta
+        for t in range(1, T + 1):
+            sgpu.fill16(grads, world, n, n, 0, n, 0, synth.TAG_GRAD, 0, t, 1e-3, "bf16")
+            z.zero_fused_step(ctx, 0, 0, grads, n, 0, master, m, v, p16, t, lr)
+        torch.cuda.synchronize()
+        pos = windows([0, 1 << 30, n - 1, (1 << 30) - 512, n - 1029], 0, n, 1 << 14, seed=30)
+        want = sampled.trajectory(pos, world, T, "bf16", 1e-3, lr)
+        compare({"master": gather_at(master, pos).cpu().numpy(), "m": gather_at(m, pos).cpu().numpy(),
+                 "v": gather_at(v, pos).cpu().numpy()},
+                {"master": want[0], "m": want[1], "v": want[2]}, host16(gather_at(p16, pos)), want[3],
+                f"piece over 2^30 defer={defer}")
+        assert cast_matches(master, p16, "bf16") == 0
+        del grads, master, m, v, p16
+    finally:
+        z.zsmr_set_launch_shape()
+        free()
+
+
+def test_stage3_gather_more_ranks_than_one_launch():
+    """A ZeRO-3 gather over 100 ranks takes two launches (64 shard pointers
+    each at most); padded units; every gathered unit equals its shards."""
+    world, units = 100, [100 * 37, 100 * 5 + 3, 7]
+    numel = sum(units)
+    ctx = z.zero_init_shards(numel, world, 3, "fp16", pad=True, units=units)
+    info = ctx.info()
+    shards = torch.arange(info["padded_numel"], dtype=torch.int32, device="cuda").to(torch.int16)
+    buf = torch.full((info["max_unit_numel"] + 8,), -1, dtype=torch.int16, device="cuda")
+    for u in range(len(units)):
+        q0, su, _ = z.zero_layout(ctx, 0, u)
+        ptrs = [shards[z.zero_layout(ctx, r, u)[0]:] for r in range(world)]
+        z.zero_stage3_unit_gather(ctx, u, ptrs, buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf[:world * su], shards[q0:q0 + world * su]), f"unit {u}"
+        if u == 0:                       # the widest unit: nothing written past it
+            assert bool((buf[world * su:] == -1).all())
+        z.zero_stage3_unit_release(ctx, u)
+    c = z.zero_counters(ctx, 17)
+    lay = make_layout(numel, world, 3, units, pad=True)
+    assert c["ag_elems"] == (world - 1) * lay.shard_numel

@@ -47,6 +47,9 @@
 #ifndef ZSMR_COPY_CHUNKED
 #define ZSMR_COPY_CHUNKED 1     // copies: one contiguous chunk per workgroup
 #endif
+#ifndef ZSMR_COPY_STAGE
+#define ZSMR_COPY_STAGE 4       // 128-bit copies: vectors per lane staged in LDS per burst
+#endif
 #ifndef ZSMR_SPLIT
 #define ZSMR_SPLIT 1            // wave-contiguous element map (see Groups)
 #endif
@@ -511,6 +514,29 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
     const int64_t body_end = head + nb * E;
     const V* s = reinterpret_cast<const V*>(src + head);
     V* d = reinterpret_cast<V*>(dst + head);
+    if constexpr (W == 16 && ZSMR_COPY_STAGE > 0) {
+        // one contiguous chunk per workgroup, moved in bursts: the workgroup
+        // loads kStage groups of kThreads vectors into LDS, then stores them.
+        // Each lane reads back only its own slots; the barriers just line the
+        // waves up so that reads and writes reach HBM in separate bursts.
+        constexpr int kStage = ZSMR_COPY_STAGE;
+        __shared__ V stage[kStage][kThreads];
+        constexpr int64_t group = (int64_t)kThreads * kStage;
+        const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
+        const int64_t lo = part * chunk;
+        const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
+        const int t = static_cast<int>(threadIdx.x);
+        for (int64_t b = lo; b < hi; b += group) {
+#pragma unroll
+            for (int k = 0; k < kStage; ++k)
+                if (b + k * kThreads + t < hi) stage[k][t] = ld(s + b + k * kThreads + t);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kStage; ++k)
+                if (b + k * kThreads + t < hi) st(d + b + k * kThreads + t, stage[k][t]);
+            __syncthreads();
+        }
+    } else {
 #if ZSMR_COPY_CHUNKED
     // one contiguous chunk per workgroup; kCopyUnroll consecutive groups of
     // kThreads vectors are loaded before any is stored
@@ -540,6 +566,7 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
             if (i + k * stride < nb) st(d + i + k * stride, tmp[k]);
     }
 #endif
+    }
     if (part == 0) {
         const int t = static_cast<int>(threadIdx.x);
         if (t < head) dst[t] = src[t];
