@@ -123,6 +123,40 @@ def copy_reference(z, nbytes: int, reps: int = 5) -> float:
     return 2 * nbytes / ms / 1e6
 
 
+def bucketed_overlap(share, args, reps: int = 5) -> dict:
+    """Steps that include the simulated backward pass (the gradient fill of
+    all 64 rows): sequential (fill everything, then one fused launch) against
+    bucketed (each bucket's fill on a second stream, its fused launch as soon
+    as it is ready).  Reported beside the headline, which excludes the fill."""
+    import torch
+    side = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(2 + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def sequential(t):
+        share.gen_grads(t)
+        share.step(t)
+
+    seq = timed(sequential)
+    fill = timed(share.gen_grads)
+    buck = timed(lambda t: share.step_bucketed(t, args.buckets, side))
+    share.gen_grads(1)
+    torch.cuda.synchronize()
+    return {"n_buckets": args.buckets, "backward_fill_ms": round(fill, 4),
+            "sequential_ms": round(seq, 4), "bucketed_overlapped_ms": round(buck, 4),
+            "hidden_fraction_of_step": round((seq - buck) / (seq - fill), 4) if seq > fill else None}
+
+
 def bench_share64(args, w):
     import torch
     import workloads as wl
@@ -150,6 +184,7 @@ def bench_share64(args, w):
     ms_step = wall * 1e3 / args.steps
 
     S, N = share.S, w.world
+    bucketed = bucketed_overlap(share, args) if args.buckets else None
     fused_bytes = S * (2 * N + 26)              # N x 2 B grads, 24 B master/m/v r+w, 2 B cast
     recv_bytes = (share.P - S) * 4              # 2 B read + 2 B written per peer element
     parts = {
@@ -161,6 +196,8 @@ def bench_share64(args, w):
                          "frac": round(recv_bytes / recv_ms / 1e6 / PEAK_HBM_GBPS, 4)},
         "step_GBps": round((fused_bytes + recv_bytes) / ms_step / 1e6, 1),
     }
+    if bucketed:
+        parts["bucketed_with_backward"] = bucketed
     dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
     fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
                     else "step_vec8_kernel")
@@ -191,16 +228,21 @@ def bench_world(args, w):
     z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
-        world = wl.Stage3World(w)
+        # each unit size's gradients are made once, so that whole steps --
+        # gathers, fused launches and (with --prefetch) the overlap of the next
+        # gather -- are timed end to end on the compute stream
+        world = wl.Stage3World(w, prefetch=args.prefetch, fixed_grads=True)
     else:
         world = wl.ShardedWorld(w)
         world.gen_grads(1)
-    timer = wl.Timer(stream)
     warm(lambda t: world.step(t), args.warmup)
-    timer.reset()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(args.steps):
-        world.step(args.warmup + 1 + i, timer)
-    ms_step = timer.ms() / args.steps
+        world.step(args.warmup + 1 + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
     N = w.world
     byts = w.numel * (2 * N + 26) + (8 * w.numel if w.stage == 3 else 0)
     gbps = byts / ms_step / 1e6
@@ -209,7 +251,7 @@ def bench_world(args, w):
             "kernel": "step_vec8_kernel", "algorithmic_bytes_per_step": byts}
     return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
-        "steps_T": w.steps, "lr": w.lr}
+        "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3)}
 
 
 def main():
@@ -224,6 +266,10 @@ def main():
     ap.add_argument("--defer-min-rows", type=int, default=32,
                     help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="ZeRO-3 workload: gather the next unit while the current one is in use")
+    ap.add_argument("--buckets", type=int, default=0,
+                    help="share64: also measure steps with the simulated backward, bucketed")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the N ranks of the ZeRO world are simulated in "

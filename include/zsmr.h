@@ -201,6 +201,20 @@ int32_t zero_fused_step(zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* g
                         float* v, void* p16_dst, int32_t t, const zsmr_adam* hp,
                         hipStream_t stream);
 
+/* The fused step on elements [begin, begin + count) of the (rank, unit)
+ * piece only, for gradients that arrive in buckets during the backward pass
+ * ("ZeRO and FSDP", the remark that real ZeRO-2 reduce-scatters bucket by
+ * bucket during backward; "ZeRO, annotated" section 5.2 and 6.2, buckets and
+ * constant-size buffers).  Pointers and base_elem refer to the whole piece,
+ * exactly as for zero_fused_step; the call touches only the sub-range.
+ * Calls over disjoint sub-ranges that cover the piece, with the same t, give
+ * the same bits as one zero_fused_step.  ZSMR_ERR_ARG if begin < 0, count < 0
+ * or begin + count exceeds the piece.  Counts count elements of traffic. */
+int32_t zero_fused_step_range(zsmr_ctx* ctx, int32_t rank, int32_t unit, int64_t begin,
+                              int64_t count, const void* grads, int64_t row_stride,
+                              int64_t base_elem, float* master, float* m, float* v,
+                              void* p16_dst, int32_t t, const zsmr_adam* hp, hipStream_t stream);
+
 /* All-gather receive: copy n 16-bit elements src -> dst (peers' slices into
  * the working copy of recv_rank); counted as all-gather traffic received by
  * recv_rank.  Overlapping src and dst is not allowed. */

@@ -172,3 +172,16 @@ def test_stage3_state_errors_on_the_host():
     with pytest.raises(z.ZsmrError) as e:
         z.zsmr_set_launch_shape(2, 4, 5, 0)
     assert e.value.code == z.ZSMR_ERR_ARG
+
+
+def test_fused_range_bounds_are_checked_on_the_host():
+    ctx = z.zero_init_shards(64, 4, 2, "bf16")
+    ok = 1 << 20
+    for begin, count in ((-1, 4), (0, -1), (10, 7), (17, 0), (0, 17)):
+        with pytest.raises(z.ZsmrError) as e:
+            z.zero_fused_step_range(ctx, 0, 0, begin, count, ok, 16, 0, ok, ok, ok, ok, 1, 1e-3,
+                                    stream=0)
+        assert e.value.code == z.ZSMR_ERR_ARG, (begin, count)
+    for begin in (0, 7, 16):                   # empty ranges inside the piece are no-ops
+        z.zero_fused_step_range(ctx, 1, 0, begin, 0, ok, 16, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
+    assert z.zero_counters(ctx, 1)["traffic_elems"] == 0

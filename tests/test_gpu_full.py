@@ -208,3 +208,82 @@ def test_stage3_gather_more_ranks_than_one_launch():
     c = z.zero_counters(ctx, 17)
     lay = make_layout(numel, world, 3, units, pad=True)
     assert c["ag_elems"] == (world - 1) * lay.shard_numel
+
+
+def _small_stage3():
+    units = (3 * 1 << 20, 1 << 20, 5 * 1 << 19, 1 << 20)
+    return wl.Workload("s3small", "stage3_small_4_units_n8_bf16", sum(units), 8, 3, "bf16", 1e-3, 1e-4,
+                       2, units=units)
+
+
+def test_stage3_prefetch_matches_plain_schedule():
+    """Gathering the next unit on a second stream while the current one is in
+    use (two units live) gives the same bits as the plain schedule; only the
+    peak changes, to the largest pair of adjacent units."""
+    w = _small_stage3()
+    plain = wl.Stage3World(w, check_gathers=True)
+    plain.run(w.steps)
+    pre = wl.Stage3World(w, check_gathers=True, prefetch=True)
+    pre.run(w.steps)
+    torch.cuda.synchronize()
+    assert plain.gather_mismatch == 0 and pre.gather_mismatch == 0
+    for a, b in ((plain.master, pre.master), (plain.m, pre.m), (plain.v, pre.v)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(plain.p16.view(torch.int16), pre.p16.view(torch.int16))
+    lay = make_layout(w.numel, w.world, 3, list(w.units))
+    c_plain, c_pre = z.zero_counters(plain.ctx, 0), z.zero_counters(pre.ctx, 0)
+    assert c_pre["stage3_gathers"] == c_plain["stage3_gathers"] == 2 * lay.n_units * w.steps
+    assert c_pre["ag_elems"] == c_plain["ag_elems"]
+    assert c_plain["peak_live_bytes"] == acc.bytes_per_rank(lay, max_live=1).gathered
+    assert c_pre["peak_live_bytes"] == acc.bytes_per_rank(lay, max_live=2).gathered
+    del plain, pre
+    free()
+
+
+@pytest.mark.parametrize("n_buckets", [1, 3, 16])
+def test_bucketed_step_matches_one_launch(n_buckets):
+    """Gradients arriving in buckets (last parameters first, filled on a
+    second stream) and consumed bucket by bucket give the same bits as one
+    fused launch over the shard."""
+    S = 2_000_003
+    w = wl.Workload("share64small", "one_rank_share_small_n64_zero2_bf16", 64 * S, 64, 2, "bf16",
+                    1e-3, 1e-4, 2)
+    ref = wl.RankShare(w, rank=5)
+    ref.run(w.steps)
+    bk = wl.RankShare(w, rank=5)
+    side = torch.cuda.Stream()
+    for t in range(1, w.steps + 1):
+        bk.step_bucketed(t, n_buckets, side)
+    torch.cuda.synchronize()
+    for a, b in ((ref.master, bk.master), (ref.m, bk.m), (ref.v, bk.v)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(ref.wc.view(torch.int16), bk.wc.view(torch.int16))
+    assert z.zero_counters(ref.ctx, 5) == z.zero_counters(bk.ctx, 5)
+    del ref, bk
+    free()
+
+
+def test_fused_ranges_with_ragged_unaligned_cuts():
+    """Sub-ranges whose ends fall anywhere (odd offsets, so the 16-byte
+    vector path and the one-element path both run) give the bits of one
+    zero_fused_step over the shard, and count the same traffic."""
+    w = wl.Workload("cuts", "one_rank_share_ragged_cuts_n64_zero2_bf16", 64 * 300_007, 64, 2,
+                    "bf16", 1e-3, 1e-4, 2)
+    ref, cut = wl.RankShare(w, rank=63), wl.RankShare(w, rank=63)
+    S = ref.S
+    edges = [0, 1, 513, 777, 4096, 150_001, S - 3, S]
+    for t in (1, 2):
+        ref.gen_grads(t)
+        cut.gen_grads(t)
+        ref.fused(t)
+        for b0, b1 in zip(edges[:-1], edges[1:]):
+            z.zero_fused_step_range(cut.ctx, 63, 0, b0, b1 - b0, cut.grads, cut.row_stride, 0,
+                                    cut.master, cut.m, cut.v, cut.wc[cut.off:], t, w.lr, w.betas,
+                                    w.eps)
+    torch.cuda.synchronize()
+    for a, b in ((ref.master, cut.master), (ref.m, cut.m), (ref.v, cut.v)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(ref.wc.view(torch.int16), cut.wc.view(torch.int16))
+    assert z.zero_counters(ref.ctx, 63) == z.zero_counters(cut.ctx, 63)
+    del ref, cut
+    free()

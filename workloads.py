@@ -230,6 +230,38 @@ class RankShare:
             self.gen_grads(t)
             self.step(t, timer)
 
+    def bucket_bounds(self, n_buckets: int):
+        """[begin, end) of each bucket of the owned shard, in the order a
+        backward pass produces them (last parameters first); boundaries are
+        multiples of 512 elements (one wave tile)."""
+        size = -(-self.S // n_buckets + 511) // 512 * 512
+        edges = list(range(0, self.S, size)) + [self.S]
+        return [(edges[i], edges[i + 1]) for i in reversed(range(len(edges) - 1))]
+
+    def step_bucketed(self, t: int, n_buckets: int, backward_stream, generate: bool = True):
+        """One step whose gradients arrive in buckets: the simulated backward
+        (the input generator, on ``backward_stream``) fills one bucket of all
+        N rows at a time, and the fused step consumes each bucket on the
+        current stream as soon as it is ready, overlapping the two."""
+        w = self.w
+        compute = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(compute)
+        backward_stream.wait_event(start)
+        for b0, b1 in self.bucket_bounds(n_buckets):
+            if generate:
+                with torch.cuda.stream(backward_stream):
+                    sgpu.fill16(self.grads[b0:], w.world, self.row_stride, b1 - b0, self.off + b0,
+                                b1 - b0, w.seed, synth.TAG_GRAD, 0, t, w.grad_sigma, w.dtype,
+                                w.outlier_permyriad, stream=backward_stream)
+            ready = torch.cuda.Event()
+            ready.record(backward_stream)
+            compute.wait_event(ready)
+            z.zero_fused_step_range(self.ctx, self.rank, 0, b0, b1 - b0, self.grads, self.row_stride,
+                                    0, self.master, self.m, self.v, self.wc[self.off:], t, w.lr,
+                                    w.betas, w.eps)
+        self.receive()
+
 
 # ---------------------------------------------------------------- stage 3 --
 class Stage3World:
@@ -239,10 +271,20 @@ class Stage3World:
     gradients of one unit (N rows of N*S_u) are generated when the backward
     pass reaches it."""
 
-    def __init__(self, w: Workload, device="cuda", check_gathers: bool = False):
+    def __init__(self, w: Workload, device="cuda", check_gathers: bool = False,
+                 prefetch: bool = False, fixed_grads: bool = False):
+        """prefetch: gather the next unit on a second stream while the current
+        one is in use (two unit buffers, at most two units live).
+        fixed_grads: generate each unit size's gradients once and reuse them
+        in every step (timing runs; the values then differ from the per-step
+        recipe, so parity runs leave it off)."""
         self.w = w
+        self.prefetch = prefetch
+        self.fixed_grads = fixed_grads
         self.ctx = z.zero_init_shards(w.numel, w.world, 3, w.dtype, pad=w.pad,
                                       units=list(w.units) if w.units else None)
+        if prefetch:
+            z.zero_stage3_set_max_live(self.ctx, 2)
         info = self.ctx.info()
         self.P = info["padded_numel"]
         self.U = info["n_units"]
@@ -259,10 +301,23 @@ class Stage3World:
         self.m = torch.empty_like(self.master)
         self.v = torch.empty_like(self.master)
         self.p16 = empty16(self.P, w.dtype, device)
-        self.unit_buf = empty16(self.maxw, w.dtype, device)
-        self.grads = empty16(w.world * self.maxw, w.dtype, device)
+        self.unit_bufs = [empty16(self.maxw, w.dtype, device) for _ in range(2 if prefetch else 1)]
+        self.unit_buf = self.unit_bufs[0]
         self.check_gathers = check_gathers
         self.gather_mismatch = 0
+        self.gather_stream = torch.cuda.Stream() if prefetch else None
+        if fixed_grads:
+            # one gradient set per distinct unit width, made once (step 1)
+            self.grads_by_width = {}
+            for u in range(self.U):
+                width = w.world * self.S_u[u]
+                if width not in self.grads_by_width:
+                    g = empty16(w.world * width, w.dtype, device)
+                    sgpu.fill16(g, w.world, width, width, self.P_start[u], self.P_size[u], w.seed,
+                                synth.TAG_GRAD, 0, 1, w.grad_sigma, w.dtype, w.outlier_permyriad)
+                    self.grads_by_width[width] = g
+        else:
+            self.grads = empty16(w.world * self.maxw, w.dtype, device)
         theta = torch.empty(self.maxw, dtype=torch.float32, device=device)
         for u in range(self.U):
             width = w.world * self.S_u[u]
@@ -274,12 +329,13 @@ class Stage3World:
                                   self.m[o:], self.v[o:], self.p16[o:])
         del theta
 
-    def _gather(self, u: int):
+    def _gather(self, u: int, buf=None):
+        buf = self.unit_buf if buf is None else buf
         shards = [self.p16[self.Q_u[u] + r * self.S_u[u]:] for r in range(self.w.world)]
-        z.zero_stage3_unit_gather(self.ctx, u, shards, self.unit_buf)
+        z.zero_stage3_unit_gather(self.ctx, u, shards, buf)
         if self.check_gathers:
             width = self.w.world * self.S_u[u]
-            same = torch.equal(self.unit_buf[:width].view(torch.int16),
+            same = torch.equal(buf[:width].view(torch.int16),
                                self.p16[self.Q_u[u]:self.Q_u[u] + width].view(torch.int16))
             self.gather_mismatch += 0 if same else 1
 
@@ -289,33 +345,86 @@ class Stage3World:
         sgpu.fill16(self.grads, w.world, width, width, self.P_start[u], self.P_size[u], w.seed,
                     synth.TAG_GRAD, 0, step, w.grad_sigma, w.dtype, w.outlier_permyriad)
 
-    def step(self, t: int, timer: Optional[Timer] = None):
+    def _grads_for(self, u: int, t: int):
+        if self.fixed_grads:
+            return self.grads_by_width[self.w.world * self.S_u[u]]
+        self.gen_grads(u, t)                          # the unit's gradients appear
+        return self.grads
+
+    def _update(self, u: int, t: int, grads):
         w = self.w
-        if timer:
+        width = w.world * self.S_u[u]
+        for r in range(w.world):
+            o = self.Q_u[u] + r * self.S_u[u]
+            z.zero_fused_step(self.ctx, r, u, grads, width, r * self.S_u[u], self.master[o:],
+                              self.m[o:], self.v[o:], self.p16[o:], t, w.lr, w.betas, w.eps)
+
+    def step(self, t: int, timer: Optional[Timer] = None):
+        if self.prefetch:
+            return self._step_prefetch(t)
+        timed = timer is not None and not self.fixed_grads
+        if timer and self.fixed_grads:
             timer.start()
         for u in range(self.U):                        # forward: gather -> use -> release
+            if timed:
+                timer.start()
             self._gather(u)
             z.zero_stage3_unit_release(self.ctx, u)
-        if timer:
-            timer.stop()
+            if timed:
+                timer.stop()
         for u in reversed(range(self.U)):              # backward: re-gather -> reduce+Adam+cast
-            if timer:
+            if timed:
                 timer.start()
             self._gather(u)
-            if timer:
+            if timed:
                 timer.stop()
-            self.gen_grads(u, t)                       # untimed: the unit's gradients appear
-            if timer:
+            grads = self._grads_for(u, t)              # untimed when generated here
+            if timed:
                 timer.start()
-            width = w.world * self.S_u[u]
-            for r in range(w.world):
-                o = self.Q_u[u] + r * self.S_u[u]
-                z.zero_fused_step(self.ctx, r, u, self.grads, width, r * self.S_u[u],
-                                  self.master[o:], self.m[o:], self.v[o:], self.p16[o:], t, w.lr,
-                                  w.betas, w.eps)
+            self._update(u, t, grads)
             z.zero_stage3_unit_release(self.ctx, u)
-            if timer:
+            if timed:
                 timer.stop()
+        if timer and self.fixed_grads:
+            timer.stop()
+
+    def _step_prefetch(self, t: int):
+        """Forward and backward with the next unit gathered on the gather
+        stream while the current one is in use; a unit buffer is refilled
+        only after the unit it held was released and its consumers ran."""
+        compute, gs = torch.cuda.current_stream(), self.gather_stream
+        order = list(range(self.U)) + list(reversed(range(self.U)))
+        done = [torch.cuda.Event() for _ in range(2)]     # buffer free again
+        for d in done:
+            d.record(compute)
+        gathered = [None] * len(order)
+
+        def issue(k):
+            u, slot = order[k], k % 2
+            gs.wait_event(done[slot])
+            with torch.cuda.stream(gs):
+                self._gather(u, self.unit_bufs[slot])
+            ev = torch.cuda.Event()
+            ev.record(gs)
+            gathered[k] = ev
+
+        issue(0)
+        for k, u in enumerate(order):
+            more = k + 1 < len(order)
+            # prefetch: two units live -- except at the turn from forward to
+            # backward, where the next unit is this one, gathered again once
+            # it has been released
+            early = more and order[k + 1] != u
+            if early:
+                issue(k + 1)
+            compute.wait_event(gathered[k])
+            if k >= self.U:                            # backward half: update the unit
+                self._update(u, t, self._grads_for(u, t))
+            z.zero_stage3_unit_release(self.ctx, u)
+            done[k % 2].record(compute)
+            if more and not early:
+                issue(k + 1)
+        compute.wait_stream(gs)
 
     def run(self, steps: int, timer: Optional[Timer] = None):
         for t in range(1, steps + 1):

@@ -75,6 +75,8 @@ SIGNATURES = {
     "zero_gather_cast": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "zero_fused_step": (_i32, [_vp, _i32, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32,
                                ctypes.POINTER(zsmr_adam), _vp]),
+    "zero_fused_step_range": (_i32, [_vp, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+                                     _vp, _i32, ctypes.POINTER(zsmr_adam), _vp]),
     "zero_gather_copy": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
     "zero_stage3_set_max_live": (_i32, [_vp, _i32]),
     "zero_stage3_unit_gather": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _vp, _vp]),
@@ -242,6 +244,16 @@ def zero_fused_step(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base
     _check(_lib().zero_fused_step(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
                                   int(base_elem), _ptr(master), _ptr(m), _ptr(v), _ptr(p16_dst),
                                   int(t), ctypes.byref(hp), _stream(stream)), "zero_fused_step")
+
+
+def zero_fused_step_range(ctx: Ctx, rank: int, unit: int, begin: int, count: int, grads,
+                          row_stride: int, base_elem: int, master, m, v, p16_dst, t: int,
+                          lr: float, betas=(0.9, 0.999), eps: float = 1e-8, stream=None):
+    hp = _hp(lr, betas, eps)
+    _check(_lib().zero_fused_step_range(ctx.handle, rank, unit, int(begin), int(count), _ptr(grads),
+                                        int(row_stride), int(base_elem), _ptr(master), _ptr(m),
+                                        _ptr(v), _ptr(p16_dst), int(t), ctypes.byref(hp),
+                                        _stream(stream)), "zero_fused_step_range")
 
 
 def zero_gather_copy(ctx: Ctx, recv_rank: int, src, dst, n: int, stream=None):

@@ -404,36 +404,58 @@ int32_t zero_gather_cast(zsmr_ctx* c, int32_t rank, int32_t unit, const float* m
     return ZSMR_OK;
 }
 
-int32_t zero_fused_step(zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
-                        int64_t row_stride, int64_t base, float* master, float* m, float* v,
-                        void* p16_dst, int32_t t, const zsmr_adam* hp, hipStream_t stream) {
+static int32_t fused_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begin, int64_t count,
+                           bool whole, const void* grads, int64_t row_stride, int64_t base,
+                           float* master, float* m, float* v, void* p16_dst, int32_t t,
+                           const zsmr_adam* hp, hipStream_t stream) {
     int32_t st = check_piece(c, rank, unit);
     if (st) return st;
     int64_t len = 0;
     piece(c, rank, unit, nullptr, &len, nullptr);
+    if (whole) {
+        begin = 0;
+        count = len;
+    }
+    if (begin < 0 || count < 0 || begin > len - count) return ZSMR_ERR_ARG;
     if ((st = check_grads(c, grads, row_stride, base, len))) return st;
     zsmr::AdamK k{};
     if ((st = check_adam(hp, t, &k))) return st;
     if (!master || !m || !v || !p16_dst) return ZSMR_ERR_ARG;
     if (!al(master, 4) || !al(m, 4) || !al(v, 4) || !al(p16_dst, 2)) return ZSMR_ERR_ALIGN;
+    if (count == 0) return ZSMR_OK;
     zsmr::StepArgs a{};
-    a.grads = static_cast<const uint16_t*>(grads) + base;
+    a.grads = static_cast<const uint16_t*>(grads) + base + begin;
     a.row_stride = row_stride;
     a.nrows = c->world;
     a.mean = 1;
     a.nf = (float)c->world;
-    a.master = master;
-    a.m = m;
-    a.v = v;
-    a.p16 = static_cast<uint16_t*>(p16_dst);
-    a.n = len;
+    a.master = master + begin;
+    a.m = m + begin;
+    a.v = v + begin;
+    a.p16 = static_cast<uint16_t*>(p16_dst) + begin;
+    a.n = count;
     a.k = k;
     const hipError_t e =
         zsmr::launch_step(zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST, c->gdt, c->pdt, a, stream);
     if (e != hipSuccess) return hip_fail(e);
-    count_reduce(c, rank, len);
-    count_cast(c, rank, len);
+    count_reduce(c, rank, count);
+    count_cast(c, rank, count);
     return ZSMR_OK;
+}
+
+int32_t zero_fused_step(zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
+                        int64_t row_stride, int64_t base, float* master, float* m, float* v,
+                        void* p16_dst, int32_t t, const zsmr_adam* hp, hipStream_t stream) {
+    return fused_range(c, rank, unit, 0, 0, true, grads, row_stride, base, master, m, v, p16_dst, t,
+                       hp, stream);
+}
+
+int32_t zero_fused_step_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begin,
+                              int64_t count, const void* grads, int64_t row_stride,
+                              int64_t base, float* master, float* m, float* v, void* p16_dst,
+                              int32_t t, const zsmr_adam* hp, hipStream_t stream) {
+    return fused_range(c, rank, unit, begin, count, false, grads, row_stride, base, master, m, v,
+                       p16_dst, t, hp, stream);
 }
 
 int32_t zero_gather_copy(zsmr_ctx* c, int32_t recv_rank, const void* src, void* dst, int64_t n,
