@@ -163,6 +163,8 @@ def bench_share64(args, w):
     import zero_sharded_mixed_reduce_amd as z
 
     z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
+    z.zsmr_set_write_window(args.window_cycle_ns, args.window_write_ns, args.window_margin_ns,
+                            args.window_lead_ns)
     share = wl.RankShare(w, rank=0)
     share.gen_grads(1)
     stream = torch.cuda.current_stream()
@@ -199,7 +201,7 @@ def bench_share64(args, w):
     if bucketed:
         parts["bucketed_with_backward"] = bucketed
     dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
-    fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
+    fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows and N > 8
                     else "step_vec8_kernel")
     kname = {"fused_step": fused_kernel, "peer_receive": "copy16_kernel"}[dom]
     roof = {"bound": "hbm", "achieved": parts[dom]["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -215,7 +217,9 @@ def bench_share64(args, w):
         "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
         "rank": 0, "step_workgroups_per_cu": args.step_bpc,
         "copy_workgroups_per_cu": args.copy_bpc, "fused_defer_tiles": args.defer_tiles,
-        "fused_defer_min_rows": args.defer_min_rows}
+        "fused_defer_min_rows": args.defer_min_rows,
+        "fused_write_window_ns": {"cycle": args.window_cycle_ns, "write": args.window_write_ns,
+                                  "margin": args.window_margin_ns, "lead": args.window_lead_ns}}
 
 
 def bench_world(args, w):
@@ -226,6 +230,8 @@ def bench_world(args, w):
     import zero_sharded_mixed_reduce_amd as z
 
     z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
+    z.zsmr_set_write_window(args.window_cycle_ns, args.window_write_ns, args.window_margin_ns,
+                            args.window_lead_ns)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
         # each unit size's gradients are made once, so that whole steps --
@@ -265,6 +271,13 @@ def main():
     ap.add_argument("--defer-tiles", type=int, default=5, help="fused-step tiles kept in LDS (0-5)")
     ap.add_argument("--defer-min-rows", type=int, default=32,
                     help="fewest gradient rows for which the fused step defers its writes")
+    ap.add_argument("--window-cycle-ns", type=int, default=None,
+                    help="fused step: write-window cycle (0 = no windows)")
+    ap.add_argument("--window-write-ns", type=int, default=None, help="fused step: write window")
+    ap.add_argument("--window-margin-ns", type=int, default=None,
+                    help="fused step: no loads issued this long before a window")
+    ap.add_argument("--window-lead-ns", type=int, default=None,
+                    help="fused step: loads resume this long before a window ends")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefetch", action="store_true",
                     help="ZeRO-3 workload: gather the next unit while the current one is in use")
@@ -278,6 +291,12 @@ def main():
     sys.path.insert(0, ROOT)
     import torch
     import workloads as wl
+    import zero_sharded_mixed_reduce_amd as z
+
+    for name, dflt in zip(("window_cycle_ns", "window_write_ns", "window_margin_ns", "window_lead_ns"),
+                          z.WRITE_WINDOW_DEFAULT):
+        if getattr(args, name) is None:
+            setattr(args, name, dflt)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

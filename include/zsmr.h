@@ -245,13 +245,27 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
 /* Launch shape: workgroups per compute unit of the step kernels (reduce,
  * Adam, cast, and the fused step when it writes at once; default 2) and of
  * the copies (receive and ZeRO-3 gather; default 4), each 1..64; defer_tiles,
- * 0..5 (default 5): how many wave tiles of fused-step results a workgroup
- * keeps in LDS before writing them in one burst (0 = write at once); and
- * defer_min_rows >= 1 (default 32): the fewest gradient rows for which the
- * fused step defers its writes.  Process-wide.  Affects speed only, never
- * results. */
+ * 0..5 (default 5): how many completed 512-element tiles of fused-step
+ * results each wave keeps in LDS before it must write them (0 = write at
+ * once); and defer_min_rows >= 1 (default 32): the fewest gradient rows for
+ * which the fused step defers its writes (it never does with 8 rows or
+ * fewer).  Process-wide.  Affects speed only, never results. */
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows);
+
+/* Write windows of the fused step's deferred writes.  Every cycle_ns, the
+ * last write_ns form a window that all waves on the GPU take at the same
+ * time, read from the chip's constant-rate clock: deferred results are
+ * stored only inside windows, and no gradient loads are issued from
+ * margin_ns before a window until lead_ns before its end, so HBM sees long
+ * read-only stretches and short write-only bursts.  cycle_ns = 0 turns the
+ * windows off (a wave then stores its tiles whenever its LDS ring is full).
+ * Otherwise 1,000 <= cycle_ns <= 10,000,000, write_ns >= 1, margin_ns >= 0,
+ * write_ns + margin_ns < cycle_ns and 0 <= lead_ns < write_ns; ZSMR_ERR_ARG
+ * if not.  Defaults: 40,000 / 5,000 / 1,000 / 1,000.  Process-wide.  Affects
+ * speed only, never results. */
+int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin_ns,
+                              int32_t lead_ns);
 
 #ifdef __cplusplus
 }

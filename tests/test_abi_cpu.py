@@ -185,3 +185,15 @@ def test_fused_range_bounds_are_checked_on_the_host():
     for begin in (0, 7, 16):                   # empty ranges inside the piece are no-ops
         z.zero_fused_step_range(ctx, 1, 0, begin, 0, ok, 16, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
     assert z.zero_counters(ctx, 1)["traffic_elems"] == 0
+
+
+def test_write_window_arguments():
+    for bad in ((999, 100, 0, 0), (10_000_001, 100, 0, 0), (32000, 0, 0, 0), (32000, 4000, -1, 0),
+                (32000, 30000, 2000, 0), (32000, 4000, 0, 4000), (32000, 4000, 0, -1),
+                (0, -1, 0, 0), (0, 0, -1, 0), (0, 0, 0, -1)):
+        with pytest.raises(z.ZsmrError) as e:
+            z.zsmr_set_write_window(*bad)
+        assert e.value.code == z.ZSMR_ERR_ARG, bad
+    z.zsmr_set_write_window(0, 0, 0, 0)
+    z.zsmr_set_write_window(1000, 2, 997, 1)
+    z.zsmr_set_write_window()                 # back to the defaults

@@ -155,12 +155,13 @@ def test_stage3_llama8b_full_size():
 def test_piece_larger_than_one_launch(defer):
     """A piece of 2^30 + 1,029 elements: the host cuts it into a launch of
     2^30 elements and one of the rest (a partial wave tile plus a ragged
-    tail); checked around the cut and at the ends."""
+    tail); 9 rows, so that defer=5 runs the deferred-write kernel; checked
+    around the cut and at the ends."""
     import synth
     import synth.gpu as sgpu
     z.zsmr_set_launch_shape(2, 4, defer, 1)
     try:
-        n, world, T, lr = (1 << 30) + 1029, 2, 2, 1e-3
+        n, world, T, lr = (1 << 30) + 1029, 9, 2, 1e-3
         say(f"[full] piece over 2^30: n={n} defer={defer}")
         ctx = z.zero_init_shards(n * world, world, 2, "bf16")
         grads = torch.empty(world * n, dtype=torch.bfloat16, device="cuda")

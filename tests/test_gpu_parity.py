@@ -23,7 +23,9 @@ TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
 @pytest.fixture(params=[5, 0], ids=["deferred", "direct"])
 def fused_path(request):
     """Run a test with the fused step's deferred-write kernel (default) and
-    with the kernel that writes at once; both must give the same bits."""
+    with the kernel that writes at once; both must give the same bits.  The
+    deferred kernel runs only for more than 8 gradient rows; with fewer both
+    ids run the direct kernel."""
     z.zsmr_set_launch_shape(2, 4, request.param, 1)
     yield request.param
     z.zsmr_set_launch_shape()
@@ -189,6 +191,8 @@ def test_psi65k_stage3_one_unit_is_whole_vector_gather():
     (7, 1, 1, None, "bf16"),                    # fewer elements than one vector
     (9, 3, 3, [9], "fp16"),                     # padding inside a single unit
     (65_544, 8, 0, None, "bf16"),               # data parallel, not a multiple of 64
+    (40_003, 11, 2, None, "fp16"),              # > 8 rows: the deferred kernel, ragged
+    (50_001, 16, 3, [30_000, 20_001], "bf16"),  # > 8 rows, stage 3, padded units
 ])
 def test_ragged_and_padded(numel, world, stage, units, dt, fused_path):
     pad = True
@@ -228,7 +232,7 @@ def _oracle_piece(rows, theta, gdt, pdt, T, lr, steps_rows=None):
 ])
 @pytest.mark.parametrize("n", [8 * 256 * 3 + 5, 1, 7, 8, 9])
 def test_alignment_variants(shift16, shift32, gshift, n, fused_path):
-    world, gdt, pdt, T, lr = 4, "bf16", "bf16", 2, 1e-3
+    world, gdt, pdt, T, lr = 12, "bf16", "bf16", 2, 1e-3
     ctx = z.zero_init_shards(n * world, world, 2, gdt, pdt)
     rows, theta = _piece_inputs(n, world, gdt)
     stride = n + 8 + (8 - n % 8) % 8                       # rows 16-byte aligned apart
@@ -258,7 +262,7 @@ def test_alignment_variants(shift16, shift32, gshift, n, fused_path):
 
 @pytest.mark.parametrize("gdt,pdt", [("fp16", "bf16"), ("bf16", "fp16"), ("fp16", "fp16")])
 def test_mixed_formats(gdt, pdt, fused_path):
-    n, world, T, lr = 3 * 2048 + 3, 8, 3, 1e-2
+    n, world, T, lr = 3 * 2048 + 3, 17, 3, 1e-2
     ctx = z.zero_init_shards(n * world, world, 1, gdt, pdt)
     steps_rows = {t: _piece_inputs(n, world, gdt, step=t)[0] for t in range(1, T + 1)}
     theta = synth.theta0(0, np.arange(n))
@@ -277,12 +281,13 @@ def test_mixed_formats(gdt, pdt, fused_path):
 
 @pytest.mark.parametrize("tiles", [5, 3, 1])
 def test_deferred_kernel_many_rounds(tiles):
-    """Several rounds of the deferred-write kernel (each round covers 256
-    workgroups x tiles x 256 lanes x 8 elements) and a ragged tail."""
+    """The deferred-write kernel with each wave's LDS ring filled several
+    times over (1,024 waves, about 10 tiles each) and a ragged tail, 9 rows
+    (one whole row batch and a batch of one row), against the oracle."""
     z.zsmr_set_launch_shape(2, 4, tiles, 1)
     try:
-        n = 2 * 256 * tiles * 256 * 8 + 3 * 512 + 77
-        world, T, lr = 4, 2, 1e-3
+        n = 1024 * 10 * 512 + 3 * 512 + 77
+        world, T, lr = 9, 2, 1e-3
         ctx = z.zero_init_shards(n * world, world, 2, "bf16")
         steps_rows = {t: _piece_inputs(n, world, "bf16", step=t)[0] for t in range(1, T + 1)}
         theta = synth.theta0(0, np.arange(n))
@@ -300,9 +305,91 @@ def test_deferred_kernel_many_rounds(tiles):
         z.zsmr_set_launch_shape()
 
 
+def _fused_run(n, rows, T, defer, window, guard=64):
+    """T fused steps on one n-element piece with rows gradient rows made by
+    the device generator; returns the outputs with `guard` untouched
+    elements on both sides of every buffer."""
+    import synth.gpu as sgpu
+    z.zsmr_set_launch_shape(2, 4, defer, 1)
+    z.zsmr_set_write_window(*window)
+    try:
+        stride = n + 24
+        ctx = z.zero_init_shards(n * rows, rows, 2, "bf16")
+        G = torch.empty(rows * stride, dtype=torch.int16, device="cuda")
+        th = torch.empty(n, dtype=torch.float32, device="cuda")
+        sgpu.fill32(th, n, 0, n, 7, synth.TAG_THETA, 0, 0, 0.02)
+        buf = lambda dt: torch.full((n + 2 * guard,), -3, dtype=dt, device="cuda")
+        mb, mm, vb = buf(torch.float32), buf(torch.float32), buf(torch.float32)
+        pb = buf(torch.int16)
+        sl = slice(guard, guard + n)
+        z.zero_init_state(ctx, 0, 0, th, mb[sl], mm[sl], vb[sl], pb[sl])
+        for t in range(1, T + 1):
+            sgpu.fill16(G, rows, stride, n, 0, n, 7, synth.TAG_GRAD, 0, t, 1e-2, "bf16")
+            z.zero_fused_step(ctx, 0, 0, G, stride, 0, mb[sl], mm[sl], vb[sl], pb[sl], t, 1e-3)
+        torch.cuda.synchronize()
+        return mb, mm, vb, pb
+    finally:
+        z.zsmr_set_launch_shape()
+        z.zsmr_set_write_window()
+
+
+WINDOWS = {
+    "default": z.WRITE_WINDOW_DEFAULT,
+    "off": (0, 0, 0, 0),
+    "short": (1000, 300, 0, 0),                # many windows per tile: partial sums cross them
+    "margin": (2000, 500, 700, 200),
+    "long": (200000, 20000, 0, 5000),          # the ring fills long before a window
+}
+
+
+@pytest.mark.parametrize("window", list(WINDOWS), ids=list(WINDOWS))
+@pytest.mark.parametrize("kd", [1, 2, 5])
+@pytest.mark.parametrize("rows", [9, 16, 33, 64])
+def test_deferred_windows_match_direct_bits(window, kd, rows):
+    """Write windows and ring sizes change only when results are stored:
+    the deferred kernel gives the direct kernel's bits, and writes nothing
+    outside the piece."""
+    n = 1024 * 6 * 512 + 2 * 512 + 131           # ~6 tiles per wave, a ragged tail
+    say(f"[deferred] window={window} kd={kd} rows={rows} n={n}")
+    ref = _fused_run(n, rows, 2, 0, WINDOWS["off"])
+    got = _fused_run(n, rows, 2, kd, WINDOWS[window])
+    for name, a, b in zip(("master", "m", "v", "p16"), ref, got):
+        ai = a.view(torch.int32) if a.dtype == torch.float32 else a
+        bi = b.view(torch.int32) if b.dtype == torch.float32 else b
+        diff = int((ai != bi).sum())
+        assert diff == 0, f"{name}: {diff} elements differ"
+    g = 64
+    for b in got:
+        bi = b.view(torch.int32) if b.dtype == torch.float32 else b
+        fill = torch.full((g,), -3, dtype=b.dtype, device="cuda")
+        fi = fill.view(torch.int32) if b.dtype == torch.float32 else fill
+        assert torch.equal(bi[:g], fi) and torch.equal(bi[-g:], fi)
+
+
+def test_deferred_sampled_against_oracle():
+    """One windowed deferred run (64 rows, default windows) against the
+    oracle on every element of three whole tiles and the tail."""
+    n, rows, T = 1024 * 6 * 512 + 2 * 512 + 131, 64, 2
+    mb, mm, vb, pb = _fused_run(n, rows, T, 5, WINDOWS["default"])
+    g = 64
+    pos = np.concatenate([np.arange(0, 512), np.arange(512 * 1023, 512 * 1025),
+                          np.arange(n - 1200, n)])
+    p = pos.astype(np.int64)
+    theta = synth.theta0(7, p)
+    master, m, v = theta.copy(), np.zeros_like(theta), np.zeros_like(theta)
+    for t in range(1, T + 1):
+        r16 = [synth.grad16(7, r, t, p, 1e-2, "bf16") for r in range(rows)]
+        gr = nm.reduce_rank_order([nm.widen16(r, "bf16") for r in r16])
+        master, m, v = nm.adam_update(master, m, v, gr, nm.adam_consts(1e-3, 0.9, 0.999, 1e-8, t))
+    at = lambda x: host32(x)[g + pos] if x.dtype == torch.float32 else host16(x)[g + pos]
+    compare({"master": at(mb), "m": at(mm), "v": at(vb)}, {"master": master, "m": m, "v": v},
+            at(pb), nm.cast16(master, "bf16"), "deferred windowed sampled")
+
+
+@pytest.mark.parametrize("world", [16, 12, 64])     # the mean multiplies by 1/N for 16 and 64
 @pytest.mark.parametrize("gdt", ["bf16", "fp16"])
-def test_reduce_sum_and_mean(gdt):
-    n, world = 10_000 + 3, 16
+def test_reduce_sum_and_mean(gdt, world):
+    n = 10_000 + 3
     ctx = z.zero_init_shards(n * world, world, 2, gdt)
     rows, _ = _piece_inputs(n, world, gdt, sigma=1e-1, outlier=100)
     G = dev16(rows.ravel())

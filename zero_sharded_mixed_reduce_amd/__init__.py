@@ -84,6 +84,7 @@ SIGNATURES = {
     "zero_stage3_unit_state": (_i32, [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
                                       ctypes.POINTER(_i64)]),
     "zsmr_set_launch_shape": (_i32, [_i32, _i32, _i32, _i32]),
+    "zsmr_set_write_window": (_i32, [_i32, _i32, _i32, _i32]),
 }
 
 _LIB = None
@@ -286,3 +287,14 @@ def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 4, defer_tiles: int
                           defer_min_rows: int = 32) -> None:
     _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc), int(defer_tiles),
                                         int(defer_min_rows)), "zsmr_set_launch_shape")
+
+
+WRITE_WINDOW_DEFAULT = (40000, 5000, 1000, 1000)
+
+
+def zsmr_set_write_window(cycle_ns: int = WRITE_WINDOW_DEFAULT[0],
+                          write_ns: int = WRITE_WINDOW_DEFAULT[1],
+                          margin_ns: int = WRITE_WINDOW_DEFAULT[2],
+                          lead_ns: int = WRITE_WINDOW_DEFAULT[3]) -> None:
+    _check(_lib().zsmr_set_write_window(int(cycle_ns), int(write_ns), int(margin_ns), int(lead_ns)),
+           "zsmr_set_write_window")

@@ -342,6 +342,14 @@ static int32_t check_grads(const zsmr_ctx* c, const void* grads, int64_t row_str
     return ZSMR_OK;
 }
 
+// N as the divisor of the mean; for N a power of two also 1/N, which the
+// kernels multiply by instead (the same bits).
+static void set_mean_divisor(zsmr::StepArgs& a, int32_t world) {
+    a.nf = (float)world;
+    a.inv_pow2 = world > 0 && (world & (world - 1)) == 0;
+    a.inv_nf = a.inv_pow2 ? 1.0f / (float)world : 0.0f;
+}
+
 int32_t zero_reduce_shard(zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
                           int64_t row_stride, int64_t base, int32_t mean, float* g_out,
                           hipStream_t stream) {
@@ -357,7 +365,7 @@ int32_t zero_reduce_shard(zsmr_ctx* c, int32_t rank, int32_t unit, const void* g
     a.row_stride = row_stride;
     a.nrows = c->world;
     a.mean = mean;
-    a.nf = (float)c->world;
+    set_mean_divisor(a, c->world);
     a.g_out = g_out;
     a.n = len;
     const hipError_t e = zsmr::launch_step(zsmr::M_REDUCE | zsmr::M_GOUT, c->gdt, c->pdt, a, stream);
@@ -428,7 +436,7 @@ static int32_t fused_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begi
     a.row_stride = row_stride;
     a.nrows = c->world;
     a.mean = 1;
-    a.nf = (float)c->world;
+    set_mean_divisor(a, c->world);
     a.master = master + begin;
     a.m = m + begin;
     a.v = v + begin;
@@ -532,6 +540,17 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
         defer_tiles > 5 || defer_min_rows < 1)
         return ZSMR_ERR_ARG;
     zsmr::set_launch_shape(step_bpc, copy_bpc, defer_tiles, defer_min_rows);
+    return ZSMR_OK;
+}
+
+int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin_ns,
+                              int32_t lead_ns) {
+    if (cycle_ns != 0 && (cycle_ns < 1000 || cycle_ns > 10000000 || write_ns < 1 ||
+                          margin_ns < 0 || (int64_t)write_ns + margin_ns >= cycle_ns ||
+                          lead_ns < 0 || lead_ns >= write_ns))
+        return ZSMR_ERR_ARG;
+    if (cycle_ns == 0 && (write_ns < 0 || margin_ns < 0 || lead_ns < 0)) return ZSMR_ERR_ARG;
+    zsmr::set_write_window(cycle_ns, write_ns, margin_ns, lead_ns);
     return ZSMR_OK;
 }
 

@@ -1,10 +1,10 @@
 // gfx950 kernels of the ZeRO shard step.
 //
 // One streaming pass per launch.  The path is bound by HBM bandwidth (about
-// 0.3-0.6 flop per byte), so there is no MFMA and no LDS: every lane owns 8
-// consecutive elements, reads each 16-bit gradient row with one 128-bit load,
-// the fp32 master/m/v with two 128-bit loads each, and writes each output
-// once.  The same device code, selected by the MODE bits, gives the fused
+// 0.3-0.6 flop per byte), so there is no MFMA: every lane owns 8 elements of
+// a 512-element wave tile, reads each 16-bit gradient row and the fp32
+// master/m/v once, and writes each output once.  LDS only holds results whose
+// stores are deferred (the fused step) and copy bursts.  The same device code, selected by the MODE bits, gives the fused
 // step and the unfused reduce-only, Adam-only, cast-only and init launches,
 // so the fused and unfused results are the same bits.
 //
@@ -75,6 +75,13 @@ int g_defer_bpc = 1;
 // ... used when a step reduces at least this many rows (below it the
 // read:write ratio is low and one workgroup per CU streams too little)
 int g_defer_min_rows = 32;
+// its write windows, in ns (0: none); converted to clock ticks per device
+// (measured on MI355X over cycles of 35-65 us: 40 / 5 / 1 / 1 us is on the
+// flat top of the curve, and leaves room in the ring of 5 tiles per wave)
+int64_t g_window_cycle_ns = 40000;
+int64_t g_window_write_ns = 5000;
+int64_t g_window_margin_ns = 1000;
+int64_t g_window_lead_ns = 1000;
 
 // Streamed data is touched once per step: non-temporal loads and stores keep
 // it from displacing anything useful in L2 and the MALL.
@@ -127,6 +134,13 @@ __device__ __forceinline__ void unpack8(u32x4 w, float* f) {
         f[2 * i] = widen<DT>(w[i] & 0xffffu);
         f[2 * i + 1] = widen<DT>(w[i] >> 16);
     }
+}
+
+// The rank-order sum divided by N.  For N a power of two the quotient is
+// exact up to the one rounding both forms share, so multiplying by 1/N gives
+// the same bits as dividing, and is cheaper.
+__device__ __forceinline__ float mean_of(const StepArgs& a, float sum) {
+    return a.inv_pow2 ? sum * a.inv_nf : sum / a.nf;
 }
 
 // ------------------------------------------------------------------- Adam --
@@ -287,7 +301,7 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         }
         if (a.mean) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) g[j] = g[j] / a.nf;
+            for (int j = 0; j < 8; ++j) g[j] = mean_of(a, g[j]);
         }
         if constexpr ((MODE & M_GOUT) != 0) G::store32(a.g_out, e0, e1, g);
     } else if constexpr ((MODE & (M_ADAM | M_INIT)) != 0) {
@@ -346,7 +360,7 @@ __device__ __forceinline__ void body1(const StepArgs& a, int64_t e) {
         const uint16_t* p = a.grads + e;
         g = widen<GDT>(p[0]);
         for (int r = 1; r < a.nrows; ++r) g = g + widen<GDT>(p[(int64_t)r * a.row_stride]);
-        if (a.mean) g = g / a.nf;
+        if (a.mean) g = mean_of(a, g);
         if constexpr ((MODE & M_GOUT) != 0) a.g_out[e] = g;
     } else if constexpr ((MODE & (M_ADAM | M_INIT)) != 0) {
         g = a.g_in[e];
@@ -410,76 +424,233 @@ __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
         for (int64_t e = n_main + threadIdx.x; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
 }
 
-// The fused step with deferred writes.  Mixing a write stream into the
-// 2N-row read stream costs HBM throughput out of proportion to the bytes
-// written; a workgroup therefore computes KD wave tiles, keeps their results
-// (master, m, v and the 16-bit copy: 112 B per lane per tile) in LDS, and
-// only then writes them in one burst.  Each lane reads back only what it
-// wrote itself, so the barriers only line the workgroup's waves up; results
-// are the same bits as step_vec8_kernel's.  KD = 5 fills 140 KB of LDS, one
-// workgroup per CU.
-template <int GDT, int PDT, int DV, int KD>
-__global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a) {
-    static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
-    constexpr int MODE = M_REDUCE | M_ADAM | M_CAST;
-    __shared__ float s_w[KD][8][kThreads];
-    __shared__ float s_m[KD][8][kThreads];
-    __shared__ float s_v[KD][8][kThreads];
-    __shared__ uint32_t s_h[KD][4][kThreads];
-    const int t = threadIdx.x;
-    const uint32_t nv = static_cast<uint32_t>(vec_elems(a.n) >> 3);
-    const uint32_t per_block = KD * kThreads;
-    const uint32_t per_round = gridDim.x * per_block;
-    const uint32_t rounds = (nv + per_round - 1) / per_round;
-    for (uint32_t rd = 0; rd < rounds; ++rd) {
-        const uint32_t base = rd * per_round + blockIdx.x * per_block;
-#pragma unroll
-        for (int k = 0; k < KD; ++k) {
-            const uint32_t i = base + k * kThreads + t;
-            if (i < nv) {
-                const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;
-                Out8 o;
-                body8<true, GDT, PDT, MODE, DV, true>(a, e0, e0 + 256u, &o);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    s_w[k][j][t] = o.w[j];
-                    s_m[k][j][t] = o.m[j];
-                    s_v[k][j][t] = o.v[j];
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s_h[k][j][t] = o.h[2 * j] | (o.h[2 * j + 1] << 16);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < KD; ++k) {
-            const uint32_t i = base + k * kThreads + t;
-            if (i < nv) {
-                const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;
-                const uint32_t e1 = e0 + 256u;
-                float w[8], m[8], v[8];
-                uint32_t h[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    w[j] = s_w[k][j][t];
-                    m[j] = s_m[k][j][t];
-                    v[j] = s_v[k][j][t];
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[2 * j] = s_h[k][j][t] & 0xffffu;
-                    h[2 * j + 1] = s_h[k][j][t] >> 16;
-                }
-                Groups<true>::store32(a.master, e0, e1, w);
-                Groups<true>::store32(a.m, e0, e1, m);
-                Groups<true>::store32(a.v, e0, e1, v);
-                Groups<true>::template store16<DV>(a.p16, e0, e1, h);
-            }
-        }
-        __syncthreads();
+// Write windows of the deferred-write kernel, in ticks of the chip's
+// constant-rate clock (s_memrealtime, 100 MHz; on MI355X the eight XCDs read
+// it within a microsecond of each other): in every
+// cycle of `cycle` ticks the last `write` ticks are the write window; a wave
+// stops issuing loads `margin` ticks before it and resumes `lead` ticks
+// before it ends.  cycle == 0: no windows.
+struct Window {
+    uint32_t cycle, write, margin, lead;
+};
+
+__device__ __forceinline__ uint64_t clock_now() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Sleeps until the clock reaches t.  The spin count bounds the wait (about
+// 30 ms), so a wave always goes on even if the clock stood still.
+__device__ __forceinline__ void wait_clock(uint64_t t) {
+    for (int i = 0; i < (1 << 20); ++i) {
+        if (clock_now() >= t) break;
+        __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// The fused step with deferred, windowed writes.  A write stream mixed into
+// the 2N-row read stream costs HBM throughput out of proportion to its bytes,
+// so each wave keeps the results of its completed wave tiles (master, m, v
+// and the 16-bit copy: 112 B per lane per tile) in a ring of KD tiles in LDS
+// and writes them only in the write windows, which every wave of the chip
+// takes at the same time from the shared clock: HBM then sees long read-only
+// stretches and short write-only bursts.  Between windows a wave streams its
+// tiles' gradient rows as one double-buffered sequence of row batches, across
+// tile boundaries; a tile whose rows straddle a window keeps its partial sum
+// in registers.  Wave w owns tiles w, w + W, w + 2W, ... (W waves in the
+// grid).  Each lane reads back only what it wrote, so the waves never
+// synchronise.  Results are the same bits as step_vec8_kernel's: only the
+// time at which they are stored changes.  Needs more than kRowBatch rows (the
+// host checks), so that a tile's master/m/v, loaded with its last row batch,
+// never overwrite those of the tile still being finished, and a row stride
+// of fewer than 2^63 bytes.
+template <int GDT, int PDT, int DV, int KD>
+__global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, Window win) {
+    static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
+    constexpr int kWaves = kThreads / 64;
+    __shared__ float s_w[kWaves][KD][8][64];
+    __shared__ float s_m[kWaves][KD][8][64];
+    __shared__ float s_v[kWaves][KD][8][64];
+    __shared__ uint32_t s_h[kWaves][KD][4][64];
+    const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+    const uint32_t tiles = static_cast<uint32_t>(vec_elems(a.n) / 512);
+    const uint32_t nw = gridDim.x * kWaves;
+    const uint32_t wid = blockIdx.x * kWaves + wv;
+    const uint32_t mine = wid < tiles ? (tiles - 1 - wid) / nw + 1 : 0;
+    const uint32_t bps = (static_cast<uint32_t>(a.nrows) + kRowBatch - 1) / kRowBatch;
+    const uint32_t nb = mine * bps;
+    auto e0_of = [&](uint32_t j) { return (wid + j * nw) * 512u + lane * 4u; };
+
+    // the ring: tiles [flushed, done) of this wave are in LDS, not yet stored
+    uint32_t done = 0, flushed = 0;
+    auto flush = [&]() {
+        for (uint32_t j = flushed; j < done; ++j) {
+            const uint32_t k = j % KD, e0 = e0_of(j);
+            float w[8], m[8], v[8];
+            uint32_t h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                w[q] = s_w[wv][k][q][lane];
+                m[q] = s_m[wv][k][q][lane];
+                v[q] = s_v[wv][k][q][lane];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h[2 * q] = s_h[wv][k][q][lane] & 0xffffu;
+                h[2 * q + 1] = s_h[wv][k][q][lane] >> 16;
+            }
+            Groups<true>::store32(a.master, e0, e0 + 256u, w);
+            Groups<true>::store32(a.m, e0, e0 + 256u, m);
+            Groups<true>::store32(a.v, e0, e0 + 256u, v);
+            Groups<true>::template store16<DV>(a.p16, e0, e0 + 256u, h);
+        }
+        flushed = done;
+    };
+
+    // the clock: cyc = start of the current cycle; used = cycle whose window
+    // this wave has already taken
+    uint64_t cyc = 0, used = ~0ull;
+    auto phase_at = [&](uint64_t now) -> uint64_t {
+        if (now - cyc >= win.cycle) cyc = now - now % win.cycle;
+        return now - cyc;
+    };
+    auto phase = [&]() -> uint64_t { return phase_at(clock_now()); };
+    // decided on a clock value read one row batch earlier, right after that
+    // batch's loads were issued, so the read's latency never delays an issue
+    auto near_window = [&](uint64_t seen) -> bool {
+        if (!win.cycle) return false;
+        return phase_at(seen) + win.write + win.margin >= win.cycle && cyc != used;
+    };
+    // flush in the window of cycle `want` (waiting for it to open) unless it
+    // was taken already or has passed, then idle to the end of the cycle
+    auto take_window = [&](uint64_t want) {
+        const uint64_t ph = phase();
+        if (cyc != want || cyc == used) return;
+        if (ph + win.write < win.cycle) wait_clock(cyc + win.cycle - win.write);
+        flush();
+        used = cyc;
+        wait_clock(cyc + win.cycle - win.lead);
+    };
+    // the ring is full: flush in the next window not yet taken
+    auto make_room = [&]() {
+        if (win.cycle) {
+            phase();
+            if (cyc == used) wait_clock(cyc + win.cycle);
+            phase();
+            take_window(cyc);
+        }
+        if (done - flushed == KD) flush();   // no window (or the clock stood still)
+    };
+
+    // The row streams.  Issue and consume each walk rows 0..N-1 of one tile
+    // after another with a running row counter (no division); the issue side
+    // also keeps a running row address, and past the last row it keeps
+    // re-reading that row (every load is issued unconditionally, so the
+    // compiler can count them; consume skips the extra rows).
+    const char* const grads = reinterpret_cast<const char*>(a.grads);
+    const uint64_t stride_b = static_cast<uint64_t>(a.row_stride) * 2u;
+    const uint32_t nrows = static_cast<uint32_t>(a.nrows);
+    uint32_t i_tile = 0, i_row = 0, c_row = 0;
+    const char* i_ptr = grads;
+    u32x4 bufA[kRowBatch], bufB[kRowBatch];
+    float g[8], w[8], m[8], v[8];
+    auto issue = [&](u32x4* buf) {
+        const uint32_t e0 = e0_of(i_tile), off = e0 * 2u;
+#pragma unroll
+        for (int k = 0; k < kRowBatch; ++k) {
+            const u32x2 lo = ld(reinterpret_cast<const u32x2*>(i_ptr + off));
+            const u32x2 hi = ld(reinterpret_cast<const u32x2*>(i_ptr + off + 512u));
+            buf[k][0] = lo[0];
+            buf[k][1] = lo[1];
+            buf[k][2] = hi[0];
+            buf[k][3] = hi[1];
+            if (i_row + k + 1 < nrows) i_ptr += stride_b;
+        }
+        i_row += kRowBatch;
+        if (i_row >= nrows) {      // the tile's last batch: its master/m/v come with it
+            Groups<true>::load32(a.master, e0, e0 + 256u, w);
+            Groups<true>::load32(a.m, e0, e0 + 256u, m);
+            Groups<true>::load32(a.v, e0, e0 + 256u, v);
+            ++i_tile;
+            i_row = 0;
+            i_ptr = grads;
+        }
+    };
+    auto consume = [&](const u32x4* buf) {
+        // rows in rank order; the tile's sum starts from row 0 itself
+        if (c_row + kRowBatch <= nrows) {
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) {
+                float t[8];
+                unpack8<GDT>(buf[k], t);
+                if (k == 0 && c_row == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) g[e] = t[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) g[e] = g[e] + t[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) {
+                if (c_row + k < nrows) {
+                    float t[8];
+                    unpack8<GDT>(buf[k], t);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) g[e] = g[e] + t[e];
+                }
+            }
+        }
+        c_row += kRowBatch;
+        if (c_row < nrows) return;
+        c_row = 0;
+        if (a.mean) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g[e] = mean_of(a, g[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) adam1(a.k, g[e], w[e], m[e], v[e]);
+        if (done - flushed == KD) make_room();
+        const uint32_t k = done % KD;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s_w[wv][k][e][lane] = w[e];
+            s_m[wv][k][e][lane] = m[e];
+            s_v[wv][k][e][lane] = v[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s_h[wv][k][e][lane] = narrow<PDT>(w[2 * e]) | (narrow<PDT>(w[2 * e + 1]) << 16);
+        ++done;
+    };
+
+    uint64_t seen = win.cycle ? clock_now() : 0;
+    if (nb) issue(bufA);
+    for (uint32_t b = 0; b < nb; b += 2) {
+        bool hold = near_window(seen);
+        uint64_t want = cyc;
+        if (!hold && b + 1 < nb) issue(bufB);
+        if (win.cycle) seen = clock_now();
+        consume(bufA);
+        if (hold) {
+            take_window(want);
+            if (b + 1 < nb) issue(bufB);
+            seen = clock_now();
+        }
+        if (b + 1 >= nb) break;
+        hold = near_window(seen);
+        want = cyc;
+        if (!hold && b + 2 < nb) issue(bufA);
+        if (win.cycle) seen = clock_now();
+        consume(bufB);
+        if (hold) {
+            take_window(want);
+            if (b + 2 < nb) issue(bufA);
+            seen = clock_now();
+        }
+    }
+    flush();
     if (blockIdx.x == 0)
-        for (int64_t e = vec_elems(a.n) + t; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
+        for (int64_t e = vec_elems(a.n) + threadIdx.x; e < a.n; e += kThreads)
+            body1<GDT, PDT, M_REDUCE | M_ADAM | M_CAST>(a, e);
 }
 
 // Any-alignment path: one element per lane.
@@ -626,15 +797,43 @@ int dst_vec(const void* p) {
     return 1;
 }
 
+// ticks of the s_memrealtime clock per second on the current device (0 if
+// the runtime does not say: then no windows)
+int64_t clock_hz() {
+    static int64_t cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] > 0 ? cache[dev] : 0;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) khz = 0;
+    const int64_t hz = khz > 0 ? (int64_t)khz * 1000 : -1;
+    if (dev >= 0 && dev < 64) cache[dev] = hz;
+    return hz > 0 ? hz : 0;
+}
+
+Window window_ticks() {
+    Window w{0, 0, 0, 0};
+    const int64_t hz = clock_hz();
+    if (!g_window_cycle_ns || !hz) return w;
+    auto ticks = [&](int64_t ns) { return static_cast<uint32_t>(ns * hz / 1000000000); };
+    w.cycle = ticks(g_window_cycle_ns);
+    w.write = ticks(g_window_write_ns);
+    w.margin = ticks(g_window_margin_ns);
+    w.lead = ticks(g_window_lead_ns);
+    if (w.write < 1 || w.write + w.margin >= w.cycle || w.lead >= w.write) w = Window{0, 0, 0, 0};
+    return w;
+}
+
 template <int GDT, int PDT, int DV>
 hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
-    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_defer_bpc));
+    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_defer_bpc));   // one wave per tile at most
+    const Window w = window_ticks();
     switch (g_defer_tiles) {
-        case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 2>), grid, dim3(kThreads), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 3>), grid, dim3(kThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 4>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 5>), grid, dim3(kThreads), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a, w); break;
+        case 2: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 2>), grid, dim3(kThreads), 0, s, a, w); break;
+        case 3: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 3>), grid, dim3(kThreads), 0, s, a, w); break;
+        case 4: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 4>), grid, dim3(kThreads), 0, s, a, w); break;
+        default: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 5>), grid, dim3(kThreads), 0, s, a, w); break;
     }
     return hipGetLastError();
 }
@@ -642,7 +841,7 @@ hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
     if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST) && kSplit) {
-        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows) {
+        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows && a.nrows > kRowBatch) {
             switch (dv) {
                 case 8:
                 case 4: return launch_deferred<GDT, PDT, 4>(a, s);
@@ -683,6 +882,13 @@ void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
     g_copy_bpc = copy_bpc;
     g_defer_tiles = defer_tiles;
     g_defer_min_rows = defer_min_rows;
+}
+
+void set_write_window(int64_t cycle_ns, int64_t write_ns, int64_t margin_ns, int64_t lead_ns) {
+    g_window_cycle_ns = cycle_ns;
+    g_window_write_ns = write_ns;
+    g_window_margin_ns = margin_ns;
+    g_window_lead_ns = lead_ns;
 }
 
 namespace {

@@ -26,6 +26,8 @@ struct StepArgs {
     int32_t nrows;          // N
     int32_t mean;           // divide the sum by N
     float nf;               // (float)N
+    float inv_nf;           // 1/N when N is a power of two (then exact)
+    int32_t inv_pow2;       // N is a power of two: the mean multiplies by inv_nf
     const float* g_in;      // Adam-only input gradient, or theta0 for init
     float* g_out;           // reduce-only output
     float* master;
@@ -44,5 +46,7 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
                            uint16_t* dst, hipStream_t stream);
 void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                       int32_t defer_min_rows);
+// write windows of the fused step's deferred-write kernel (cycle_ns 0: none)
+void set_write_window(int64_t cycle_ns, int64_t write_ns, int64_t margin_ns, int64_t lead_ns);
 
 }  // namespace zsmr
