@@ -244,12 +244,13 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
 
 /* Launch shape: workgroups per compute unit of the step kernels (reduce,
  * Adam, cast, and the fused step when it writes at once; default 2) and of
- * the copies (receive and ZeRO-3 gather; default 4), each 1..64; defer_tiles,
- * 0..5 (default 5): how many completed 512-element tiles of fused-step
- * results each wave keeps in LDS before it must write them (0 = write at
- * once); and defer_min_rows >= 1 (default 32): the fewest gradient rows for
- * which the fused step defers its writes (it never does with 8 rows or
- * fewer).  Process-wide.  Affects speed only, never results. */
+ * the copies (receive and ZeRO-3 gather; default 1; copies between
+ * addresses that differ by an odd number of 2-byte elements run 4 per CU),
+ * each 1..64; defer_tiles, 0..5 (default 5): how many completed 512-element
+ * tiles of fused-step results each wave keeps in LDS before it must write
+ * them (0 = write at once); and defer_min_rows >= 1 (default 32): the fewest
+ * gradient rows for which the fused step defers its writes (it never does
+ * with 8 rows or fewer).  Process-wide.  Affects speed only, never results. */
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows);
 

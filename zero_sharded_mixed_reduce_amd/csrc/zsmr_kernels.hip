@@ -44,11 +44,8 @@
 #ifndef ZSMR_STEP_CHUNKED
 #define ZSMR_STEP_CHUNKED 0     // step kernel: one contiguous chunk per workgroup
 #endif
-#ifndef ZSMR_COPY_CHUNKED
-#define ZSMR_COPY_CHUNKED 1     // copies: one contiguous chunk per workgroup
-#endif
-#ifndef ZSMR_COPY_STAGE
-#define ZSMR_COPY_STAGE 4       // 128-bit copies: vectors per lane staged in LDS per burst
+#ifndef ZSMR_COPY_BURST_BYTES
+#define ZSMR_COPY_BURST_BYTES 512   // copies: bytes per lane per register burst (32 KB per wave)
 #endif
 #ifndef ZSMR_SPLIT
 #define ZSMR_SPLIT 1            // wave-contiguous element map (see Groups)
@@ -65,9 +62,11 @@ constexpr int kThreads = 256;
 constexpr int kRowBatch = ZSMR_ROW_BATCH;
 constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // workgroups per compute unit of the grid-stride launches (measured on
-// MI355X: the step kernel streams best with 2, the copies with 4)
+// MI355X: the step kernel streams best with 2, the burst copies with 1; the
+// 2-byte copies run 4 per CU)
 int g_step_bpc = 2;
-int g_copy_bpc = 4;
+int g_copy_bpc = 1;
+constexpr int kNarrowCopyBpc = 4;
 // the fused step's deferred-write kernel: tiles kept in LDS per workgroup
 // (0 = write at once with step_vec8_kernel) and workgroups per CU
 int g_defer_tiles = 5;
@@ -675,7 +674,8 @@ struct VecOf<2> { typedef uint16_t T; };
 
 // Copy n elements: `head` scalar elements bring dst (and src, which has the
 // same alignment modulo W) to a W-byte boundary, then W-byte vectors, then
-// the scalar tail.  Lanes of workgroup `part` of `parts` stride the body.
+// the scalar tail.  Workgroup `part` of `parts` takes its share of the
+// vectors.
 template <int W>
 __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, int64_t n,
                                            int64_t head, int64_t part, int64_t parts) {
@@ -685,30 +685,33 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
     const int64_t body_end = head + nb * E;
     const V* s = reinterpret_cast<const V*>(src + head);
     V* d = reinterpret_cast<V*>(dst + head);
-    if constexpr (W == 16 && ZSMR_COPY_STAGE > 0) {
-        // one contiguous chunk per workgroup, moved in bursts: the workgroup
-        // loads kStage groups of kThreads vectors into LDS, then stores them.
-        // Each lane reads back only its own slots; the barriers just line the
-        // waves up so that reads and writes reach HBM in separate bursts.
-        constexpr int kStage = ZSMR_COPY_STAGE;
-        __shared__ V stage[kStage][kThreads];
-        constexpr int64_t group = (int64_t)kThreads * kStage;
-        const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
-        const int64_t lo = part * chunk;
-        const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
-        const int t = static_cast<int>(threadIdx.x);
-        for (int64_t b = lo; b < hi; b += group) {
+    if constexpr (W >= 4) {
+        // Register bursts: each wave loads kBurst vectors per lane (32 KB per
+        // wave) before it stores any, so every wave alternates a read burst
+        // and a write burst; wave w of the launch takes chunks w, w + waves,
+        // ... (neighbouring waves, neighbouring chunks).  The last, partial
+        // chunk goes one guarded vector at a time.
+        constexpr int kBurst = ZSMR_COPY_BURST_BYTES / W;
+        constexpr uint64_t chunk = (uint64_t)kBurst * 64;
+        const uint64_t lane = threadIdx.x & 63u;
+        const uint64_t waves = (uint64_t)parts * (kThreads / 64);
+        const uint64_t wid = (uint64_t)part * (kThreads / 64) + (threadIdx.x >> 6);
+        const uint64_t nv = static_cast<uint64_t>(nb);
+        for (uint64_t c = wid; c * chunk < nv; c += waves) {
+            const uint64_t base = c * chunk + lane;
+            if (base + (chunk - 64) < nv) {
+                V r[kBurst];
 #pragma unroll
-            for (int k = 0; k < kStage; ++k)
-                if (b + k * kThreads + t < hi) stage[k][t] = ld(s + b + k * kThreads + t);
-            __syncthreads();
+                for (int i = 0; i < kBurst; ++i) r[i] = ld(s + base + i * 64);
+                __builtin_amdgcn_sched_barrier(0);   // the whole read burst is issued first
 #pragma unroll
-            for (int k = 0; k < kStage; ++k)
-                if (b + k * kThreads + t < hi) st(d + b + k * kThreads + t, stage[k][t]);
-            __syncthreads();
+                for (int i = 0; i < kBurst; ++i) st(d + base + i * 64, r[i]);
+            } else {
+                for (int i = 0; i < kBurst; ++i)
+                    if (base + i * 64 < nv) st(d + base + i * 64, ld(s + base + i * 64));
+            }
         }
     } else {
-#if ZSMR_COPY_CHUNKED
     // one contiguous chunk per workgroup; kCopyUnroll consecutive groups of
     // kThreads vectors are loaded before any is stored
     constexpr int64_t group = (int64_t)kThreads * kCopyUnroll;
@@ -724,19 +727,6 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
         for (int k = 0; k < kCopyUnroll; ++k)
             if (i + k * kThreads < hi) st(d + i + k * kThreads, tmp[k]);
     }
-#else
-    const int64_t stride = parts * kThreads;
-    // kCopyUnroll independent vectors per lane are loaded before any is stored
-    for (int64_t i = part * kThreads + threadIdx.x; i < nb; i += stride * kCopyUnroll) {
-        V tmp[kCopyUnroll];
-#pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            if (i + k * stride < nb) tmp[k] = ld(s + i + k * stride);
-#pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            if (i + k * stride < nb) st(d + i + k * stride, tmp[k]);
-    }
-#endif
     }
     if (part == 0) {
         const int t = static_cast<int>(threadIdx.x);
@@ -941,9 +931,16 @@ static int copy_width(uintptr_t a, uintptr_t b) {
     return 2;
 }
 
+// Elements copied one by one before the vector body.  W-byte vectors need dst
+// (and src, equal to it modulo W) W-aligned; the burst copies (W >= 4) also
+// start their body on a 128-byte line of dst: HBM writes that cover part of a
+// line cost far more than their bytes (measured on MI355X: a copy whose
+// destination starts 16-96 bytes into a line runs about 8% slower, whatever
+// the source's offset).  At most 63 elements, within one workgroup.
 static int64_t head_for(const void* dst, int w, int64_t n) {
-    const uintptr_t mis = reinterpret_cast<uintptr_t>(dst) % static_cast<uintptr_t>(w);
-    int64_t h = mis ? static_cast<int64_t>((w - mis) / 2) : 0;
+    const uintptr_t align = w >= 4 ? 128 : static_cast<uintptr_t>(w);
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(dst) % align;
+    int64_t h = mis ? static_cast<int64_t>((align - mis) / 2) : 0;
     return h < n ? h : n;
 }
 
@@ -951,7 +948,9 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     if (n <= 0) return hipSuccess;
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
     const int64_t head = head_for(dst, w, n);
-    const dim3 grid(grid_for((n - head) / (w / 2) + 1, g_copy_bpc));
+    const int64_t vecs = (n - head) / (w / 2) + 1;
+    const dim3 grid(w >= 4 ? grid_for(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
+                           : grid_for(vecs, kNarrowCopyBpc));
     switch (w) {
         case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
         case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
@@ -980,8 +979,9 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
             g.head[i] = head_for(g.dst + (int64_t)i * each, w, each);
         }
         const int64_t per = each / (w / 2) + 1;
-        const int64_t cap = (int64_t)cu_count() * g_copy_bpc;
-        int64_t bx = (per + kThreads - 1) / kThreads;
+        const int64_t cap = (int64_t)cu_count() * (w >= 4 ? g_copy_bpc : kNarrowCopyBpc);
+        const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
+        int64_t bx = (units + kThreads - 1) / kThreads;
         const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
         if (bx > lim) bx = lim;
         if (bx < 1) bx = 1;
