@@ -26,17 +26,23 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 METRIC = "fused ZeRO shard-step params/sec and achieved HBM GB/s (% of peak), 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_reduce_amd", "csrc", "zsmr_kernels.hip")
+TRAFFIC_SOURCES = (os.path.join(ROOT, "zero_sharded_mixed_reduce_amd", "csrc", "zsmr_kernels.hip"),
+                   os.path.join(ROOT, "workloads.py"))
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """The measured traffic depends on the kernels and on the workloads'
+    buffer layout: hash both sources."""
+    h = hashlib.sha256()
+    for path in TRAFFIC_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel and workload sources; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -46,7 +52,7 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_and_workload_source_sha256_16") != kernel_source_hash():
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -201,7 +207,7 @@ def bench_share64(args, w):
     if bucketed:
         parts["bucketed_with_backward"] = bucketed
     dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
-    fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows and N > 8
+    fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
                     else "step_vec8_kernel")
     kname = {"fused_step": fused_kernel, "peer_receive": "copy16_kernel"}[dom]
     roof = {"bound": "hbm", "achieved": parts[dom]["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -252,9 +258,13 @@ def bench_world(args, w):
     N = w.world
     byts = w.numel * (2 * N + 26) + (8 * w.numel if w.stage == 3 else 0)
     gbps = byts / ms_step / 1e6
+    kname = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
+             else "step_vec8_kernel")
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": read_traffic("step_vec8_kernel", w.key),
-            "kernel": "step_vec8_kernel", "algorithmic_bytes_per_step": byts}
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": read_traffic(kname, w.key),
+            "kernel": kname, "algorithmic_bytes_per_step": byts,
+            "note": "whole step (every rank's fused launch" + (", and the unit gathers" if w.stage == 3 else "")
+                    + ") timed with HIP events on the compute stream"}
     return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
         "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3)}
@@ -269,7 +279,7 @@ def main():
     ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
     ap.add_argument("--copy-bpc", type=int, default=1, help="workgroups per CU, 16-byte copies")
     ap.add_argument("--defer-tiles", type=int, default=5, help="fused-step tiles kept in LDS (0-5)")
-    ap.add_argument("--defer-min-rows", type=int, default=32,
+    ap.add_argument("--defer-min-rows", type=int, default=16,
                     help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--window-cycle-ns", type=int, default=None,
                     help="fused step: write-window cycle (0 = no windows)")

@@ -344,11 +344,12 @@ WINDOWS = {
 
 @pytest.mark.parametrize("window", list(WINDOWS), ids=list(WINDOWS))
 @pytest.mark.parametrize("kd", [1, 2, 5])
-@pytest.mark.parametrize("rows", [9, 16, 33, 64])
+@pytest.mark.parametrize("rows", [1, 4, 8, 9, 16, 33, 64])
 def test_deferred_windows_match_direct_bits(window, kd, rows):
     """Write windows and ring sizes change only when results are stored:
     the deferred kernel gives the direct kernel's bits, and writes nothing
-    outside the piece."""
+    outside the piece.  With 8 rows or fewer a tile is one row batch (its
+    first and last); windows apply from 32 rows."""
     n = 1024 * 6 * 512 + 2 * 512 + 131           # ~6 tiles per wave, a ragged tail
     say(f"[deferred] window={window} kd={kd} rows={rows} n={n}")
     ref = _fused_run(n, rows, 2, 0, WINDOWS["off"])

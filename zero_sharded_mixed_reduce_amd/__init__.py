@@ -284,7 +284,7 @@ def zero_stage3_unit_state(ctx: Ctx, unit: int):
 
 
 def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 1, defer_tiles: int = 5,
-                          defer_min_rows: int = 32) -> None:
+                          defer_min_rows: int = 16) -> None:
     _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc), int(defer_tiles),
                                         int(defer_min_rows)), "zsmr_set_launch_shape")
 

@@ -67,16 +67,27 @@ constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 int g_step_bpc = 2;
 int g_copy_bpc = 1;
 constexpr int kNarrowCopyBpc = 4;
-// the fused step's deferred-write kernel: tiles kept in LDS per workgroup
-// (0 = write at once with step_vec8_kernel) and workgroups per CU
+// the fused step's deferred-write kernel: tiles kept in LDS per wave with
+// write windows (0 = write at once with step_vec8_kernel), and workgroups
+// per CU
 int g_defer_tiles = 5;
 int g_defer_bpc = 1;
-// ... used when a step reduces at least this many rows (below it the
-// read:write ratio is low and one workgroup per CU streams too little)
-int g_defer_min_rows = 32;
+// ... used when a step reduces at least this many rows.  Measured on MI355X
+// against the direct kernel: single long launches at 16 rows +7%, 24 rows
+// +8.5%, 64 rows +22% (with windows); the 1.558e9-element, 16-rank world
+// +7-9% per step; but the 8-rank worlds, whose steps are many short
+// launches, 2-4% slower, and 1-2 rows 5% slower.
+int g_defer_min_rows = 16;
+// without windows the ring holds at most this many tiles: smaller bursts at
+// ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
+constexpr int kRingWithoutWindows = 2;
 // its write windows, in ns (0: none); converted to clock ticks per device
 // (measured on MI355X over cycles of 35-65 us: 40 / 5 / 1 / 1 us is on the
-// flat top of the curve, and leaves room in the ring of 5 tiles per wave)
+// flat top of the curve, and leaves room in the ring of 5 tiles per wave).
+// Windows pay from 32 rows on; with fewer a tile is read so fast that the
+// ring fills long before a window (at 16 rows the windowed kernel ran 4%
+// slower than with stores at ring-full, which beat the direct kernel by 2%).
+constexpr int kWindowMinRows = 32;
 int64_t g_window_cycle_ns = 40000;
 int64_t g_window_write_ns = 5000;
 int64_t g_window_margin_ns = 1000;
@@ -456,9 +467,7 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 // in registers.  Wave w owns tiles w, w + W, w + 2W, ... (W waves in the
 // grid).  Each lane reads back only what it wrote, so the waves never
 // synchronise.  Results are the same bits as step_vec8_kernel's: only the
-// time at which they are stored changes.  Needs more than kRowBatch rows (the
-// host checks), so that a tile's master/m/v, loaded with its last row batch,
-// never overwrite those of the tile still being finished, and a row stride
+// time at which they are stored changes.  Any number of rows; a row stride
 // of fewer than 2^63 bytes.
 template <int GDT, int PDT, int DV, int KD>
 __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, Window win) {
@@ -548,9 +557,16 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
     const uint32_t nrows = static_cast<uint32_t>(a.nrows);
     uint32_t i_tile = 0, i_row = 0, c_row = 0;
     const char* i_ptr = grads;
+    // two row buffers, each with the master/m/v of the tile whose last batch
+    // it holds: a buffer is consumed before it is issued again, so a tile's
+    // state is never overwritten before its Adam step, whatever N
+    struct State {
+        float w[8], m[8], v[8];
+    };
     u32x4 bufA[kRowBatch], bufB[kRowBatch];
-    float g[8], w[8], m[8], v[8];
-    auto issue = [&](u32x4* buf) {
+    State stA, stB;
+    float g[8];
+    auto issue = [&](u32x4* buf, State& st) {
         const uint32_t e0 = e0_of(i_tile), off = e0 * 2u;
 #pragma unroll
         for (int k = 0; k < kRowBatch; ++k) {
@@ -564,35 +580,27 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
         }
         i_row += kRowBatch;
         if (i_row >= nrows) {      // the tile's last batch: its master/m/v come with it
-            Groups<true>::load32(a.master, e0, e0 + 256u, w);
-            Groups<true>::load32(a.m, e0, e0 + 256u, m);
-            Groups<true>::load32(a.v, e0, e0 + 256u, v);
+            Groups<true>::load32(a.master, e0, e0 + 256u, st.w);
+            Groups<true>::load32(a.m, e0, e0 + 256u, st.m);
+            Groups<true>::load32(a.v, e0, e0 + 256u, st.v);
             ++i_tile;
             i_row = 0;
             i_ptr = grads;
         }
     };
-    auto consume = [&](const u32x4* buf) {
-        // rows in rank order; the tile's sum starts from row 0 itself
-        if (c_row + kRowBatch <= nrows) {
+    auto consume = [&](const u32x4* buf, State& st) {
+        // rows in rank order; the tile's sum starts from row 0 itself (for
+        // N <= 8 a tile's one batch is both its first and its last)
+        const bool full = c_row + kRowBatch <= nrows;
 #pragma unroll
-            for (int k = 0; k < kRowBatch; ++k) {
+        for (int k = 0; k < kRowBatch; ++k) {
+            if (full || c_row + k < nrows) {
                 float t[8];
                 unpack8<GDT>(buf[k], t);
                 if (k == 0 && c_row == 0) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) g[e] = t[e];
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) g[e] = g[e] + t[e];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < kRowBatch; ++k) {
-                if (c_row + k < nrows) {
-                    float t[8];
-                    unpack8<GDT>(buf[k], t);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) g[e] = g[e] + t[e];
                 }
@@ -606,43 +614,43 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
             for (int e = 0; e < 8; ++e) g[e] = mean_of(a, g[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) adam1(a.k, g[e], w[e], m[e], v[e]);
+        for (int e = 0; e < 8; ++e) adam1(a.k, g[e], st.w[e], st.m[e], st.v[e]);
         if (done - flushed == KD) make_room();
         const uint32_t k = done % KD;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            s_w[wv][k][e][lane] = w[e];
-            s_m[wv][k][e][lane] = m[e];
-            s_v[wv][k][e][lane] = v[e];
+            s_w[wv][k][e][lane] = st.w[e];
+            s_m[wv][k][e][lane] = st.m[e];
+            s_v[wv][k][e][lane] = st.v[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            s_h[wv][k][e][lane] = narrow<PDT>(w[2 * e]) | (narrow<PDT>(w[2 * e + 1]) << 16);
+            s_h[wv][k][e][lane] = narrow<PDT>(st.w[2 * e]) | (narrow<PDT>(st.w[2 * e + 1]) << 16);
         ++done;
     };
 
     uint64_t seen = win.cycle ? clock_now() : 0;
-    if (nb) issue(bufA);
+    if (nb) issue(bufA, stA);
     for (uint32_t b = 0; b < nb; b += 2) {
         bool hold = near_window(seen);
         uint64_t want = cyc;
-        if (!hold && b + 1 < nb) issue(bufB);
+        if (!hold && b + 1 < nb) issue(bufB, stB);
         if (win.cycle) seen = clock_now();
-        consume(bufA);
+        consume(bufA, stA);
         if (hold) {
             take_window(want);
-            if (b + 1 < nb) issue(bufB);
+            if (b + 1 < nb) issue(bufB, stB);
             seen = clock_now();
         }
         if (b + 1 >= nb) break;
         hold = near_window(seen);
         want = cyc;
-        if (!hold && b + 2 < nb) issue(bufA);
+        if (!hold && b + 2 < nb) issue(bufA, stA);
         if (win.cycle) seen = clock_now();
-        consume(bufB);
+        consume(bufB, stB);
         if (hold) {
             take_window(want);
-            if (b + 2 < nb) issue(bufA);
+            if (b + 2 < nb) issue(bufA, stA);
             seen = clock_now();
         }
     }
@@ -817,8 +825,9 @@ Window window_ticks() {
 template <int GDT, int PDT, int DV>
 hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_defer_bpc));   // one wave per tile at most
-    const Window w = window_ticks();
-    switch (g_defer_tiles) {
+    const Window w = a.nrows >= kWindowMinRows ? window_ticks() : Window{0, 0, 0, 0};
+    const int kd = w.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
+    switch (kd) {
         case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a, w); break;
         case 2: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 2>), grid, dim3(kThreads), 0, s, a, w); break;
         case 3: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 3>), grid, dim3(kThreads), 0, s, a, w); break;
@@ -831,7 +840,7 @@ hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
     if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST) && kSplit) {
-        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows && a.nrows > kRowBatch) {
+        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows) {
             switch (dv) {
                 case 8:
                 case 4: return launch_deferred<GDT, PDT, 4>(a, s);
