@@ -27,6 +27,16 @@ Readings where the pages leave a step open:
   ceil(Psi/N)); stages 1-2 a reduce-scatter plus an all-gather; stage 3 two
   all-gathers plus a reduce-scatter.  Bytes are elements times 2 (16-bit
   gradients and parameters on the wire).
+* Stage 3 with owner broadcast ("One Poem Suffices: ZeRO" section 4.1.4;
+  "ZeRO, annotated" section 7, "Stage 3, step by step"): rank r keeps the
+  16 bytes per element of its own units only, own(r) elements.  Each weight
+  comes in twice (forward and backward) and each gradient goes once to its
+  owner, so r receives 2(Psi - own(r)) and sends Psi - own(r) elements per
+  step; with equal shares that is the same 3(N-1)/N Psi as the split layout.
+  Its peak adds the borrowed units live at once (its own units need no
+  buffer): at most ``max_live`` consecutive units of the schedule, counting
+  only units r does not own.  Ranks differ when the units do not split
+  evenly; ``rank=None`` reports the rank with the largest peak.
 """
 from __future__ import annotations
 
@@ -64,7 +74,28 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1) -> Bytes:
+def _owner_bytes(lay: Layout, rank: int, gather_bytes: int, max_live: int) -> Bytes:
+    own = lay.own_numel(rank)
+    p16, grad, master, m, v = B_P16 * own, B_GRAD * own, B_MASTER * own, B_M * own, B_V * own
+    resident = p16 + grad + master + m + v
+    borrowed = [0 if o == rank else size for size, o in zip(lay.units, lay.owners)]
+    k = max(1, min(max_live, len(borrowed)))
+    gathered = gather_bytes * max(sum(borrowed[i:i + k]) for i in range(len(borrowed) - k + 1))
+    unit_grad = B_GRAD * max(lay.units)
+    rs = lay.numel - own
+    ag = 2 * (lay.numel - own)
+    elems = rs + ag
+    return Bytes(p16, grad, master, m, v, resident, gathered, resident + gathered, unit_grad,
+                 rs, ag, 0, elems, elems * WIRE_BYTES)
+
+
+def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1,
+                   rank=None) -> Bytes:
+    if lay.owner_broadcast:
+        if rank is not None:
+            return _owner_bytes(lay, rank, gather_bytes, max_live)
+        per = [_owner_bytes(lay, r, gather_bytes, max_live) for r in range(lay.world)]
+        return max(per, key=lambda b: b.peak)        # max() keeps the first (lowest) rank on ties
     n, w = lay.numel, lay.world
     shard_opt, shard_grad, shard_param = FLAGS[lay.stage]
     s_tot = lay.shard_numel if lay.stage else n

@@ -12,6 +12,15 @@ Test infrastructure only (see the package header).
   zero pad; rank r owns [Q_u + r*S_u, Q_u + (r+1)*S_u) of the padded vector,
   where Q_u is the padded start of unit u.  Data parallel keeps no shard: the
   rank's "owned" range is the whole vector.
+* Stage 3, owner broadcast ("One Poem Suffices: ZeRO" section 4.1.4, the
+  64-device, 192-block example; "ZeRO, annotated" sections 5.3 and 7, where
+  GPU i owns shard i): every unit belongs whole to one rank, which sends it to
+  the others when it is needed.  Nothing is padded; the vector keeps its
+  natural order.  The pages only show equal partitions (each rank owning the
+  same number of equal blocks); the reading taken for any unit sizes is that
+  unit u goes to the rank whose equal share [r*Psi/N, (r+1)*Psi/N) holds the
+  unit's midpoint, which gives exactly the pages' contiguous k-blocks-per-rank
+  ownership when U = k*N equal units.
 """
 from __future__ import annotations
 
@@ -37,6 +46,11 @@ class Layout:
     shard_u: tuple              # S_u per unit (stage 3); (S,) for stages 1-2; (Psi,) for DP
     unit_start: tuple           # true start P_u of each unit in [0, Psi)
     unit_pstart: tuple          # padded start Q_u of each unit
+    owners: tuple = ()          # owner broadcast: the rank owning each unit; () otherwise
+
+    @property
+    def owner_broadcast(self) -> bool:
+        return bool(self.owners)
 
     @property
     def n_units(self) -> int:
@@ -44,13 +58,22 @@ class Layout:
 
     @property
     def padded_numel(self) -> int:
-        if self.stage == 0:
+        if self.stage == 0 or self.owner_broadcast:
             return self.numel
         return sum(self.world * s for s in self.shard_u)
 
+    def own_numel(self, rank: int) -> int:
+        """Elements of optimizer state ``rank`` keeps."""
+        if self.owner_broadcast:
+            return sum(n for n, o in zip(self.units, self.owners) if o == rank)
+        return self.shard_numel
+
     @property
     def shard_numel(self) -> int:
-        """Elements of optimizer state each rank keeps."""
+        """Elements of optimizer state each rank keeps (owner broadcast: the
+        largest over the ranks)."""
+        if self.owner_broadcast:
+            return max(self.own_numel(r) for r in range(self.world))
         return sum(self.shard_u)
 
     def owned(self, rank: int, unit: int = 0):
@@ -66,16 +89,22 @@ class Layout:
                 raise IndexError(unit)
             s = self.shard_u[0]
             return rank * s, s
+        if self.owner_broadcast:
+            return self.unit_start[unit], (self.units[unit] if self.owners[unit] == rank else 0)
         s = self.shard_u[unit]
         return self.unit_pstart[unit] + rank * s, s
 
     def local_offset(self, unit: int) -> int:
-        """Offset of ``unit``'s piece inside a rank's concatenated shard."""
+        """Offset of ``unit``'s piece inside a rank's concatenated shard (owner
+        broadcast: inside its owner's concatenated units)."""
+        if self.owner_broadcast:
+            o = self.owners[unit]
+            return sum(self.units[v] for v in range(unit) if self.owners[v] == o)
         return sum(self.shard_u[:unit])
 
     def param_index(self, padded_pos: int) -> Optional[int]:
         """True parameter index held at a padded position, or None for pad."""
-        if self.stage == 0:
+        if self.stage == 0 or self.owner_broadcast:
             return padded_pos if 0 <= padded_pos < self.numel else None
         if self.stage in (1, 2):
             return padded_pos if padded_pos < self.numel else None
@@ -90,7 +119,7 @@ class Layout:
         """Vectorised ``param_index``: (param indices, valid mask) for positions."""
         import numpy as np
         pos = np.asarray(positions, dtype=np.int64)
-        if self.stage in (0, 1, 2):
+        if self.stage in (0, 1, 2) or self.owner_broadcast:
             return pos.copy(), pos < self.numel
         par = np.zeros_like(pos)
         ok = np.zeros(pos.shape, dtype=bool)
@@ -104,14 +133,30 @@ class Layout:
         return par, ok
 
 
+def unit_owners(units: Sequence[int], world: int) -> tuple:
+    """Owner of each unit under owner broadcast: the rank whose equal share of
+    the vector holds the unit's midpoint, floor(N * (start + size/2) / Psi)."""
+    numel = sum(units)
+    owners, start = [], 0
+    for size in units:
+        owners.append(min(world - 1, (world * (2 * start + size)) // (2 * numel)))
+        start += size
+    return tuple(owners)
+
+
 def make_layout(numel: int, world: int, stage: int, units: Optional[Sequence[int]] = None,
-                pad: bool = False) -> Layout:
+                pad: bool = False, owner_broadcast: bool = False) -> Layout:
     if numel < 1 or world < 1 or stage not in (0, 1, 2, 3):
         raise ValueError("bad numel/world/stage")
+    if owner_broadcast and stage != 3:
+        raise ValueError("owner broadcast is a stage-3 layout")
     unit_list: List[int] = list(units) if units else [numel]
     if any(u < 1 for u in unit_list) or sum(unit_list) != numel:
         raise ValueError("unit sizes must be positive and sum to numel")
     starts = [sum(unit_list[:i]) for i in range(len(unit_list))]
+    if owner_broadcast:
+        return Layout(numel, world, 3, tuple(unit_list), pad, tuple(unit_list), tuple(starts),
+                      tuple(starts), unit_owners(unit_list, world))
     if stage == 0:
         shard_u = (numel,)
     elif stage in (1, 2):

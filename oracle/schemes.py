@@ -23,6 +23,11 @@ Readings where the pages leave a step open:
   gradients arrive; elementwise, this equals running it after the whole
   backward pass.
 * ``t`` advances once per step, not per unit.
+* Owner broadcast (``ZeRO3Owner``; "One Poem Suffices: ZeRO" section 4.1.4,
+  "ZeRO, annotated" section 7): whole units belong to one rank each.  A
+  unit's owner sends its 16-bit copy to the others for the forward pass and
+  again for the backward pass; its gradients are summed onto the owner (the
+  same rank-order fp32 mean), which alone updates the unit.
 """
 from __future__ import annotations
 
@@ -75,6 +80,46 @@ class Stage3Schedule:
         self.live.remove(unit)
         self.releases[unit] += 1
         self.live_bytes -= self.gather_bytes * self.lay.world * self.lay.shard_u[unit]
+
+
+class OwnerSchedule:
+    """Gather/release state machine of ZeRO-3 with owner broadcast, with
+    per-rank counters: a gather of unit u delivers it to every rank but its
+    owner, which needs no buffer for it."""
+
+    def __init__(self, lay: Layout, gather_bytes: int = 2, max_live: int = 1):
+        self.lay = lay
+        self.gather_bytes = gather_bytes
+        self.max_live = max_live
+        self.live: List[int] = []
+        self.gathers = [0] * lay.n_units
+        self.releases = [0] * lay.n_units
+        self.ag_elems = [0] * lay.world              # received per rank
+        self.live_bytes = [0] * lay.world
+        self.peak_live_bytes = [0] * lay.world
+
+    def gather(self, unit: int) -> None:
+        if unit in self.live:
+            raise ScheduleError(f"unit {unit} is already gathered")
+        if len(self.live) >= self.max_live:
+            raise ScheduleError(f"{len(self.live)} unit(s) live, limit {self.max_live}")
+        self.live.append(unit)
+        self.gathers[unit] += 1
+        size = self.lay.units[unit]
+        for r in range(self.lay.world):
+            if r != self.lay.owners[unit]:
+                self.ag_elems[r] += size
+                self.live_bytes[r] += self.gather_bytes * size
+                self.peak_live_bytes[r] = max(self.peak_live_bytes[r], self.live_bytes[r])
+
+    def release(self, unit: int) -> None:
+        if unit not in self.live:
+            raise ScheduleError(f"unit {unit} is not gathered")
+        self.live.remove(unit)
+        self.releases[unit] += 1
+        for r in range(self.lay.world):
+            if r != self.lay.owners[unit]:
+                self.live_bytes[r] -= self.gather_bytes * self.lay.units[unit]
 
 
 class _Scheme:
@@ -301,17 +346,94 @@ class ZeRO3(_Scheme):
         return self._unpad(self._padded(self.p16))
 
 
+class ZeRO3Owner(_Scheme):
+    """ZeRO-3 with whole units owned by single ranks: the owner broadcasts a
+    unit when it is needed; gradients are reduced onto the owner."""
+    stage = 3
+
+    def __init__(self, lay: Layout, theta0, dtype16, lr=1e-2, betas=(0.9, 0.999), eps=1e-8,
+                 max_live: int = 1, use: Optional[Callable[[str, int, np.ndarray], None]] = None):
+        if not lay.owner_broadcast:
+            raise ValueError("ZeRO3Owner needs an owner-broadcast layout")
+        self.schedule = OwnerSchedule(lay, gather_bytes=2, max_live=max_live)
+        self.use = use
+        super().__init__(lay, theta0, dtype16, lr, betas, eps)
+
+    def _init(self, theta: np.ndarray) -> None:
+        lay = self.lay
+        # unit u's bands live on its owner only
+        self.master, self.m, self.v, self.p16 = {}, {}, {}, {}
+        for u in range(lay.n_units):
+            p, n = lay.unit_start[u], lay.units[u]
+            self.master[u] = theta[p:p + n].copy()
+            self.m[u] = np.zeros(n, np.float32)
+            self.v[u] = np.zeros(n, np.float32)
+            self.p16[u] = nm.cast16(self.master[u], self.dtype)
+
+    def gather(self, unit: int) -> np.ndarray:
+        """The owner's 16-bit copy of the unit, as every other rank receives it."""
+        self.schedule.gather(unit)
+        return self.p16[unit].copy()
+
+    def release(self, unit: int) -> None:
+        self.schedule.release(unit)
+
+    def _use(self, phase: str, unit: int, buf: np.ndarray) -> None:
+        if self.use is not None:
+            self.use(phase, unit, buf)
+
+    def step(self, grads16) -> None:
+        self.t += 1
+        lay, w = self.lay, self.lay.world
+        rows = self._rows(grads16)
+        k = self._consts()
+        for u in range(lay.n_units):                         # forward
+            buf = self.gather(u)
+            self._use("forward", u, buf)
+            self.release(u)
+        for u in reversed(range(lay.n_units)):               # backward
+            buf = self.gather(u)
+            self._use("backward", u, buf)
+            p, n, owner = lay.unit_start[u], lay.units[u], lay.owners[u]
+            g = nm.reduce_rank_order([row[p:p + n] for row in rows])
+            for r in range(w):
+                if r != owner:
+                    self.rs_elems[r] += n                    # r's contribution to the owner
+            self.master[u], self.m[u], self.v[u] = nm.adam_update(
+                self.master[u], self.m[u], self.v[u], g, k)
+            self.p16[u] = nm.cast16(self.master[u], self.dtype)
+            self.release(u)
+        self.ag_elems = list(self.schedule.ag_elems)
+
+    def _cat(self, band) -> np.ndarray:
+        return np.concatenate([band[u] for u in range(self.lay.n_units)])
+
+    def full_master(self):
+        return self._cat(self.master)
+
+    def full_m(self):
+        return self._cat(self.m)
+
+    def full_v(self):
+        return self._cat(self.v)
+
+    def working_copy(self, rank: int = 0):
+        return self._cat(self.p16)
+
+
 SCHEMES = {0: DP, 1: ZeRO1, 2: ZeRO2, 3: ZeRO3}
 
 
 def run(stage: int, numel: int, world: int, theta0: np.ndarray,
         grads_per_step: Callable[[int], Sequence[np.ndarray]], steps: int, dtype16: str,
         lr: float, betas=(0.9, 0.999), eps: float = 1e-8, units=None, pad: bool = False,
-        **kw):
+        owner_broadcast: bool = False, **kw):
     """Build a scheme and run ``steps`` steps; ``grads_per_step(t)`` returns the
-    N per-rank 16-bit gradient vectors of step t (t = 1..steps)."""
-    lay = make_layout(numel, world, stage, units, pad)
-    sch = SCHEMES[stage](lay, theta0, dtype16, lr, betas, eps, **kw)
+    N per-rank 16-bit gradient vectors of step t (t = 1..steps).  Stage 3 with
+    ``owner_broadcast`` runs ``ZeRO3Owner``."""
+    lay = make_layout(numel, world, stage, units, pad, owner_broadcast)
+    cls = ZeRO3Owner if owner_broadcast else SCHEMES[stage]
+    sch = cls(lay, theta0, dtype16, lr, betas, eps, **kw)
     for t in range(1, steps + 1):
         sch.step(grads_per_step(t))
     return sch

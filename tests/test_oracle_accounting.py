@@ -12,6 +12,15 @@ from oracle.layout import IndivisibleError, make_layout
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_accounting.txt")
 
 
+def _units(tok):
+    if tok == "-":
+        return None
+    if "x" in tok:
+        k, size = tok.split("x")
+        return [int(size)] * int(k)
+    return [int(x) for x in tok.split(",")]
+
+
 def load_pins():
     pins = []
     with open(GOLDEN) as f:
@@ -20,8 +29,9 @@ def load_pins():
             if not line or line.startswith("#"):
                 continue
             tok = shlex.split(line)
-            pins.append(dict(id=tok[0], numel=int(tok[1]), world=int(tok[2]), stage=int(tok[3]),
-                             units=None if tok[4] == "-" else [int(x) for x in tok[4].split(",")],
+            pins.append(dict(id=tok[0], numel=int(tok[1]), world=int(tok[2]),
+                             stage=int(tok[3].rstrip("o")), owner=tok[3].endswith("o"),
+                             units=_units(tok[4]),
                              pad=bool(int(tok[5])), gather_bytes=int(tok[6]), quantity=tok[7],
                              printed=Decimal(tok[8]), scale=Decimal(tok[9]), decimals=int(tok[10]),
                              source=" ".join(tok[11:])))
@@ -29,7 +39,8 @@ def load_pins():
 
 
 def quantity(pin):
-    lay = make_layout(pin["numel"], pin["world"], pin["stage"], pin["units"], pin["pad"])
+    lay = make_layout(pin["numel"], pin["world"], pin["stage"], pin["units"], pin["pad"],
+                      owner_broadcast=pin["owner"])
     b = acc.bytes_per_rank(lay, gather_bytes=pin["gather_bytes"])
     q = pin["quantity"]
     if q == "resident":
@@ -46,6 +57,9 @@ def quantity(pin):
         return Decimal(b.rs_elems)
     if q == "traffic_bytes_x_n_over_psi":
         return Decimal(b.traffic_bytes) * pin["world"] / ((pin["world"] - 1) * Decimal(pin["numel"]))
+    if q == "peak_params_x_n_over_psi":
+        held = Decimal(b.res_p16) / acc.B_P16 + Decimal(b.gathered) / pin["gather_bytes"]
+        return held * pin["world"] / Decimal(pin["numel"])
     raise KeyError(q)
 
 
@@ -138,3 +152,55 @@ def test_layout_owned_ranges_tile_the_padded_vector():
             par, ok = lay.padded_to_param(range(lay.padded_numel))
             assert sorted(par[ok].tolist()) == list(range(numel))
             assert int(ok.sum()) == numel
+
+
+# ------------------------------------------------------- owner broadcast --
+def test_owner_rule_gives_the_pages_contiguous_partitions():
+    # "One Poem Suffices: ZeRO" s4.1.4: 64 devices, 192 blocks, 3 per device in
+    # model order; "ZeRO, annotated" s7: GPU i owns shard i
+    assert make_layout(192, 64, 3, [1] * 192, owner_broadcast=True).owners == \
+        tuple(u // 3 for u in range(192))
+    assert make_layout(8, 4, 3, [2] * 4, owner_broadcast=True).owners == (0, 1, 2, 3)
+
+
+def test_owner_peak_two_64ths_either_reading():
+    # the 3 blocks a device broadcasts as one unit (max_live 1), or 192
+    # single-block units with the 3 of a partition live at once: both 2/64
+    for units, live in (([3000] * 64, 1), ([1000] * 192, 3)):
+        b = acc.bytes_per_rank(make_layout(192000, 64, 3, units, owner_broadcast=True),
+                               max_live=live)
+        assert (b.res_p16 // 2 + b.gathered // 2) * 64 == 2 * 192000
+
+
+@pytest.mark.parametrize("world,k", [(4, 1), (4, 3), (8, 4), (64, 3)])
+def test_owner_balanced_equals_split_layout(world, k):
+    # equal shares: the same bytes and the same 3(N-1)/N traffic as the
+    # per-unit split (f3's claim); only the peak's gathered part differs
+    size = 192                                           # divisible by every world here
+    units = [size] * (k * world)
+    own = acc.bytes_per_rank(make_layout(size * k * world, world, 3, units, owner_broadcast=True))
+    split = acc.bytes_per_rank(make_layout(size * k * world, world, 3, units))
+    assert own.resident == split.resident
+    assert (own.rs_elems, own.ag_elems) == (split.rs_elems, split.ag_elems)
+    assert own.gathered == 2 * size                      # one borrowed unit
+    assert split.gathered == 2 * size                    # one unit, all N shards
+
+
+def test_owner_accounting_per_rank_closed_forms():
+    rnd = random.Random(11)
+    for _ in range(200):
+        world = rnd.randint(1, 9)
+        units = [rnd.randint(1, 100) for _ in range(rnd.randint(1, 12))]
+        numel = sum(units)
+        lay = make_layout(numel, world, 3, units, owner_broadcast=True)
+        assert sum(lay.own_numel(r) for r in range(world)) == numel
+        assert all(lay.owners[i] <= lay.owners[i + 1] for i in range(len(units) - 1))
+        per = [acc.bytes_per_rank(lay, rank=r) for r in range(world)]
+        for r, b in enumerate(per):
+            own = lay.own_numel(r)
+            assert b.resident == 16 * own
+            assert (b.rs_elems, b.ag_elems) == (numel - own, 2 * (numel - own))
+            borrowed = [0 if o == r else n for n, o in zip(units, lay.owners)]
+            assert b.gathered == 2 * max(borrowed)
+        worst = acc.bytes_per_rank(lay)
+        assert worst.peak == max(b.peak for b in per)

@@ -234,3 +234,75 @@ def test_schedule_errors():
     pre.gather(0)
     pre.gather(1)
     assert pre.peak_live_bytes == acc.bytes_per_rank(lay, max_live=2).gathered
+
+
+# ------------------------------------------------------- owner broadcast --
+@pytest.mark.parametrize("numel,world,units", [
+    (8, 4, [2, 2, 2, 2]),                          # the pages' tiny model, GPU i owns layer i
+    (65536, 4, [16384] * 4),
+    (6000, 5, [1000, 7, 2993, 1500, 500]),         # uneven units: rank 1 owns none
+    (4096, 3, [4096]),                             # one unit: rank 1 owns everything
+    (777, 1, [300, 477]),                          # a world of one
+])
+def test_owner_broadcast_computes_the_same_model(numel, world, units):
+    # "One Poem Suffices: ZeRO" s4.1.4 / "ZeRO, annotated" s7: the owner
+    # layout changes who stores and sends what, never the arithmetic
+    theta = synth.theta0(0, np.arange(numel))
+    g = grads_fn(numel, world, "bf16", 1e-2)
+    own = sc.run(3, numel, world, theta, g, 3, "bf16", 1e-3, units=units, owner_broadcast=True)
+    dp = sc.run(0, numel, world, theta, g, 3, "bf16", 1e-3)
+    for a, b in ((own.full_master(), dp.full_master()), (own.full_m(), dp.full_m()),
+                 (own.full_v(), dp.full_v())):
+        assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(own.working_copy(), dp.working_copy())
+
+
+def test_owner_broadcast_schedule_and_counters():
+    numel, world, T = 6000, 5, 3
+    units = [1000, 7, 2993, 1500, 500]
+    lay = make_layout(numel, world, 3, units, owner_broadcast=True)
+    seen = []
+
+    def use(phase, u, buf):
+        seen.append((phase, u))
+        p, n = lay.unit_start[u], lay.units[u]
+        assert np.array_equal(buf, s.working_copy()[p:p + n])     # the owner's copy
+    theta = synth.theta0(0, np.arange(numel))
+    s = sc.ZeRO3Owner(lay, theta, "bf16", 1e-3, use=use)
+    g = grads_fn(numel, world, "bf16", 1e-3)
+    for t in range(1, T + 1):
+        s.step(g(t))
+    U = len(units)
+    order = [("forward", u) for u in range(U)] + [("backward", u) for u in reversed(range(U))]
+    assert seen == order * T
+    assert s.schedule.gathers == [2 * T] * U == s.schedule.releases
+    for r in range(world):
+        b = acc.bytes_per_rank(lay, rank=r)
+        assert (s.rs_elems[r], s.ag_elems[r]) == (T * b.rs_elems, T * b.ag_elems)
+        assert s.schedule.peak_live_bytes[r] == b.gathered
+    # the owners hold no buffer for their own units: rank 0 owns units 0 and 1,
+    # so its largest borrowed unit is unit 2, a non-owner's is unit 2 as well
+    assert s.schedule.peak_live_bytes == [2 * 2993, 2 * 2993, 2 * 1500, 2 * 2993, 2 * 2993]
+
+
+def test_owner_schedule_errors_and_prefetch():
+    lay = make_layout(64, 4, 3, [16] * 4, owner_broadcast=True)
+    sch = sc.OwnerSchedule(lay)
+    with pytest.raises(sc.ScheduleError):
+        sch.release(0)
+    sch.gather(0)
+    with pytest.raises(sc.ScheduleError):
+        sch.gather(0)
+    with pytest.raises(sc.ScheduleError):
+        sch.gather(1)                       # max_live = 1
+    sch.release(0)
+    pre = sc.OwnerSchedule(lay, max_live=2)
+    pre.gather(0)                           # a forward pass with the next unit prefetched
+    for u in range(1, 4):
+        pre.gather(u)
+        pre.release(u - 1)
+    pre.release(3)
+    for r in range(4):
+        assert pre.peak_live_bytes[r] == acc.bytes_per_rank(lay, max_live=2, rank=r).gathered
+    with pytest.raises(ValueError):
+        sc.ZeRO3Owner(make_layout(64, 4, 3, [16] * 4), np.zeros(64, np.float32), "bf16")
