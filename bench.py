@@ -243,7 +243,7 @@ def bench_world(args, w):
         # each unit size's gradients are made once, so that whole steps --
         # gathers, fused launches and (with --prefetch) the overlap of the next
         # gather -- are timed end to end on the compute stream
-        world = wl.Stage3World(w, prefetch=args.prefetch, fixed_grads=True)
+        world = wl.Stage3World(w, prefetch=args.prefetch, fixed_grads=True, owner=args.owner)
     else:
         world = wl.ShardedWorld(w)
         world.gen_grads(1)
@@ -267,7 +267,8 @@ def bench_world(args, w):
                     + ") timed with HIP events on the compute stream"}
     return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
-        "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3)}
+        "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3),
+        "stage3_layout": ("owner_broadcast" if args.owner else "per_unit_split") if w.stage == 3 else None}
 
 
 def main():
@@ -291,6 +292,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefetch", action="store_true",
                     help="ZeRO-3 workload: gather the next unit while the current one is in use")
+    ap.add_argument("--owner", action="store_true",
+                    help="ZeRO-3 workload: whole units owned by single ranks (owner broadcast)")
     ap.add_argument("--buckets", type=int, default=0,
                     help="share64: also measure steps with the simulated backward, bucketed")
     args = ap.parse_args()

@@ -66,6 +66,11 @@ extern "C" {
 #define ZSMR_ZERO1 1  /* optimizer state sharded                            */
 #define ZSMR_ZERO2 2  /* + gradients sharded                                */
 #define ZSMR_ZERO3 3  /* + parameters sharded, gathered per unit            */
+/* stage 3 with owner broadcast ("One Poem Suffices: ZeRO" section 4.1.4, the
+ * 64-device, 192-block example; "ZeRO, annotated" section 7, where GPU i owns
+ * shard i): every unit belongs whole to one rank, which sends it to the
+ * others when it is needed; gradients are summed onto the owner */
+#define ZSMR_ZERO3_OWNER 4
 
 typedef struct zsmr_ctx zsmr_ctx;
 
@@ -81,8 +86,8 @@ typedef struct zsmr_adam {
 typedef struct zsmr_layout_info {
     int64_t numel;         /* Psi                                               */
     int64_t padded_numel;  /* flat length including the zero pad (DP: Psi)      */
-    int64_t shard_numel;   /* elements of optimizer state one rank keeps        */
-    int64_t max_unit_numel;/* largest padded unit N*S_u (stage 3), else padded  */
+    int64_t shard_numel;   /* elements of optimizer state one rank keeps (stage 4: the most any rank keeps) */
+    int64_t max_unit_numel;/* largest padded unit N*S_u (stage 3), largest unit (stage 4), else padded */
     int32_t world, stage, n_units, grad_dtype, param_dtype, pad;
 } zsmr_layout_info;
 
@@ -92,7 +97,10 @@ typedef struct zsmr_layout_info {
  * the elements one rank sends per step: DP one all-reduce of 2(N-1)
  * chunks of ceil(Psi/N); stages 1-2 a reduce-scatter plus an all-gather of
  * (N-1)*S each; stage 3 a reduce-scatter plus two all-gathers of
- * (N-1)*sum(S_u) each ("ZeRO, annotated" section 7).  Bytes = elements x 2. */
+ * (N-1)*sum(S_u) each ("ZeRO, annotated" section 7).  Stage 4, rank r owning
+ * own(r) elements: 16*own(r) resident; it receives the Psi - own(r) elements
+ * it does not own twice (ag) and sends their gradients once (rs); its peak
+ * counts only borrowed units (its own need no buffer).  Bytes = elements x 2. */
 typedef struct zsmr_bytes {
     int64_t res_p16, res_grad, res_master, res_m, res_v;
     int64_t resident;      /* sum of the five bands                             */
@@ -104,7 +112,9 @@ typedef struct zsmr_bytes {
 } zsmr_bytes;
 
 /* What the calls made on a context actually did, for one rank: elements that
- * rank received through each simulated collective, plus the ZeRO-3 schedule. */
+ * rank received through each simulated all-gather and all-reduce, and sent
+ * through each reduce-scatter (at stages 1-3 the same as it received), plus
+ * the ZeRO-3 schedule (live and peak bytes are this rank's). */
 typedef struct zsmr_counters {
     int64_t rs_elems, ag_elems, ar_elems;
     int64_t traffic_elems, traffic_bytes;
@@ -119,7 +129,8 @@ const char* zsmr_strerror(int32_t status);
 const char* zsmr_last_hip_error(void);
 
 /* Build the partition of Psi = numel elements over `world` ranks (host only).
- * stage: ZSMR_DP..ZSMR_ZERO3.  grad_dtype/param_dtype: ZSMR_FP16 or ZSMR_BF16.
+ * stage: ZSMR_DP..ZSMR_ZERO3_OWNER.  grad_dtype/param_dtype: ZSMR_FP16 or
+ * ZSMR_BF16.
  * units: n_units sizes summing to numel (ZeRO-3 splits each unit N ways with
  * its own pad, "ZeRO and FSDP", "ZeRO-3 and FSDP"); n_units == 0 with
  * unit_numel == NULL means one unit of numel.  Stages 0-2 ignore the unit
@@ -128,8 +139,11 @@ const char* zsmr_last_hip_error(void);
  * pad == 1: shards are ceil(./N) and the tail is zero (ZeroAdam in "ZeRO and
  * FSDP").  Rank r of stages 1-2 owns [r*S, (r+1)*S); of stage 3 owns
  * [Q_u + r*S_u, Q_u + (r+1)*S_u) of unit u, Q_u its padded start; a data
- * parallel rank "owns" [0, Psi).  *out receives a context to free with
- * zero_destroy(). */
+ * parallel rank "owns" [0, Psi).  Stage 4 keeps units whole and unpadded in
+ * their natural order: unit u goes to the rank whose equal share
+ * [r*Psi/N, (r+1)*Psi/N) holds the unit's midpoint (with U = k*N equal units
+ * the pages' k consecutive units per rank); pad is ignored.  *out receives a
+ * context to free with zero_destroy(). */
 int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
                          int32_t grad_dtype, int32_t param_dtype, int32_t pad,
                          const int64_t* unit_numel, int32_t n_units);
@@ -142,16 +156,27 @@ int32_t zero_layout_info(const zsmr_ctx* ctx, zsmr_layout_info* out);
 
 /* Index map (host only): padded flat offset and length of what `rank` owns
  * in `unit` (stages 0-2: unit must be 0), and the offset of that piece inside
- * the rank's own concatenated shard.  Any output pointer may be NULL. */
+ * the rank's own concatenated shard.  Stage 4: the unit's start and length
+ * for its owner, length 0 for every other rank; the local offset is within
+ * the owner's units.  Any output pointer may be NULL. */
 int32_t zero_layout(const zsmr_ctx* ctx, int32_t rank, int32_t unit,
                     int64_t* offset, int64_t* len, int64_t* local_offset);
+
+/* Stage 4: the rank owning `unit` (host only).  ZSMR_ERR_ARG at other stages. */
+int32_t zero_unit_owner(const zsmr_ctx* ctx, int32_t unit, int32_t* owner);
 
 /* Accounting for one rank (pure, host only).  gather_bytes: bytes per
  * gathered element of the stage-3 peak (0 = the 16-bit working copy's 2; the
  * prototype's fp32 gather is 4).  max_live: units gathered at once (0 = 1;
- * 2 = prefetch of the next unit). */
+ * 2 = prefetch of the next unit).  Ranks are alike at stages 0-3; at stage 4
+ * this reports the rank with the largest peak (the lowest such rank). */
 int32_t zero_bytes_per_rank(const zsmr_ctx* ctx, int32_t gather_bytes, int32_t max_live,
                             zsmr_bytes* out);
+
+/* The same accounting for a given rank (stage 4: ranks owning different
+ * amounts hold and move different amounts). */
+int32_t zero_bytes_of_rank(const zsmr_ctx* ctx, int32_t rank, int32_t gather_bytes,
+                           int32_t max_live, zsmr_bytes* out);
 
 /* Counters of `rank` accumulated by the calls below since creation or the
  * last zero_reset_counters() (host only). */
@@ -231,7 +256,12 @@ int32_t zero_stage3_set_max_live(zsmr_ctx* ctx, int32_t max_live);
  * array of N device pointers, shard r of S_u elements) into unit_buf (N*S_u
  * elements, shard r at r*S_u).  ZSMR_ERR_STATE if the unit is already live or
  * max_live units are live.  Counts one all-gather of (N-1)*S_u elements
- * received by every rank, and the live/peak gathered bytes. */
+ * received by every rank, and the live/peak gathered bytes.
+ * Stage 4 (owner broadcast): shard_ptrs holds one pointer, the owner's 16-bit
+ * copy of the whole unit (P_u elements), which is copied to unit_buf (they
+ * may not overlap); every rank but the owner receives P_u elements and holds
+ * P_u x 2 bytes while the unit is live.  The schedule calls below work the
+ * same at stages 3 and 4. */
 int32_t zero_stage3_unit_gather(zsmr_ctx* ctx, int32_t unit, const void* const* shard_ptrs,
                                 void* unit_buf, hipStream_t stream);
 

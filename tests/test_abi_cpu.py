@@ -104,7 +104,7 @@ def test_init_errors():
         z.zero_init_shards(10, 4, 3, "bf16", units=[5, 5])
     assert e.value.code == z.ZSMR_ERR_INDIVISIBLE
     for bad in [dict(numel=0, world=1, stage=0), dict(numel=8, world=0, stage=0),
-                dict(numel=8, world=2, stage=4), dict(numel=8, world=2, stage=3, units=[4, 5])]:
+                dict(numel=8, world=2, stage=5), dict(numel=8, world=2, stage=3, units=[4, 5])]:
         with pytest.raises(z.ZsmrError) as e:
             z.zero_init_shards(bad["numel"], bad["world"], bad["stage"], "bf16", units=bad.get("units"))
         assert e.value.code == z.ZSMR_ERR_ARG
@@ -197,3 +197,75 @@ def test_write_window_arguments():
     z.zsmr_set_write_window(0, 0, 0, 0)
     z.zsmr_set_write_window(1000, 2, 997, 1)
     z.zsmr_set_write_window()                 # back to the defaults
+
+
+
+def _owner_case(numel, world, units):
+    ctx = z.zero_init_shards(numel, world, z.ZSMR_ZERO3_OWNER, "bf16", units=units)
+    lay = make_layout(numel, world, 3, units, owner_broadcast=True)
+    return ctx, lay
+
+
+@pytest.mark.parametrize("numel,world,units", [
+    (8, 4, [2] * 4), (192_000, 64, [3000] * 64), (192_000, 64, [1000] * 192),
+    (8_030_261_248, 8, [1_050_677_248] + [218_112_000] * 32),
+    (6000, 5, [1000, 7, 2993, 1500, 500]),
+])
+def test_owner_layout_and_accounting_match_oracle(numel, world, units):
+    ctx, lay = _owner_case(numel, world, units)
+    info = ctx.info()
+    assert info["padded_numel"] == numel and info["shard_numel"] == lay.shard_numel
+    assert info["max_unit_numel"] == max(units)
+    for u in range(len(units)):
+        assert z.zero_unit_owner(ctx, u) == lay.owners[u]
+        for r in range(world):
+            off, ln, loc = z.zero_layout(ctx, r, u)
+            assert (off, ln) == lay.owned(r, u)
+            assert loc == lay.local_offset(u)
+    for gb, ml in ((2, 1), (4, 2), (2, 3)):
+        for r in range(world):
+            got = z.zero_bytes_of_rank(ctx, r, gb, ml)
+            want = acc.bytes_per_rank(lay, gather_bytes=gb, max_live=ml, rank=r)
+            for k, v in got.items():
+                assert v == getattr(want, k), (r, k)
+        worst = z.zero_bytes_per_rank(ctx, gb, ml)
+        want = acc.bytes_per_rank(lay, gather_bytes=gb, max_live=ml)
+        for k, v in worst.items():
+            assert v == getattr(want, k), k
+
+
+def test_owner_random_layouts_match_oracle():
+    rnd = random.Random(99)
+    for _ in range(300):
+        world = rnd.randint(1, 40)
+        units = [rnd.randint(1, 10 ** rnd.randint(1, 6)) for _ in range(rnd.randint(1, 20))]
+        ctx, lay = _owner_case(sum(units), world, units)
+        for u in range(len(units)):
+            assert z.zero_unit_owner(ctx, u) == lay.owners[u]
+        r = rnd.randrange(world)
+        got = z.zero_bytes_of_rank(ctx, r, 2, rnd.randint(1, 3))
+        assert got["resident"] == 16 * lay.own_numel(r)
+
+
+def test_owner_argument_errors():
+    ctx, _ = _owner_case(64, 4, [16] * 4)
+    with pytest.raises(z.ZsmrError) as e:     # a null owner copy is refused before launching
+        z.zero_stage3_unit_gather(ctx, 0, [0], 1 << 21, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:     # owner copy and unit buffer overlap
+        z.zero_stage3_unit_gather(ctx, 0, [1 << 20], (1 << 20) + 8, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_unit_owner(ctx, 4)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    split = z.zero_init_shards(64, 4, 3, "bf16", units=[32, 32])
+    with pytest.raises(z.ZsmrError) as e:     # no owners in the split layout
+        z.zero_unit_owner(split, 0)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_bytes_of_rank(ctx, 4)
+    assert e.value.code == z.ZSMR_ERR_ARG
+    ok = 1 << 20                              # a non-owner's fused call is an empty no-op
+    z.zero_fused_step(ctx, 1, 0, ok, 16, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
+    assert z.zero_counters(ctx, 0)["traffic_elems"] == 0
+    assert z.zero_stage3_unit_state(ctx, 0) == (False, 0, 0)

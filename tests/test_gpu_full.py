@@ -288,3 +288,81 @@ def test_fused_ranges_with_ragged_unaligned_cuts():
     assert z.zero_counters(ref.ctx, 63) == z.zero_counters(cut.ctx, 63)
     del ref, cut
     free()
+
+
+# ------------------------------------------------- owner-broadcast ZeRO-3 --
+def _owner_small():
+    units = (300_001, 1 << 17, 250_003, (1 << 17) - 1, 64, 200_000)
+    return wl.Workload("owner_small", "stage3_owner_small_6_units_n5_bf16", sum(units), 5, 3, "bf16",
+                       1e-2, 1e-3, 2, units=units)
+
+
+@pytest.mark.parametrize("prefetch", [False, True])
+def test_owner_broadcast_matches_oracle(prefetch):
+    """Whole units owned by single ranks (odd world, uneven units, so one
+    rank owns nothing and pieces start at any alignment): every element
+    against the oracle's owner-broadcast scheme, every rank's counters against
+    the per-rank accounting, and gathered units against the owners' copies."""
+    import synth
+    from oracle import schemes as sc
+    w = _owner_small()
+    say(f"[owner] small prefetch={prefetch}")
+    s3 = wl.Stage3World(w, check_gathers=True, owner=True, prefetch=prefetch)
+    s3.run(w.steps)
+    torch.cuda.synchronize()
+    assert s3.gather_mismatch == 0
+    p = np.arange(w.numel)
+    theta = synth.theta0(w.seed, p, w.theta_sigma)
+    g = lambda t: [synth.grad16(w.seed, r, t, p, w.grad_sigma, w.dtype) for r in range(w.world)]
+    ref = sc.run(3, w.numel, w.world, theta, g, w.steps, w.dtype, w.lr, units=list(w.units),
+                 owner_broadcast=True)
+    compare({"master": s3.master.cpu().numpy(), "m": s3.m.cpu().numpy(), "v": s3.v.cpu().numpy()},
+            {"master": ref.full_master(), "m": ref.full_m(), "v": ref.full_v()},
+            host16(s3.p16), ref.working_copy(), "owner broadcast small")
+    assert np.array_equal(s3.master.cpu().numpy().view(np.uint32), ref.full_master().view(np.uint32))
+    assert np.array_equal(host16(s3.p16), ref.working_copy())
+    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True)
+    assert [z.zero_unit_owner(s3.ctx, u) for u in range(lay.n_units)] == list(lay.owners)
+    ml = 2 if prefetch else 1
+    for r in range(w.world):
+        c = z.zero_counters(s3.ctx, r)
+        want = acc.bytes_per_rank(lay, max_live=ml, rank=r)
+        assert (c["rs_elems"], c["ag_elems"]) == (w.steps * want.rs_elems, w.steps * want.ag_elems)
+        assert (c["rs_elems"], c["ag_elems"]) == (ref.rs_elems[r], ref.ag_elems[r])
+        assert c["peak_live_bytes"] == want.gathered, r
+        assert c["live_units"] == 0
+    c0 = z.zero_counters(s3.ctx, 0)
+    assert c0["stage3_gathers"] == 2 * lay.n_units * w.steps == c0["stage3_releases"]
+    del s3
+    free()
+
+
+def test_owner_broadcast_llama8b_full_size():
+    """The Llama-3-8B shape with whole units owned by ranks: sampled elements
+    against the oracle, the whole 16-bit copy against the cast of the master,
+    and the counters of every rank."""
+    base = wl.WORKLOADS["llama8b"]
+    w = wl.Workload("llama8b_owner", "llama3_8b_shape_33_units_n8_zero3_owner_bf16", base.numel,
+                    base.world, 3, base.dtype, base.grad_sigma, base.lr, base.steps, units=base.units)
+    say(f"[full] llama8b owner broadcast: units={len(w.units)}")
+    s3 = wl.Stage3World(w, check_gathers=True, owner=True)
+    s3.run(w.steps)
+    torch.cuda.synchronize()
+    assert s3.gather_mismatch == 0
+    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True)
+    marks = []
+    for u in range(lay.n_units):
+        marks += [lay.unit_start[u], lay.unit_start[u] + lay.units[u] - 1]
+    marks += [(1 << 31), (1 << 32), w.numel - 1]
+    pos = windows(marks, 0, w.numel, 1 << 16, seed=9)
+    check_sampled(w, pos, gather_at(s3.master, pos).cpu().numpy(), gather_at(s3.m, pos).cpu().numpy(),
+                  gather_at(s3.v, pos).cpu().numpy(), host16(gather_at(s3.p16, pos)),
+                  "llama8b owner sampled")
+    assert cast_matches(s3.master, s3.p16, w.dtype) == 0
+    for r in range(w.world):
+        c = z.zero_counters(s3.ctx, r)
+        want = acc.bytes_per_rank(lay, rank=r)
+        assert (c["rs_elems"], c["ag_elems"]) == (w.steps * want.rs_elems, w.steps * want.ag_elems)
+        assert c["peak_live_bytes"] == want.gathered
+    del s3
+    free()

@@ -271,10 +271,16 @@ class Stage3World:
     shards are kept in the padded order (unit-major, rank-minor), so shard
     (r, u) sits at Q_u + r*S_u; one unit buffer holds the gathered unit; the
     gradients of one unit (N rows of N*S_u) are generated when the backward
-    pass reaches it."""
+    pass reaches it.
+
+    owner=True: the owner-broadcast layout instead (whole units owned by
+    single ranks, natural order, no pad): unit u sits at its start Q_u, its
+    owner alone initialises and updates it, a gather copies the owner's
+    16-bit copy into the unit buffer, and a unit's gradients are N rows of
+    P_u."""
 
     def __init__(self, w: Workload, device="cuda", check_gathers: bool = False,
-                 prefetch: bool = False, fixed_grads: bool = False):
+                 prefetch: bool = False, fixed_grads: bool = False, owner: bool = False):
         """prefetch: gather the next unit on a second stream while the current
         one is in use (two unit buffers, at most two units live).
         fixed_grads: generate each unit size's gradients once and reuse them
@@ -283,7 +289,9 @@ class Stage3World:
         self.w = w
         self.prefetch = prefetch
         self.fixed_grads = fixed_grads
-        self.ctx = z.zero_init_shards(w.numel, w.world, 3, w.dtype, pad=w.pad,
+        self.owner = owner
+        stage = z.ZSMR_ZERO3_OWNER if owner else 3
+        self.ctx = z.zero_init_shards(w.numel, w.world, stage, w.dtype, pad=w.pad,
                                       units=list(w.units) if w.units else None)
         if prefetch:
             z.zero_stage3_set_max_live(self.ctx, 2)
@@ -291,14 +299,20 @@ class Stage3World:
         self.P = info["padded_numel"]
         self.U = info["n_units"]
         self.maxw = info["max_unit_numel"]
-        self.S_u = [z.zero_layout(self.ctx, 0, u)[1] for u in range(self.U)]
-        self.Q_u = [z.zero_layout(self.ctx, 0, u)[0] for u in range(self.U)]
+        self.P_size = list(w.units or (w.numel,))
         starts, acc = [], 0
-        for n in (w.units or (w.numel,)):
+        for n in self.P_size:
             starts.append(acc)
             acc += n
         self.P_start = starts
-        self.P_size = list(w.units or (w.numel,))
+        if owner:
+            self.owner_of = [z.zero_unit_owner(self.ctx, u) for u in range(self.U)]
+            self.Q_u = list(starts)
+            self.width = list(self.P_size)              # a unit's gradient row
+        else:
+            self.S_u = [z.zero_layout(self.ctx, 0, u)[1] for u in range(self.U)]
+            self.Q_u = [z.zero_layout(self.ctx, 0, u)[0] for u in range(self.U)]
+            self.width = [w.world * s for s in self.S_u]
         self.master = torch.empty(self.P, dtype=torch.float32, device=device)
         self.m = torch.empty_like(self.master)
         self.v = torch.empty_like(self.master)
@@ -312,7 +326,7 @@ class Stage3World:
             # one gradient set per distinct unit width, made once (step 1)
             self.grads_by_width = {}
             for u in range(self.U):
-                width = w.world * self.S_u[u]
+                width = self.width[u]
                 if width not in self.grads_by_width:
                     g = empty16(w.world * width, w.dtype, device)
                     sgpu.fill16(g, w.world, width, width, self.P_start[u], self.P_size[u], w.seed,
@@ -322,43 +336,48 @@ class Stage3World:
             self.grads = empty16(w.world * self.maxw, w.dtype, device)
         theta = torch.empty(self.maxw, dtype=torch.float32, device=device)
         for u in range(self.U):
-            width = w.world * self.S_u[u]
-            sgpu.fill32(theta, width, self.P_start[u], self.P_size[u], w.seed, synth.TAG_THETA, 0, 0,
-                        w.theta_sigma)
-            for r in range(w.world):
-                o = self.Q_u[u] + r * self.S_u[u]
-                z.zero_init_state(self.ctx, r, u, theta[r * self.S_u[u]:], self.master[o:],
+            sgpu.fill32(theta, self.width[u], self.P_start[u], self.P_size[u], w.seed, synth.TAG_THETA,
+                        0, 0, w.theta_sigma)
+            for r, o, n in self._pieces(u):
+                z.zero_init_state(self.ctx, r, u, theta[o - self.Q_u[u]:], self.master[o:],
                                   self.m[o:], self.v[o:], self.p16[o:])
         del theta
 
+    def _pieces(self, u: int):
+        """(rank, padded offset, length) of every non-empty piece of unit u."""
+        if self.owner:
+            return [(self.owner_of[u], self.Q_u[u], self.P_size[u])]
+        return [(r, self.Q_u[u] + r * self.S_u[u], self.S_u[u]) for r in range(self.w.world)]
+
     def _gather(self, u: int, buf=None):
         buf = self.unit_buf if buf is None else buf
-        shards = [self.p16[self.Q_u[u] + r * self.S_u[u]:] for r in range(self.w.world)]
+        if self.owner:
+            shards = [self.p16[self.Q_u[u]:]]
+        else:
+            shards = [self.p16[self.Q_u[u] + r * self.S_u[u]:] for r in range(self.w.world)]
         z.zero_stage3_unit_gather(self.ctx, u, shards, buf)
         if self.check_gathers:
-            width = self.w.world * self.S_u[u]
+            width = self.width[u]
             same = torch.equal(buf[:width].view(torch.int16),
                                self.p16[self.Q_u[u]:self.Q_u[u] + width].view(torch.int16))
             self.gather_mismatch += 0 if same else 1
 
     def gen_grads(self, u: int, step: int):
         w = self.w
-        width = w.world * self.S_u[u]
+        width = self.width[u]
         sgpu.fill16(self.grads, w.world, width, width, self.P_start[u], self.P_size[u], w.seed,
                     synth.TAG_GRAD, 0, step, w.grad_sigma, w.dtype, w.outlier_permyriad)
 
     def _grads_for(self, u: int, t: int):
         if self.fixed_grads:
-            return self.grads_by_width[self.w.world * self.S_u[u]]
+            return self.grads_by_width[self.width[u]]
         self.gen_grads(u, t)                          # the unit's gradients appear
         return self.grads
 
     def _update(self, u: int, t: int, grads):
         w = self.w
-        width = w.world * self.S_u[u]
-        for r in range(w.world):
-            o = self.Q_u[u] + r * self.S_u[u]
-            z.zero_fused_step(self.ctx, r, u, grads, width, r * self.S_u[u], self.master[o:],
+        for r, o, n in self._pieces(u):
+            z.zero_fused_step(self.ctx, r, u, grads, self.width[u], o - self.Q_u[u], self.master[o:],
                               self.m[o:], self.v[o:], self.p16[o:], t, w.lr, w.betas, w.eps)
 
     def step(self, t: int, timer: Optional[Timer] = None):

@@ -19,6 +19,7 @@ ZSMR_OK, ZSMR_ERR_ARG, ZSMR_ERR_INDIVISIBLE, ZSMR_ERR_STATE = 0, 1, 2, 3
 ZSMR_ERR_DTYPE, ZSMR_ERR_ALIGN, ZSMR_ERR_HIP = 4, 5, 6
 ZSMR_FP16, ZSMR_BF16 = 1, 2
 ZSMR_DP, ZSMR_ZERO1, ZSMR_ZERO2, ZSMR_ZERO3 = 0, 1, 2, 3
+ZSMR_ZERO3_OWNER = 4           # stage 3 with whole units owned by single ranks (owner broadcast)
 DTYPES = {"fp16": ZSMR_FP16, "bf16": ZSMR_BF16}
 
 _i32, _i64, _vp, _f32p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
@@ -67,6 +68,8 @@ SIGNATURES = {
     "zero_layout": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                            ctypes.POINTER(_i64)]),
     "zero_bytes_per_rank": (_i32, [_vp, _i32, _i32, ctypes.POINTER(zsmr_bytes)]),
+    "zero_bytes_of_rank": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(zsmr_bytes)]),
+    "zero_unit_owner": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
     "zero_counters": (_i32, [_vp, _i32, ctypes.POINTER(zsmr_counters)]),
     "zero_reset_counters": (_i32, [_vp]),
     "zero_init_state": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -202,6 +205,19 @@ def zero_bytes_per_rank(ctx: Ctx, gather_bytes: int = 0, max_live: int = 0) -> d
     _check(_lib().zero_bytes_per_rank(ctx.handle, gather_bytes, max_live, ctypes.byref(out)),
            "zero_bytes_per_rank")
     return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def zero_bytes_of_rank(ctx: Ctx, rank: int, gather_bytes: int = 0, max_live: int = 0) -> dict:
+    out = zsmr_bytes()
+    _check(_lib().zero_bytes_of_rank(ctx.handle, rank, gather_bytes, max_live, ctypes.byref(out)),
+           "zero_bytes_of_rank")
+    return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def zero_unit_owner(ctx: Ctx, unit: int) -> int:
+    o = _i32()
+    _check(_lib().zero_unit_owner(ctx.handle, unit, ctypes.byref(o)), "zero_unit_owner")
+    return o.value
 
 
 def zero_counters(ctx: Ctx, rank: int) -> dict:

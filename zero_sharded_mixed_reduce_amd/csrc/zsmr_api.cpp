@@ -18,17 +18,21 @@ struct zsmr_ctx {
     int64_t numel = 0;
     int32_t world = 0, stage = 0, gdt = 0, pdt = 0, pad = 0;
     std::vector<int64_t> units;        // true unit sizes
-    std::vector<int64_t> shard_u;      // S_u (stage 3); {S} stages 1-2; {Psi} DP
-    std::vector<int64_t> unit_pstart;  // padded start Q_u (stage 3); {0} otherwise
-    std::vector<int64_t> local_off;    // offset of unit u's piece in a rank's shard
+    std::vector<int64_t> shard_u;      // S_u (stage 3); {S} stages 1-2; {Psi} DP; P_u (stage 4)
+    std::vector<int64_t> unit_pstart;  // padded start Q_u (stage 3); unit start (stage 4); {0} otherwise
+    std::vector<int64_t> local_off;    // offset of unit u's piece in its holder's shard
+    std::vector<int32_t> owners;       // stage 4: the rank owning each unit
+    std::vector<int64_t> own;          // stage 4: elements each rank owns
     int64_t padded = 0, shard_total = 0;
-    // counters: elements received per rank
+    // counters per rank (elements): all-gathers received; reduce-scatters
+    // received = sent at stages 1-3, sent at stage 4; all-reduce
     std::vector<int64_t> rs, ag, ar;
-    // ZeRO-3 schedule
+    // ZeRO-3 schedule (live and peak gathered bytes per rank: at stage 4 a
+    // rank needs no buffer for its own units)
     std::vector<int64_t> gathers, releases;
     std::vector<char> live;
     int32_t max_live = 1, live_units = 0;
-    int64_t live_bytes = 0, peak_live_bytes = 0;
+    std::vector<int64_t> live_bytes, peak_live_bytes;
 };
 
 namespace {
@@ -44,7 +48,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool dtype_ok(int32_t d) { return d == ZSMR_FP16 || d == ZSMR_BF16; }
 
-int n_pieces(const zsmr_ctx* c) { return c->stage == ZSMR_ZERO3 ? (int)c->units.size() : 1; }
+bool stage3(const zsmr_ctx* c) { return c->stage == ZSMR_ZERO3 || c->stage == ZSMR_ZERO3_OWNER; }
+
+int n_pieces(const zsmr_ctx* c) { return stage3(c) ? (int)c->units.size() : 1; }
 
 int32_t check_piece(const zsmr_ctx* c, int32_t rank, int32_t unit) {
     if (!c) return ZSMR_ERR_ARG;
@@ -59,6 +65,10 @@ void piece(const zsmr_ctx* c, int32_t rank, int32_t unit, int64_t* off, int64_t*
         o = 0;
         l = c->numel;
         lo = 0;
+    } else if (c->stage == ZSMR_ZERO3_OWNER) {
+        o = c->unit_pstart[unit];
+        l = c->owners[unit] == rank ? c->units[unit] : 0;
+        lo = c->local_off[unit];
     } else if (c->stage != ZSMR_ZERO3) {
         l = c->shard_u[0];
         o = (int64_t)rank * l;
@@ -96,13 +106,26 @@ int32_t check_adam(const zsmr_adam* hp, int32_t t, zsmr::AdamK* k) {
 
 // Counting of one reduce over (rank, unit) of `len` elements: a data-parallel
 // replica takes part in one all-reduce of the whole vector; a sharded rank
-// receives (N-1) peers' contributions to its piece.
+// receives (N-1) peers' contributions to its piece (and sends as many); at
+// stage 4 every other rank sends its contribution to the owner.
 void count_reduce(zsmr_ctx* c, int32_t rank, int64_t len) {
     const int64_t w = c->world;
-    if (c->stage == ZSMR_DP)
+    if (c->stage == ZSMR_DP) {
         c->ar[rank] += 2 * (w - 1) * ceil_div(c->numel, w);
-    else
+    } else if (c->stage == ZSMR_ZERO3_OWNER) {
+        for (int32_t q = 0; q < c->world; ++q)
+            if (q != rank) c->rs[q] += len;
+    } else {
         c->rs[rank] += (w - 1) * len;
+    }
+}
+
+// Stage 4: the owner of each unit is the rank whose equal share of the vector
+// holds the unit's midpoint, floor(N * (2 * start + size) / (2 * Psi)).
+int32_t midpoint_owner(int64_t start, int64_t size, int64_t numel, int32_t world) {
+    const __int128 num = (__int128)world * (2 * (__int128)start + size);
+    const int64_t r = (int64_t)(num / (2 * (__int128)numel));
+    return r < world - 1 ? (int32_t)r : world - 1;
 }
 
 // Counting of one cast of (rank, unit): at stages 1-2 the all-gather delivers
@@ -137,7 +160,8 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
                          const int64_t* unit_numel, int32_t n_units) {
     if (!out) return ZSMR_ERR_ARG;
     *out = nullptr;
-    if (numel < 1 || world < 1 || stage < ZSMR_DP || stage > ZSMR_ZERO3 || (pad != 0 && pad != 1))
+    if (numel < 1 || world < 1 || stage < ZSMR_DP || stage > ZSMR_ZERO3_OWNER ||
+        (pad != 0 && pad != 1))
         return ZSMR_ERR_ARG;
     if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZSMR_ERR_DTYPE;
     if (n_units < 0 || (n_units > 0 && !unit_numel) || (n_units == 0 && unit_numel))
@@ -169,6 +193,21 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
         c->local_off = {0};
         c->padded = numel;
         c->shard_total = numel;
+    } else if (stage == ZSMR_ZERO3_OWNER) {
+        // whole units, natural order, no padding
+        int64_t start = 0;
+        c->own.assign(world, 0);
+        for (int64_t u : units) {
+            const int32_t o = midpoint_owner(start, u, numel, world);
+            c->shard_u.push_back(u);
+            c->unit_pstart.push_back(start);
+            c->local_off.push_back(c->own[o]);
+            c->owners.push_back(o);
+            c->own[o] += u;
+            start += u;
+        }
+        c->padded = numel;
+        c->shard_total = *std::max_element(c->own.begin(), c->own.end());
     } else if (stage != ZSMR_ZERO3) {
         if (numel % world && !pad) {
             delete c;
@@ -203,6 +242,8 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
     c->gathers.assign(units.size(), 0);
     c->releases.assign(units.size(), 0);
     c->live.assign(units.size(), 0);
+    c->live_bytes.assign(world, 0);
+    c->peak_live_bytes.assign(world, 0);
     *out = c;
     return ZSMR_OK;
 }
@@ -217,6 +258,8 @@ int32_t zero_layout_info(const zsmr_ctx* c, zsmr_layout_info* out) {
     int64_t mx = 0;
     if (c->stage == ZSMR_ZERO3) {
         for (int64_t s : c->shard_u) mx = s * c->world > mx ? s * c->world : mx;
+    } else if (c->stage == ZSMR_ZERO3_OWNER) {
+        for (int64_t u : c->units) mx = u > mx ? u : mx;
     } else {
         mx = c->padded;
     }
@@ -238,11 +281,42 @@ int32_t zero_layout(const zsmr_ctx* c, int32_t rank, int32_t unit, int64_t* offs
     return ZSMR_OK;
 }
 
-int32_t zero_bytes_per_rank(const zsmr_ctx* c, int32_t gather_bytes, int32_t max_live,
-                            zsmr_bytes* o) {
-    if (!c || !o || gather_bytes < 0 || max_live < 0) return ZSMR_ERR_ARG;
-    if (gather_bytes == 0) gather_bytes = 2;
-    if (max_live == 0) max_live = 1;
+namespace {
+
+// Stage 4, one rank: its own units' 16 bytes per element; it receives each
+// weight it does not own twice and sends each of those gradients once; its
+// peak adds the borrowed units live at once ("One Poem Suffices: ZeRO"
+// section 4.1.4; "ZeRO, annotated" section 7).
+void owner_bytes(const zsmr_ctx* c, int32_t rank, int64_t gather_bytes, int64_t max_live,
+                 zsmr_bytes* o) {
+    const int64_t own = c->own[rank];
+    std::memset(o, 0, sizeof(*o));
+    o->res_p16 = 2 * own;
+    o->res_grad = 2 * own;
+    o->res_master = 4 * own;
+    o->res_m = 4 * own;
+    o->res_v = 4 * own;
+    o->resident = 16 * own;
+    const int64_t nu = (int64_t)c->units.size();
+    const int64_t k = max_live < nu ? max_live : nu;
+    int64_t best = 0, widest = 0;
+    for (int64_t i = 0; i + k <= nu; ++i) {
+        int64_t sum = 0;
+        for (int64_t j = i; j < i + k; ++j) sum += c->owners[j] == rank ? 0 : c->units[j];
+        best = sum > best ? sum : best;
+    }
+    for (int64_t u : c->units) widest = u > widest ? u : widest;
+    o->gathered = gather_bytes * best;
+    o->unit_grad = 2 * widest;
+    o->peak = o->resident + o->gathered;
+    o->rs_elems = c->numel - own;
+    o->ag_elems = 2 * (c->numel - own);
+    o->traffic_elems = o->rs_elems + o->ag_elems;
+    o->traffic_bytes = 2 * o->traffic_elems;
+}
+
+// Stages 0-3: every rank holds the same.
+void even_bytes(const zsmr_ctx* c, int64_t gather_bytes, int64_t max_live, zsmr_bytes* o) {
     const int64_t n = c->numel, w = c->world;
     const bool shard_opt = c->stage >= ZSMR_ZERO1, shard_grad = c->stage >= ZSMR_ZERO2,
                shard_param = c->stage >= ZSMR_ZERO3;
@@ -282,6 +356,34 @@ int32_t zero_bytes_per_rank(const zsmr_ctx* c, int32_t gather_bytes, int32_t max
     }
     o->traffic_elems = o->rs_elems + o->ag_elems + o->ar_elems;
     o->traffic_bytes = 2 * o->traffic_elems;
+}
+
+}  // namespace
+
+int32_t zero_bytes_of_rank(const zsmr_ctx* c, int32_t rank, int32_t gather_bytes,
+                           int32_t max_live, zsmr_bytes* o) {
+    if (!c || !o || rank < 0 || rank >= c->world || gather_bytes < 0 || max_live < 0)
+        return ZSMR_ERR_ARG;
+    if (gather_bytes == 0) gather_bytes = 2;
+    if (max_live == 0) max_live = 1;
+    if (c->stage == ZSMR_ZERO3_OWNER)
+        owner_bytes(c, rank, gather_bytes, max_live, o);
+    else
+        even_bytes(c, gather_bytes, max_live, o);
+    return ZSMR_OK;
+}
+
+int32_t zero_bytes_per_rank(const zsmr_ctx* c, int32_t gather_bytes, int32_t max_live,
+                            zsmr_bytes* o) {
+    if (!c || !o || gather_bytes < 0 || max_live < 0) return ZSMR_ERR_ARG;
+    if (c->stage != ZSMR_ZERO3_OWNER) return zero_bytes_of_rank(c, 0, gather_bytes, max_live, o);
+    // stage 4: the rank with the largest peak (the lowest such rank)
+    zsmr_bytes best{}, cur{};
+    for (int32_t r = 0; r < c->world; ++r) {
+        zero_bytes_of_rank(c, r, gather_bytes, max_live, &cur);
+        if (r == 0 || cur.peak > best.peak) best = cur;
+    }
+    *o = best;
     return ZSMR_OK;
 }
 
@@ -298,8 +400,8 @@ int32_t zero_counters(const zsmr_ctx* c, int32_t rank, zsmr_counters* o) {
         o->stage3_releases += c->releases[u];
     }
     o->live_units = c->live_units;
-    o->live_bytes = c->live_bytes;
-    o->peak_live_bytes = c->peak_live_bytes;
+    o->live_bytes = c->live_bytes[rank];
+    o->peak_live_bytes = c->peak_live_bytes[rank];
     return ZSMR_OK;
 }
 
@@ -483,7 +585,7 @@ int32_t zero_gather_copy(zsmr_ctx* c, int32_t recv_rank, const void* src, void* 
 }
 
 int32_t zero_stage3_set_max_live(zsmr_ctx* c, int32_t max_live) {
-    if (!c || c->stage != ZSMR_ZERO3 || max_live < 1) return ZSMR_ERR_ARG;
+    if (!c || !stage3(c) || max_live < 1) return ZSMR_ERR_ARG;
     if (c->live_units) return ZSMR_ERR_STATE;
     c->max_live = max_live;
     return ZSMR_OK;
@@ -491,46 +593,67 @@ int32_t zero_stage3_set_max_live(zsmr_ctx* c, int32_t max_live) {
 
 int32_t zero_stage3_unit_gather(zsmr_ctx* c, int32_t unit, const void* const* shard_ptrs,
                                 void* unit_buf, hipStream_t stream) {
-    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
-        return ZSMR_ERR_ARG;
+    if (!c || !stage3(c) || unit < 0 || unit >= (int32_t)c->units.size()) return ZSMR_ERR_ARG;
     if (!shard_ptrs || !unit_buf) return ZSMR_ERR_ARG;
-    for (int32_t r = 0; r < c->world; ++r)
+    const bool owner = c->stage == ZSMR_ZERO3_OWNER;
+    const int32_t nsrc = owner ? 1 : c->world;      // stage 4: the owner's copy only
+    for (int32_t r = 0; r < nsrc; ++r)
         if (!shard_ptrs[r]) return ZSMR_ERR_ARG;
-    for (int32_t r = 0; r < c->world; ++r)
+    for (int32_t r = 0; r < nsrc; ++r)
         if (!al(shard_ptrs[r], 2)) return ZSMR_ERR_ALIGN;
     if (!al(unit_buf, 2)) return ZSMR_ERR_ALIGN;
     if (c->live[unit] || c->live_units >= c->max_live) return ZSMR_ERR_STATE;
-    const int64_t su = c->shard_u[unit];
+    const int64_t each = owner ? c->units[unit] : c->shard_u[unit];
+    if (owner) {
+        const uint16_t* src = static_cast<const uint16_t*>(shard_ptrs[0]);
+        uint16_t* dst = static_cast<uint16_t*>(unit_buf);
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+        const uintptr_t bytes = static_cast<uintptr_t>(each) * 2;
+        if (s0 < d0 + bytes && d0 < s0 + bytes) return ZSMR_ERR_ARG;
+    }
     const hipError_t e = zsmr::launch_gather16(reinterpret_cast<const uint16_t* const*>(shard_ptrs),
-                                               c->world, su, static_cast<uint16_t*>(unit_buf), stream);
+                                               nsrc, each, static_cast<uint16_t*>(unit_buf), stream);
     if (e != hipSuccess) return hip_fail(e);
     c->live[unit] = 1;
     c->live_units += 1;
     c->gathers[unit] += 1;
-    for (int32_t r = 0; r < c->world; ++r) c->ag[r] += (int64_t)(c->world - 1) * su;
-    c->live_bytes += 2 * (int64_t)c->world * su;
-    if (c->live_bytes > c->peak_live_bytes) c->peak_live_bytes = c->live_bytes;
+    for (int32_t r = 0; r < c->world; ++r) {
+        if (owner && r == c->owners[unit]) continue;       // the owner holds it already
+        c->ag[r] += owner ? each : (int64_t)(c->world - 1) * each;
+        c->live_bytes[r] += owner ? 2 * each : 2 * (int64_t)c->world * each;
+        if (c->live_bytes[r] > c->peak_live_bytes[r]) c->peak_live_bytes[r] = c->live_bytes[r];
+    }
     return ZSMR_OK;
 }
 
 int32_t zero_stage3_unit_release(zsmr_ctx* c, int32_t unit) {
-    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
-        return ZSMR_ERR_ARG;
+    if (!c || !stage3(c) || unit < 0 || unit >= (int32_t)c->units.size()) return ZSMR_ERR_ARG;
     if (!c->live[unit]) return ZSMR_ERR_STATE;
+    const bool owner = c->stage == ZSMR_ZERO3_OWNER;
     c->live[unit] = 0;
     c->live_units -= 1;
     c->releases[unit] += 1;
-    c->live_bytes -= 2 * (int64_t)c->world * c->shard_u[unit];
+    for (int32_t r = 0; r < c->world; ++r) {
+        if (owner && r == c->owners[unit]) continue;
+        c->live_bytes[r] -= owner ? 2 * c->units[unit] : 2 * (int64_t)c->world * c->shard_u[unit];
+    }
     return ZSMR_OK;
 }
 
 int32_t zero_stage3_unit_state(const zsmr_ctx* c, int32_t unit, int32_t* live, int64_t* gathers,
                                int64_t* releases) {
-    if (!c || c->stage != ZSMR_ZERO3 || unit < 0 || unit >= (int32_t)c->units.size())
-        return ZSMR_ERR_ARG;
+    if (!c || !stage3(c) || unit < 0 || unit >= (int32_t)c->units.size()) return ZSMR_ERR_ARG;
     if (live) *live = c->live[unit];
     if (gathers) *gathers = c->gathers[unit];
     if (releases) *releases = c->releases[unit];
+    return ZSMR_OK;
+}
+
+int32_t zero_unit_owner(const zsmr_ctx* c, int32_t unit, int32_t* owner) {
+    if (!c || !owner || c->stage != ZSMR_ZERO3_OWNER || unit < 0 ||
+        unit >= (int32_t)c->units.size())
+        return ZSMR_ERR_ARG;
+    *owner = c->owners[unit];
     return ZSMR_OK;
 }
 
