@@ -465,18 +465,23 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 // tiles' gradient rows as one double-buffered sequence of row batches, across
 // tile boundaries; a tile whose rows straddle a window keeps its partial sum
 // in registers.  Wave w owns tiles w, w + W, w + 2W, ... (W waves in the
-// grid).  Each lane reads back only what it wrote, so the waves never
-// synchronise.  Results are the same bits as step_vec8_kernel's: only the
-// time at which they are stored changes.  Any number of rows; a row stride
-// of fewer than 2^63 bytes.
+// grid).  While computing, lane l holds the tile's 8 consecutive elements
+// [8l, 8l+8): one 16-byte load per gradient row.  The ring keeps each tile in
+// element order, and the flush reads it back in the store map (lane l:
+// [4l, 4l+4) and [256+4l, 256+4l+4)), so that every store instruction covers
+// one contiguous run; the ring is a wave's own, and a wave's LDS operations
+// complete in order, so waves never synchronise.  Results are the same bits
+// as step_vec8_kernel's: only the time at which they are stored changes.
+// Any number of rows; rows 16-byte aligned (the host checks); a row stride of
+// fewer than 2^63 bytes.
 template <int GDT, int PDT, int DV, int KD>
 __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, Window win) {
     static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
     constexpr int kWaves = kThreads / 64;
-    __shared__ float s_w[kWaves][KD][8][64];
-    __shared__ float s_m[kWaves][KD][8][64];
-    __shared__ float s_v[kWaves][KD][8][64];
-    __shared__ uint32_t s_h[kWaves][KD][4][64];
+    __shared__ float s_w[kWaves][KD][512];      // a tile's results in element order
+    __shared__ float s_m[kWaves][KD][512];
+    __shared__ float s_v[kWaves][KD][512];
+    __shared__ uint32_t s_h[kWaves][KD][256];   // 16-bit copy, two elements per word
     const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
     const uint32_t tiles = static_cast<uint32_t>(vec_elems(a.n) / 512);
     const uint32_t nw = gridDim.x * kWaves;
@@ -484,25 +489,32 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
     const uint32_t mine = wid < tiles ? (tiles - 1 - wid) / nw + 1 : 0;
     const uint32_t bps = (static_cast<uint32_t>(a.nrows) + kRowBatch - 1) / kRowBatch;
     const uint32_t nb = mine * bps;
-    auto e0_of = [&](uint32_t j) { return (wid + j * nw) * 512u + lane * 4u; };
+    auto tile_of = [&](uint32_t j) { return (wid + j * nw) * 512u; };
 
     // the ring: tiles [flushed, done) of this wave are in LDS, not yet stored
     uint32_t done = 0, flushed = 0;
     auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");   // the ring holds other lanes' values
         for (uint32_t j = flushed; j < done; ++j) {
-            const uint32_t k = j % KD, e0 = e0_of(j);
+            const uint32_t k = j % KD, e0 = tile_of(j) + lane * 4u;
             float w[8], m[8], v[8];
             uint32_t h[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                w[q] = s_w[wv][k][q][lane];
-                m[q] = s_m[wv][k][q][lane];
-                v[q] = s_v[wv][k][q][lane];
+            for (int q = 0; q < 4; ++q) {
+                w[q] = s_w[wv][k][lane * 4u + q];
+                w[4 + q] = s_w[wv][k][256u + lane * 4u + q];
+                m[q] = s_m[wv][k][lane * 4u + q];
+                m[4 + q] = s_m[wv][k][256u + lane * 4u + q];
+                v[q] = s_v[wv][k][lane * 4u + q];
+                v[4 + q] = s_v[wv][k][256u + lane * 4u + q];
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                h[2 * q] = s_h[wv][k][q][lane] & 0xffffu;
-                h[2 * q + 1] = s_h[wv][k][q][lane] >> 16;
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t lo = s_h[wv][k][lane * 2u + q], hi = s_h[wv][k][128u + lane * 2u + q];
+                h[2 * q] = lo & 0xffffu;
+                h[2 * q + 1] = lo >> 16;
+                h[4 + 2 * q] = hi & 0xffffu;
+                h[4 + 2 * q + 1] = hi >> 16;
             }
             Groups<true>::store32(a.master, e0, e0 + 256u, w);
             Groups<true>::store32(a.m, e0, e0 + 256u, m);
@@ -567,22 +579,17 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
     State stA, stB;
     float g[8];
     auto issue = [&](u32x4* buf, State& st) {
-        const uint32_t e0 = e0_of(i_tile), off = e0 * 2u;
+        const uint32_t e0 = tile_of(i_tile) + lane * 8u, off = e0 * 2u;
 #pragma unroll
         for (int k = 0; k < kRowBatch; ++k) {
-            const u32x2 lo = ld(reinterpret_cast<const u32x2*>(i_ptr + off));
-            const u32x2 hi = ld(reinterpret_cast<const u32x2*>(i_ptr + off + 512u));
-            buf[k][0] = lo[0];
-            buf[k][1] = lo[1];
-            buf[k][2] = hi[0];
-            buf[k][3] = hi[1];
+            buf[k] = ld(reinterpret_cast<const u32x4*>(i_ptr + off));
             if (i_row + k + 1 < nrows) i_ptr += stride_b;
         }
         i_row += kRowBatch;
         if (i_row >= nrows) {      // the tile's last batch: its master/m/v come with it
-            Groups<true>::load32(a.master, e0, e0 + 256u, st.w);
-            Groups<true>::load32(a.m, e0, e0 + 256u, st.m);
-            Groups<true>::load32(a.v, e0, e0 + 256u, st.v);
+            Groups<false>::load32(a.master, e0, e0 + 4u, st.w);
+            Groups<false>::load32(a.m, e0, e0 + 4u, st.m);
+            Groups<false>::load32(a.v, e0, e0 + 4u, st.v);
             ++i_tile;
             i_row = 0;
             i_ptr = grads;
@@ -619,13 +626,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, 
         const uint32_t k = done % KD;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            s_w[wv][k][e][lane] = st.w[e];
-            s_m[wv][k][e][lane] = st.m[e];
-            s_v[wv][k][e][lane] = st.v[e];
+            s_w[wv][k][lane * 8u + e] = st.w[e];
+            s_m[wv][k][lane * 8u + e] = st.m[e];
+            s_v[wv][k][lane * 8u + e] = st.v[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            s_h[wv][k][e][lane] = narrow<PDT>(st.w[2 * e]) | (narrow<PDT>(st.w[2 * e + 1]) << 16);
+            s_h[wv][k][lane * 4u + e] = narrow<PDT>(st.w[2 * e]) | (narrow<PDT>(st.w[2 * e + 1]) << 16);
         ++done;
     };
 
@@ -840,7 +847,8 @@ hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
     if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST) && kSplit) {
-        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows) {
+        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows && al(a.grads, 16) &&
+            a.row_stride % 8 == 0) {
             switch (dv) {
                 case 8:
                 case 4: return launch_deferred<GDT, PDT, 4>(a, s);
