@@ -279,7 +279,7 @@ def main():
     ap.add_argument("--workload", default="share64")
     ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
     ap.add_argument("--copy-bpc", type=int, default=1, help="workgroups per CU, 16-byte copies")
-    ap.add_argument("--defer-tiles", type=int, default=5, help="fused-step tiles kept in LDS (0-5)")
+    ap.add_argument("--defer-tiles", type=int, default=2, help="fused-step tiles kept in LDS per wave (0-5)")
     ap.add_argument("--defer-min-rows", type=int, default=16,
                     help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--window-cycle-ns", type=int, default=None,

@@ -68,10 +68,13 @@ int g_step_bpc = 2;
 int g_copy_bpc = 1;
 constexpr int kNarrowCopyBpc = 4;
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
-// write windows (0 = write at once with step_vec8_kernel), and workgroups
-// per CU
-int g_defer_tiles = 5;
-int g_defer_bpc = 1;
+// write windows (0 = write at once with step_vec8_kernel).  With windows and
+// a ring of at most 2 tiles, two workgroups run per CU (2 x 56 KB of LDS,
+// two waves per SIMD): more loads in flight while the other wave runs its
+// Adam tail.  Measured on MI355X, share64: 2 tiles x 2 workgroups 2.86-2.90
+// ms per step against 3.07 ms for 5 tiles x 1; without windows one
+// workgroup per CU is 5% faster (16-24 rows).
+int g_defer_tiles = 2;
 // ... used when a step reduces at least this many rows.  Measured on MI355X
 // against the direct kernel: single long launches at 16 rows +7%, 24 rows
 // +8.5%, 64 rows +22% (with windows); the 1.558e9-element, 16-rank world
@@ -82,16 +85,18 @@ int g_defer_min_rows = 16;
 // ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
 constexpr int kRingWithoutWindows = 2;
 // its write windows, in ns (0: none); converted to clock ticks per device
-// (measured on MI355X over cycles of 35-65 us: 40 / 5 / 1 / 1 us is on the
-// flat top of the curve, and leaves room in the ring of 5 tiles per wave).
+// (measured on MI355X, share64, 2 tiles x 2 workgroups per CU: 50 / 8 / 1 /
+// 2 us gave 2.853-2.868 ms per step; the read phase, 42 us, is about the time
+// two waves per SIMD take to fill their 2-tile rings, so a longer cycle idles
+// until its window: 60 us cost 17%).
 // Windows pay from 32 rows on; with fewer a tile is read so fast that the
 // ring fills long before a window (at 16 rows the windowed kernel ran 4%
 // slower than with stores at ring-full, which beat the direct kernel by 2%).
 constexpr int kWindowMinRows = 32;
-int64_t g_window_cycle_ns = 40000;
-int64_t g_window_write_ns = 5000;
+int64_t g_window_cycle_ns = 50000;
+int64_t g_window_write_ns = 8000;
 int64_t g_window_margin_ns = 1000;
-int64_t g_window_lead_ns = 1000;
+int64_t g_window_lead_ns = 2000;
 
 // Streamed data is touched once per step: non-temporal loads and stores keep
 // it from displacing anything useful in L2 and the MALL.
@@ -475,7 +480,7 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 // Any number of rows; rows 16-byte aligned (the host checks); a row stride of
 // fewer than 2^63 bytes.
 template <int GDT, int PDT, int DV, int KD>
-__global__ __launch_bounds__(kThreads, 1) void step_deferred_kernel(StepArgs a, Window win) {
+__global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, Window win) {
     static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
     constexpr int kWaves = kThreads / 64;
     __shared__ float s_w[kWaves][KD][512];      // a tile's results in element order
@@ -831,9 +836,10 @@ Window window_ticks() {
 
 template <int GDT, int PDT, int DV>
 hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
-    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_defer_bpc));   // one wave per tile at most
     const Window w = a.nrows >= kWindowMinRows ? window_ticks() : Window{0, 0, 0, 0};
     const int kd = w.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
+    const int bpc = w.cycle && kd <= 2 ? 2 : 1;
+    const dim3 grid(grid_for(vec_elems(a.n) >> 3, bpc));   // one wave per tile at most
     switch (kd) {
         case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a, w); break;
         case 2: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 2>), grid, dim3(kThreads), 0, s, a, w); break;
