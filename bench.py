@@ -105,6 +105,37 @@ def warm(step, warmup: int, min_seconds: float = 1.0) -> None:
         torch.cuda.synchronize()
 
 
+def tune_write_window(share, reps: int = 6) -> dict:
+    """Pick the fused step's write-window cycle for this device.  The best
+    cycle is the time the waves' LDS rings take to fill, which follows the
+    device's read rate; a few candidates around the library default are
+    timed (untimed for the result: these are extra warm-up steps) and the
+    fastest is kept.  The window changes only when results are stored."""
+    import torch
+    import zero_sharded_mixed_reduce_amd as z
+    c0, w0, margin, lead = z.WRITE_WINDOW_DEFAULT
+    cands = [(c0 + dc, w0 + dw, margin, lead) for dc in (-8000, -4000, 0, 4000, 8000)
+             for dw in (-2000, 0)]
+    stream = torch.cuda.current_stream()
+    best = None
+    for cfg in cands:
+        z.zsmr_set_write_window(*cfg)
+        share.fused(1000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            share.fused(1000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        if best is None or ms < best[0]:
+            best = (ms, cfg)
+    z.zsmr_set_write_window(*best[1])
+    return {"cycle": best[1][0], "write": best[1][1], "margin": best[1][2], "lead": best[1][3],
+            "tuned_over": len(cands)}
+
+
 def copy_reference(z, nbytes: int, reps: int = 5) -> float:
     """GB/s (read + write) of the library's 128-bit copy between two fresh,
     equally aligned buffers of ``nbytes``, measured in the same process: the
@@ -176,6 +207,10 @@ def bench_share64(args, w):
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     warm(lambda t: share.step(t), args.warmup)
+    window = {"cycle": args.window_cycle_ns, "write": args.window_write_ns,
+              "margin": args.window_margin_ns, "lead": args.window_lead_ns, "tuned_over": 0}
+    if not args.window_explicit:
+        window = tune_write_window(share)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -224,8 +259,7 @@ def bench_share64(args, w):
         "rank": 0, "step_workgroups_per_cu": args.step_bpc,
         "copy_workgroups_per_cu": args.copy_bpc, "fused_defer_tiles": args.defer_tiles,
         "fused_defer_min_rows": args.defer_min_rows,
-        "fused_write_window_ns": {"cycle": args.window_cycle_ns, "write": args.window_write_ns,
-                                  "margin": args.window_margin_ns, "lead": args.window_lead_ns}}
+        "fused_write_window_ns": window}
 
 
 def bench_world(args, w):
@@ -279,7 +313,7 @@ def main():
     ap.add_argument("--workload", default="share64")
     ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
     ap.add_argument("--copy-bpc", type=int, default=1, help="workgroups per CU, 16-byte copies")
-    ap.add_argument("--defer-tiles", type=int, default=2, help="fused-step tiles kept in LDS per wave (0-5)")
+    ap.add_argument("--defer-tiles", type=int, default=3, help="fused-step tiles kept in LDS per wave (0-5)")
     ap.add_argument("--defer-min-rows", type=int, default=16,
                     help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--window-cycle-ns", type=int, default=None,
@@ -306,8 +340,9 @@ def main():
     import workloads as wl
     import zero_sharded_mixed_reduce_amd as z
 
-    for name, dflt in zip(("window_cycle_ns", "window_write_ns", "window_margin_ns", "window_lead_ns"),
-                          z.WRITE_WINDOW_DEFAULT):
+    names = ("window_cycle_ns", "window_write_ns", "window_margin_ns", "window_lead_ns")
+    args.window_explicit = any(getattr(args, n) is not None for n in names)
+    for name, dflt in zip(names, z.WRITE_WINDOW_DEFAULT):
         if getattr(args, name) is None:
             setattr(args, name, dflt)
 

@@ -276,10 +276,10 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
  * Adam, cast, and the fused step when it writes at once; default 2) and of
  * the copies (receive and ZeRO-3 gather; default 1; copies between
  * addresses that differ by an odd number of 2-byte elements run 4 per CU),
- * each 1..64; defer_tiles, 0..5 (default 2): how many completed 512-element
+ * each 1..64; defer_tiles, 0..5 (default 3): how many completed 512-element
  * tiles of fused-step results each wave keeps in LDS before it must write
  * them (0 = write at once; without write windows, that is below 32 rows or
- * with windows off, at most 2; with windows and at most 2, two workgroups
+ * with windows off, at most 2; with windows and at most 3, two workgroups
  * run per CU); and defer_min_rows >= 1 (default 16): the fewest gradient
  * rows for which the fused step defers its writes.
  * Process-wide.  Affects speed only, never results. */
@@ -296,8 +296,10 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
  * tiles whenever its LDS ring is full).
  * Otherwise 1,000 <= cycle_ns <= 10,000,000, write_ns >= 1, margin_ns >= 0,
  * write_ns + margin_ns < cycle_ns and 0 <= lead_ns < write_ns; ZSMR_ERR_ARG
- * if not.  Defaults: 50,000 / 8,000 / 1,000 / 2,000.  Process-wide.  Affects
- * speed only, never results. */
+ * if not.  Defaults: 74,000 / 12,000 / 1,000 / 2,000.  The best cycle follows
+ * the device's read rate (it is the time the rings take to fill), so a
+ * caller that can time the step may tune it.  Process-wide.  Affects speed
+ * only, never results. */
 int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin_ns,
                               int32_t lead_ns);
 

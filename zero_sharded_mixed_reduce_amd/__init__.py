@@ -299,13 +299,13 @@ def zero_stage3_unit_state(ctx: Ctx, unit: int):
     return bool(live.value), g.value, r.value
 
 
-def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 1, defer_tiles: int = 2,
+def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 1, defer_tiles: int = 3,
                           defer_min_rows: int = 16) -> None:
     _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc), int(defer_tiles),
                                         int(defer_min_rows)), "zsmr_set_launch_shape")
 
 
-WRITE_WINDOW_DEFAULT = (50000, 8000, 1000, 2000)
+WRITE_WINDOW_DEFAULT = (74000, 12000, 1000, 2000)
 
 
 def zsmr_set_write_window(cycle_ns: int = WRITE_WINDOW_DEFAULT[0],

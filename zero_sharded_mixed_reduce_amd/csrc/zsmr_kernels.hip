@@ -69,12 +69,13 @@ int g_copy_bpc = 1;
 constexpr int kNarrowCopyBpc = 4;
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
 // write windows (0 = write at once with step_vec8_kernel).  With windows and
-// a ring of at most 2 tiles, two workgroups run per CU (2 x 56 KB of LDS,
-// two waves per SIMD): more loads in flight while the other wave runs its
-// Adam tail.  Measured on MI355X, share64: 2 tiles x 2 workgroups 2.86-2.90
-// ms per step against 3.07 ms for 5 tiles x 1; without windows one
+// a ring of at most 3 tiles (72 KB per workgroup), two workgroups run per CU
+// (two waves per SIMD): one wave's loads stay in flight while the other runs
+// its Adam tail.  Measured on MI355X, share64, per step: 3 tiles x 2
+// workgroups 2.78 ms, 2 x 2 2.85 ms, 5 x 1 3.07 ms; without windows one
 // workgroup per CU is 5% faster (16-24 rows).
-int g_defer_tiles = 2;
+int g_defer_tiles = 3;
+constexpr int kRingTwoPerCu = 3;
 // ... used when a step reduces at least this many rows.  Measured on MI355X
 // against the direct kernel: single long launches at 16 rows +7%, 24 rows
 // +8.5%, 64 rows +22% (with windows); the 1.558e9-element, 16-rank world
@@ -85,16 +86,18 @@ int g_defer_min_rows = 16;
 // ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
 constexpr int kRingWithoutWindows = 2;
 // its write windows, in ns (0: none); converted to clock ticks per device
-// (measured on MI355X, share64, 2 tiles x 2 workgroups per CU: 50 / 8 / 1 /
-// 2 us gave 2.853-2.868 ms per step; the read phase, 42 us, is about the time
-// two waves per SIMD take to fill their 2-tile rings, so a longer cycle idles
-// until its window: 60 us cost 17%).
+// (measured on MI355X, share64, 3 tiles x 2 workgroups per CU: 74 / 12 / 1 /
+// 2 us gave 2.779 ms per step.  The read phase, ~63 us, is about the time two
+// waves per SIMD take to fill their 3-tile rings: a longer cycle idles until
+// its window, a shorter one pays the window more often; +-4 us cost 3-5%.
+// The best cycle follows the box's read rate, so callers that can measure
+// should tune it.)
 // Windows pay from 32 rows on; with fewer a tile is read so fast that the
 // ring fills long before a window (at 16 rows the windowed kernel ran 4%
 // slower than with stores at ring-full, which beat the direct kernel by 2%).
 constexpr int kWindowMinRows = 32;
-int64_t g_window_cycle_ns = 50000;
-int64_t g_window_write_ns = 8000;
+int64_t g_window_cycle_ns = 74000;
+int64_t g_window_write_ns = 12000;
 int64_t g_window_margin_ns = 1000;
 int64_t g_window_lead_ns = 2000;
 
@@ -462,8 +465,9 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 
 // The fused step with deferred, windowed writes.  A write stream mixed into
 // the 2N-row read stream costs HBM throughput out of proportion to its bytes,
-// so each wave keeps the results of its completed wave tiles (master, m, v
-// and the 16-bit copy: 112 B per lane per tile) in a ring of KD tiles in LDS
+// so each wave keeps the results of its completed wave tiles (master, m and
+// v: 96 B per lane per tile; the 16-bit copy is cast from the master when
+// the tile is stored) in a ring of KD tiles in LDS
 // and writes them only in the write windows, which every wave of the chip
 // takes at the same time from the shared clock: HBM then sees long read-only
 // stretches and short write-only bursts.  Between windows a wave streams its
@@ -486,7 +490,6 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
     __shared__ float s_w[kWaves][KD][512];      // a tile's results in element order
     __shared__ float s_m[kWaves][KD][512];
     __shared__ float s_v[kWaves][KD][512];
-    __shared__ uint32_t s_h[kWaves][KD][256];   // 16-bit copy, two elements per word
     const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
     const uint32_t tiles = static_cast<uint32_t>(vec_elems(a.n) / 512);
     const uint32_t nw = gridDim.x * kWaves;
@@ -514,13 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
                 v[4 + q] = s_v[wv][k][256u + lane * 4u + q];
             }
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint32_t lo = s_h[wv][k][lane * 2u + q], hi = s_h[wv][k][128u + lane * 2u + q];
-                h[2 * q] = lo & 0xffffu;
-                h[2 * q + 1] = lo >> 16;
-                h[4 + 2 * q] = hi & 0xffffu;
-                h[4 + 2 * q + 1] = hi >> 16;
-            }
+            for (int q = 0; q < 8; ++q) h[q] = narrow<PDT>(w[q]);   // the cast, at store time
             Groups<true>::store32(a.master, e0, e0 + 256u, w);
             Groups<true>::store32(a.m, e0, e0 + 256u, m);
             Groups<true>::store32(a.v, e0, e0 + 256u, v);
@@ -635,9 +632,6 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
             s_m[wv][k][lane * 8u + e] = st.m[e];
             s_v[wv][k][lane * 8u + e] = st.v[e];
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            s_h[wv][k][lane * 4u + e] = narrow<PDT>(st.w[2 * e]) | (narrow<PDT>(st.w[2 * e + 1]) << 16);
         ++done;
     };
 
@@ -838,7 +832,7 @@ template <int GDT, int PDT, int DV>
 hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
     const Window w = a.nrows >= kWindowMinRows ? window_ticks() : Window{0, 0, 0, 0};
     const int kd = w.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
-    const int bpc = w.cycle && kd <= 2 ? 2 : 1;
+    const int bpc = w.cycle && kd <= kRingTwoPerCu ? 2 : 1;
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, bpc));   // one wave per tile at most
     switch (kd) {
         case 1: hipLaunchKernelGGL((step_deferred_kernel<GDT, PDT, DV, 1>), grid, dim3(kThreads), 0, s, a, w); break;
