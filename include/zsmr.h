@@ -278,7 +278,7 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
  * addresses that differ by an odd number of 2-byte elements run 4 per CU),
  * each 1..64; defer_tiles, 0..5 (default 3): how many completed 512-element
  * tiles of fused-step results each wave keeps in LDS before it must write
- * them (0 = write at once; without write windows, that is below 32 rows or
+ * them (0 = write at once; without write windows, that is below 16 rows or
  * with windows off, at most 2; with windows and at most 3, two workgroups
  * run per CU); and defer_min_rows >= 1 (default 16): the fewest gradient
  * rows for which the fused step defers its writes.
@@ -292,8 +292,12 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
  * stored only inside windows, and no gradient loads are issued from
  * margin_ns before a window until lead_ns before its end, so HBM sees long
  * read-only stretches and short write-only bursts.  Windows apply to steps
- * of 32 or more rows.  cycle_ns = 0 turns them off (a wave then stores its
- * tiles whenever its LDS ring is full).
+ * of 16 or more rows.  cycle_ns is the cycle of a 64-row step; a step of R
+ * rows uses cycle_ns * (2R + 26) / 154 (its bytes per element against the
+ * 64-row step's: the time the rings take to fill scales with them), and runs
+ * without windows where that cannot hold write_ns + margin_ns.  cycle_ns = 0
+ * turns them off (a wave then stores its tiles whenever its LDS ring is
+ * full).
  * Otherwise 1,000 <= cycle_ns <= 10,000,000, write_ns >= 1, margin_ns >= 0,
  * write_ns + margin_ns < cycle_ns and 0 <= lead_ns < write_ns; ZSMR_ERR_ARG
  * if not.  Defaults: 74,000 / 12,000 / 1,000 / 2,000.  The best cycle follows

@@ -260,6 +260,86 @@ def test_alignment_variants(shift16, shift32, gshift, n, fused_path):
     assert not host32(mb)[:s].any() and not host32(mb)[s + n:].any()
 
 
+# (gradient rows, fp32 state, 16-bit copy) offsets in elements from a 128-byte line
+LINE_OFFSETS = [
+    (0, 0, 0),
+    (24, 24, 24),     # a rank's shard at r*S with S = 24 mod 64 (1.558e9 elements on 16 ranks)
+    (8, 8, 8),
+    (56, 56, 56),
+    (40, 0, 0),       # rows and state on different lines: the tiles follow the rows
+    (4, 0, 4),        # rows 8-byte aligned: after a head of 60 all on a line
+    (4, 0, 0),        # ... and the 16-bit copy then 8-byte aligned (64-bit stores)
+    (0, 12, 0),       # state off its line, rows on theirs: no head
+    (8, 2, 8),        # state 8-byte aligned: one element per lane, no head
+]
+
+
+def _line_buffers(n, world, gdt, goff, soff, poff):
+    rows, theta = _piece_inputs(n, world, gdt, seed=3)
+    stride = n + 64 - n % 64                                # rows 128 bytes apart
+    gbuf = np.zeros(goff + world * stride, np.uint16)
+    for r in range(world):
+        gbuf[goff + r * stride: goff + r * stride + n] = rows[r]
+    mk32 = lambda: torch.zeros(n + 64, dtype=torch.float32, device="cuda")
+    th = mk32()
+    th[soff:soff + n] = torch.from_numpy(theta).cuda()
+    return rows, theta, dev16(gbuf), stride, th, mk32(), mk32(), mk32(), mk32(), \
+        torch.zeros(n + 64, dtype=torch.bfloat16, device="cuda")
+
+
+@pytest.mark.parametrize("goff,soff,poff", LINE_OFFSETS)
+@pytest.mark.parametrize("world", [4, 16])
+def test_line_heads_fused(goff, soff, poff, world, fused_path):
+    """Pieces that do not start on a 128-byte line: the vector body's tiles
+    start on the line of the gradient rows, and the elements before it run
+    one by one.  Results match the oracle; nothing outside the piece is
+    written."""
+    n, gdt, T, lr = 512 * 40 + 77, "bf16", 2, 1e-3
+    say(f"[line heads fused] offsets={goff},{soff},{poff} world={world} defer={fused_path}")
+    rows, theta, G, stride, th, mb, mm, vb, _, pb = _line_buffers(n, world, gdt, goff, soff, poff)
+    ctx = z.zero_init_shards(n * world, world, 2, gdt)
+    s, q = soff, poff
+    z.zero_init_state(ctx, 0, 0, th[s:], mb[s:], mm[s:], vb[s:], pb[q:])
+    for t in range(1, T + 1):
+        z.zero_fused_step(ctx, 0, 0, G[goff:], stride, 0, mb[s:], mm[s:], vb[s:], pb[q:], t, lr)
+    torch.cuda.synchronize()
+    master, m, v, p16 = _oracle_piece(rows, theta, gdt, gdt, T, lr)
+    got16 = host16(pb)
+    compare({"master": host32(mb)[s:s + n], "m": host32(mm)[s:s + n], "v": host32(vb)[s:s + n]},
+            {"master": master, "m": m, "v": v}, got16[q:q + n], p16,
+            f"line heads offsets={goff},{soff},{poff} world={world}")
+    assert not got16[:q].any() and not got16[q + n:].any()
+    for b in (mb, mm, vb):
+        assert not host32(b)[:s].any() and not host32(b)[s + n:].any()
+
+
+@pytest.mark.parametrize("goff,soff,poff", LINE_OFFSETS)
+def test_line_heads_three_kernels(goff, soff, poff):
+    """The same pieces through the reduce, Adam and cast kernels: the reduce
+    aligns on the gradient rows, Adam and the cast on the fp32 master."""
+    n, world, gdt, lr = 512 * 40 + 77, 6, "bf16", 1e-3
+    say(f"[line heads three kernels] offsets={goff},{soff},{poff}")
+    rows, theta, G, stride, th, mb, mm, vb, gb, pb = _line_buffers(n, world, gdt, goff, soff, poff)
+    ctx = z.zero_init_shards(n * world, world, 2, gdt)
+    s, q = soff, poff
+    z.zero_init_state(ctx, 0, 0, th[s:], mb[s:], mm[s:], vb[s:], pb[q:])
+    z.zero_reduce_shard(ctx, 0, 0, G[goff:], stride, 0, True, gb[s:])
+    z.zero_adam_step(mb[s:], mm[s:], vb[s:], gb[s:], n, 1, lr)
+    z.zero_gather_cast(ctx, 0, 0, mb[s:], pb[q:])
+    torch.cuda.synchronize()
+    g = nm.reduce_rank_order([nm.widen16(r, gdt) for r in rows])
+    assert np.array_equal(host32(gb)[s:s + n].view(np.uint32), g.view(np.uint32))
+    master, m, v, p16 = _oracle_piece(rows, theta, gdt, gdt, 1, lr)
+    got16 = host16(pb)
+    compare({"master": host32(mb)[s:s + n], "m": host32(mm)[s:s + n], "v": host32(vb)[s:s + n]},
+            {"master": master, "m": m, "v": v}, got16[q:q + n], p16,
+            f"line heads (three kernels) offsets={goff},{soff},{poff}")
+    assert not got16[:q].any() and not got16[q + n:].any()
+    for b in (mb, mm, vb, gb):
+        assert not host32(b)[:s].any() and not host32(b)[s + n:].any()
+
+
+
 @pytest.mark.parametrize("gdt,pdt", [("fp16", "bf16"), ("bf16", "fp16"), ("fp16", "fp16")])
 def test_mixed_formats(gdt, pdt, fused_path):
     n, world, T, lr = 3 * 2048 + 3, 17, 3, 1e-2
@@ -337,7 +417,7 @@ WINDOWS = {
     "default": z.WRITE_WINDOW_DEFAULT,
     "off": (0, 0, 0, 0),
     "short": (1000, 300, 0, 0),                # many windows per tile: partial sums cross them
-    "margin": (2000, 500, 700, 200),
+    "margin": (4000, 500, 700, 200),           # scaled to 1,506 ns at 16 rows
     "long": (200000, 20000, 0, 5000),          # the ring fills long before a window
 }
 
@@ -349,7 +429,8 @@ def test_deferred_windows_match_direct_bits(window, kd, rows):
     """Write windows and ring sizes change only when results are stored:
     the deferred kernel gives the direct kernel's bits, and writes nothing
     outside the piece.  With 8 rows or fewer a tile is one row batch (its
-    first and last); windows apply from 32 rows."""
+    first and last); windows apply from 16 rows, their cycle scaled to the
+    row count."""
     n = 1024 * 6 * 512 + 2 * 512 + 131           # ~6 tiles per wave, a ragged tail
     say(f"[deferred] window={window} kd={kd} rows={rows} n={n}")
     ref = _fused_run(n, rows, 2, 0, WINDOWS["off"])

@@ -92,10 +92,20 @@ constexpr int kRingWithoutWindows = 2;
 // its window, a shorter one pays the window more often; +-4 us cost 3-5%.
 // The best cycle follows the box's read rate, so callers that can measure
 // should tune it.)
-// Windows pay from 32 rows on; with fewer a tile is read so fast that the
-// ring fills long before a window (at 16 rows the windowed kernel ran 4%
-// slower than with stores at ring-full, which beat the direct kernel by 2%).
-constexpr int kWindowMinRows = 32;
+// The cycle as set is the one for 64 rows of 16-bit gradients.  A wave's
+// ring fills in a time proportional to the bytes its tiles move per element
+// (2 * rows + 26: the gradient rows, master, m and v read and written, the
+// 16-bit copy written), so a step of other row counts scales the cycle by
+// (2 * rows + 26) / 154; the write window, margin and lead stay as set.
+// Measured on MI355X, 97,375,000 elements, 3 tiles x 2 workgroups per CU
+// (no windows / scaled / the 64-row cycle unscaled): 16 rows 1.007 / 1.008
+// (x1.1: 0.988) ms, 24 rows 1.292 / 1.190, 32 rows 1.577 / 1.421 / 2.260,
+// 48 rows 2.186 / 1.858 / 2.276.
+// Windows pay from 16 rows on; with 8 the ring fills so fast that the
+// windowed kernel ran 19% slower than the direct one.
+constexpr int kWindowMinRows = 16;
+constexpr int64_t kWindowRefBytes = 2 * 64 + 26;
+constexpr int64_t kMaxCycleTicks = int64_t(1) << 30;
 int64_t g_window_cycle_ns = 74000;
 int64_t g_window_write_ns = 12000;
 int64_t g_window_margin_ns = 1000;
@@ -407,8 +417,17 @@ constexpr bool kSplit = ZSMR_SPLIT != 0;
 // elements the vector path covers: whole wave tiles (split) or whole 8s
 __host__ __device__ constexpr int64_t vec_elems(int64_t n) { return kSplit ? n / 512 * 512 : n / 8 * 8; }
 
-// Aligned path over vector index i (8 elements each); the elements past the
-// last whole tile go one per lane to workgroup 0.
+// The elements outside whole tiles, one per lane of workgroup 0: those past
+// the last tile and the head before the first.
+template <int GDT, int PDT, int MODE>
+__device__ __forceinline__ void edges1(const StepArgs& a) {
+    if (blockIdx.x != 0) return;
+    for (int64_t e = vec_elems(a.n) + threadIdx.x; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
+    for (int64_t e = (int64_t)threadIdx.x - a.head; e < 0; e += kThreads) body1<GDT, PDT, MODE>(a, e);
+}
+
+// Aligned path over vector index i (8 elements each); the elements outside
+// whole tiles go one per lane to workgroup 0.
 template <int GDT, int PDT, int MODE, int DV>
 __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
     const int64_t n_main = vec_elems(a.n);
@@ -438,8 +457,7 @@ __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
     const uint32_t stride = gridDim.x * kThreads;
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) run(i);
 #endif
-    if (blockIdx.x == 0)
-        for (int64_t e = n_main + threadIdx.x; e < a.n; e += kThreads) body1<GDT, PDT, MODE>(a, e);
+    edges1<GDT, PDT, MODE>(a);
 }
 
 // Write windows of the deferred-write kernel, in ticks of the chip's
@@ -661,9 +679,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
         }
     }
     flush();
-    if (blockIdx.x == 0)
-        for (int64_t e = vec_elems(a.n) + threadIdx.x; e < a.n; e += kThreads)
-            body1<GDT, PDT, M_REDUCE | M_ADAM | M_CAST>(a, e);
+    edges1<GDT, PDT, M_REDUCE | M_ADAM | M_CAST>(a);
 }
 
 // Any-alignment path: one element per lane.
@@ -815,12 +831,15 @@ int64_t clock_hz() {
     return hz > 0 ? hz : 0;
 }
 
-Window window_ticks() {
+// the windows of a step reducing `rows` rows (the cycle scaled to its bytes
+// per element, at most 2^30 ticks)
+Window window_ticks(int32_t rows) {
     Window w{0, 0, 0, 0};
     const int64_t hz = clock_hz();
-    if (!g_window_cycle_ns || !hz) return w;
+    if (!g_window_cycle_ns || !hz || rows < 1) return w;
     auto ticks = [&](int64_t ns) { return static_cast<uint32_t>(ns * hz / 1000000000); };
-    w.cycle = ticks(g_window_cycle_ns);
+    const int64_t cycle = int64_t(ticks(g_window_cycle_ns)) * (2 * int64_t(rows) + 26) / kWindowRefBytes;
+    w.cycle = static_cast<uint32_t>(cycle < kMaxCycleTicks ? cycle : kMaxCycleTicks);
     w.write = ticks(g_window_write_ns);
     w.margin = ticks(g_window_margin_ns);
     w.lead = ticks(g_window_lead_ns);
@@ -830,7 +849,7 @@ Window window_ticks() {
 
 template <int GDT, int PDT, int DV>
 hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
-    const Window w = a.nrows >= kWindowMinRows ? window_ticks() : Window{0, 0, 0, 0};
+    const Window w = a.nrows >= kWindowMinRows ? window_ticks(a.nrows) : Window{0, 0, 0, 0};
     const int kd = w.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
     const int bpc = w.cycle && kd <= kRingTwoPerCu ? 2 : 1;
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, bpc));   // one wave per tile at most
@@ -899,7 +918,8 @@ void set_write_window(int64_t cycle_ns, int64_t write_ns, int64_t margin_ns, int
 }
 
 namespace {
-hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
+// whether the operands a launch of `mode` uses allow the vector path
+bool vec_ok(int mode, const StepArgs& a) {
     bool vec = true;
     if (mode & M_REDUCE)
         vec = vec && (kSplit ? al(a.grads, 8) && (a.row_stride % 4) == 0
@@ -908,6 +928,47 @@ hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStr
     if (mode & (M_ADAM | M_INIT)) vec = vec && al(a.m, 16) && al(a.v, 16);
     if ((mode & M_INIT) || ((mode & M_ADAM) && !(mode & M_REDUCE))) vec = vec && al(a.g_in, 16);
     if (mode & M_GOUT) vec = vec && al(a.g_out, 16);
+    return vec;
+}
+
+// a's operands `d` elements further on, with n - d elements and head `head`
+StepArgs advanced(const StepArgs& a, int64_t d, int64_t n, int32_t head) {
+    StepArgs b = a;
+    b.n = n;
+    b.head = head;
+    if (b.grads) b.grads += d;
+    if (b.g_in) b.g_in += d;
+    if (b.g_out) b.g_out += d;
+    if (b.master) b.master += d;
+    if (b.m) b.m += d;
+    if (b.v) b.v += d;
+    if (b.p16) b.p16 += d;
+    return b;
+}
+
+// Elements to run one by one before the vector body so that its tiles start
+// on a 128-byte line of the operand read most: the gradient rows when the
+// launch reduces, else the fp32 master.  A slice at an offset that is not a
+// multiple of 64 elements (a rank's shard in a vector that N cuts into
+// shards whose size is not such a multiple) otherwise has every wave's
+// loads and stores straddle one line more than they cover; measured on
+// MI355X, 16 rows, 97,375,000 elements: 1.09-1.23 ms per launch at a
+// straddling offset against 0.98-1.01 ms on a line.  0 where the piece is
+// shorter than a tile past the head, or where the shift would cost an
+// operand its vector alignment.
+int64_t line_head(int mode, const StepArgs& a) {
+    const bool red = (mode & M_REDUCE) != 0;
+    const uintptr_t p = red ? reinterpret_cast<uintptr_t>(a.grads) : reinterpret_cast<uintptr_t>(a.master);
+    const uintptr_t es = red ? 2 : 4;
+    if (!p || p % es || !vec_ok(mode, a)) return 0;
+    const int64_t h = static_cast<int64_t>((128 - p % 128) % 128 / es);
+    if (h == 0 || a.n - h < 512) return 0;
+    return vec_ok(mode, advanced(a, h, a.n - h, 0)) ? h : 0;
+}
+
+hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
+    const bool vec = vec_ok(mode, a);
+    if (!vec && a.head) return hipErrorInvalidValue;   // the host gives a head to vector launches only
     const int dv = (mode & M_CAST) ? dst_vec(a.p16) : 8;
     switch (mode) {
         case M_REDUCE | M_ADAM | M_CAST: return launch_dt<M_REDUCE | M_ADAM | M_CAST>(gdt, pdt, a, vec, dv, s);
@@ -920,21 +981,15 @@ hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStr
 }
 }  // namespace
 
-// Pieces of 2^30 elements or more are cut into launches of at most 2^30
-// (a multiple of every vector width, so alignment is kept).
+// A piece's head (the elements before its first 128-byte line) runs with the
+// first launch; the rest is cut into launches of at most 2^30 elements (a
+// multiple of every vector width and of the line, so alignment is kept).
 hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream_t s) {
     constexpr int64_t kMaxLaunch = int64_t(1) << 30;
-    for (int64_t c = 0; c < a0.n; c += kMaxLaunch) {
-        StepArgs a = a0;
-        a.n = a0.n - c < kMaxLaunch ? a0.n - c : kMaxLaunch;
-        if (a.grads) a.grads += c;
-        if (a.g_in) a.g_in += c;
-        if (a.g_out) a.g_out += c;
-        if (a.master) a.master += c;
-        if (a.m) a.m += c;
-        if (a.v) a.v += c;
-        if (a.p16) a.p16 += c;
-        const hipError_t e = launch_step_one(mode, gdt, pdt, a, s);
+    const int64_t h = line_head(mode, a0);
+    for (int64_t c = h; c < a0.n; c += kMaxLaunch) {
+        const int64_t n = a0.n - c < kMaxLaunch ? a0.n - c : kMaxLaunch;
+        const hipError_t e = launch_step_one(mode, gdt, pdt, advanced(a0, c, n, c == h ? (int32_t)h : 0), s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -34,7 +34,11 @@ struct StepArgs {
     float* m;
     float* v;
     uint16_t* p16;
-    int64_t n;              // elements of the piece
+    int64_t n;              // elements from the pointers on
+    int32_t head;           // elements just before the pointers that also
+                            // belong to the piece (the vector path's tiles
+                            // then start on a 128-byte line); run one per
+                            // lane by workgroup 0, with the tail
     AdamK k;
 };
 
