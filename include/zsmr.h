@@ -36,7 +36,10 @@
  *    the 2.5e10-element gradient set exceed 2^32).
  *  - fp32 buffers (master, m, v, g, theta0) must be 4-byte aligned; the fast
  *    path wants 16 bytes.  16-bit buffers must be 2-byte aligned.  Any legal
- *    alignment works; the kernel variant is chosen from the pointers.
+ *    alignment works; the kernel variant is chosen from the pointers.  Where
+ *    a piece does not start on a 128-byte line, up to 63 leading elements
+ *    run one by one so that the rest is processed in line-aligned tiles
+ *    (results do not depend on it).
  */
 #ifndef ZSMR_H
 #define ZSMR_H
