@@ -3,10 +3,11 @@
 // One streaming pass per launch.  The path is bound by HBM bandwidth (about
 // 0.3-0.6 flop per byte), so there is no MFMA: every lane owns 8 elements of
 // a 512-element wave tile, reads each 16-bit gradient row and the fp32
-// master/m/v once, and writes each output once.  LDS only holds results whose
-// stores are deferred (the fused step) and copy bursts.  The same device code, selected by the MODE bits, gives the fused
-// step and the unfused reduce-only, Adam-only, cast-only and init launches,
-// so the fused and unfused results are the same bits.
+// master/m/v once, and writes each output once.  LDS only holds the results
+// whose stores are deferred (the fused step).  The same device code, selected
+// by the MODE bits, gives the fused step and the unfused reduce-only,
+// Adam-only, cast-only and init launches, so the fused and unfused results
+// are the same bits.
 //
 // Arithmetic (the pages: "The four schemes", Base._adam and the schemes'
 // reduce_scatter_mean / astype casts; "ZeRO and FSDP", ZeroAdam.step):
@@ -35,20 +36,11 @@
 #ifndef ZSMR_ROW_BATCH
 #define ZSMR_ROW_BATCH 8        // gradient rows in flight per lane
 #endif
-#ifndef ZSMR_EARLY_STATE
-#define ZSMR_EARLY_STATE 0      // issue master/m/v loads before the reduce
-#endif
 #ifndef ZSMR_COPY_UNROLL
-#define ZSMR_COPY_UNROLL 1      // 16-byte vectors in flight per lane in copies
-#endif
-#ifndef ZSMR_STEP_CHUNKED
-#define ZSMR_STEP_CHUNKED 0     // step kernel: one contiguous chunk per workgroup
+#define ZSMR_COPY_UNROLL 1      // vectors in flight per lane in the 2-byte copy
 #endif
 #ifndef ZSMR_COPY_BURST_BYTES
 #define ZSMR_COPY_BURST_BYTES 512   // copies: bytes per lane per register burst (32 KB per wave)
-#endif
-#ifndef ZSMR_SPLIT
-#define ZSMR_SPLIT 1            // wave-contiguous element map (see Groups)
 #endif
 
 namespace zsmr {
@@ -85,13 +77,18 @@ int g_defer_min_rows = 16;
 // without windows the ring holds at most this many tiles: smaller bursts at
 // ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
 constexpr int kRingWithoutWindows = 2;
-// its write windows, in ns (0: none); converted to clock ticks per device
-// (measured on MI355X, share64, 3 tiles x 2 workgroups per CU: 74 / 12 / 1 /
-// 2 us gave 2.779 ms per step.  The read phase, ~63 us, is about the time two
-// waves per SIMD take to fill their 3-tile rings: a longer cycle idles until
-// its window, a shorter one pays the window more often; +-4 us cost 3-5%.
-// The best cycle follows the box's read rate, so callers that can measure
-// should tune it.)
+// Its write windows, in ns (cycle 0: none), converted to clock ticks per
+// device.  Measured on MI355X, share64, 3 tiles x 2 workgroups per CU:
+// 74 / 12 / 1 / 2 us (cycle, write, margin, lead) gave 2.779 ms per step.
+// The read phase, ~63 us, is about the time two waves per SIMD take to fill
+// their 3-tile rings: a longer cycle idles until its window, a shorter one
+// pays the window more often; +-4 us cost 3-5%.  The best window follows
+// the device's read rate (72 / 12 / 1 / 4 won by 1.7% on one box and lost by
+// 4% on another), so callers that can time the step should tune it.
+int64_t g_window_cycle_ns = 74000;
+int64_t g_window_write_ns = 12000;
+int64_t g_window_margin_ns = 1000;
+int64_t g_window_lead_ns = 2000;
 // The cycle as set is the one for 64 rows of 16-bit gradients.  A wave's
 // ring fills in a time proportional to the bytes its tiles move per element
 // (2 * rows + 26: the gradient rows, master, m and v read and written, the
@@ -101,15 +98,12 @@ constexpr int kRingWithoutWindows = 2;
 // (no windows / scaled / the 64-row cycle unscaled): 16 rows 1.007 / 1.008
 // (x1.1: 0.988) ms, 24 rows 1.292 / 1.190, 32 rows 1.577 / 1.421 / 2.260,
 // 48 rows 2.186 / 1.858 / 2.276.
-// Windows pay from 16 rows on; with 8 the ring fills so fast that the
-// windowed kernel ran 19% slower than the direct one.
-constexpr int kWindowMinRows = 16;
 constexpr int64_t kWindowRefBytes = 2 * 64 + 26;
 constexpr int64_t kMaxCycleTicks = int64_t(1) << 30;
-int64_t g_window_cycle_ns = 74000;
-int64_t g_window_write_ns = 12000;
-int64_t g_window_margin_ns = 1000;
-int64_t g_window_lead_ns = 2000;
+// Windows pay from 16 rows on; with 8 the ring fills so fast that the
+// windowed kernel ran 19% slower than the direct one (4-13% with windows
+// sized for 8 rows).
+constexpr int kWindowMinRows = 16;
 
 // Streamed data is touched once per step: non-temporal loads and stores keep
 // it from displacing anything useful in L2 and the MALL.
@@ -201,41 +195,29 @@ __device__ __forceinline__ void store4x16(uint16_t* p, const uint32_t* h) {
 }
 
 // ------------------------------------------- two 4-element groups per lane --
-// A lane owns elements e0..e0+3 and e1..e1+3.  SPLIT: a wave owns 512
-// consecutive elements, lane l the groups at 4l and 256+4l, so every load
-// and store instruction of the wave covers one contiguous run (1 KB of fp32,
-// 512 B of 16-bit data).  Otherwise e1 = e0 + 4 (8 consecutive elements, one
-// 16-byte load per gradient row).
-template <bool SPLIT>
+// A lane owns elements e0..e0+3 and e1..e1+3.  The store map, which every
+// kernel uses for its stores and the direct kernels for everything: a wave
+// owns 512 consecutive elements, lane l the groups at 4l and 256+4l
+// (e1 = e0 + 256), so every load and store instruction of the wave covers one
+// contiguous run (1 KB of fp32, 512 B of 16-bit data).  The deferred kernel
+// computes in the contiguous map, e1 = e0 + 4: 8 consecutive elements per
+// lane, one 16-byte load per gradient row.
 struct Groups {
-    // the 8 raw 16-bit words of one row, packed two per dword
+    // the 8 raw 16-bit words of one row in the store map, packed two per dword
     __device__ static __forceinline__ u32x4 load16raw(const uint16_t* p, uint32_t e0, uint32_t e1) {
-        if constexpr (SPLIT) {
-            const u32x2 a = ld(reinterpret_cast<const u32x2*>(p + e0));
-            const u32x2 b = ld(reinterpret_cast<const u32x2*>(p + e1));
-            u32x4 r;
-            r[0] = a[0];
-            r[1] = a[1];
-            r[2] = b[0];
-            r[3] = b[1];
-            return r;
-        } else {
-            return ld(reinterpret_cast<const u32x4*>(p + e0));
-        }
+        const u32x2 a = ld(reinterpret_cast<const u32x2*>(p + e0));
+        const u32x2 b = ld(reinterpret_cast<const u32x2*>(p + e1));
+        u32x4 r;
+        r[0] = a[0];
+        r[1] = a[1];
+        r[2] = b[0];
+        r[3] = b[1];
+        return r;
     }
     template <int DV>
     __device__ static __forceinline__ void store16(uint16_t* p, uint32_t e0, uint32_t e1, const uint32_t* h) {
-        if constexpr (!SPLIT && DV == 8) {
-            u32x4 w;
-            w[0] = h[0] | (h[1] << 16);
-            w[1] = h[2] | (h[3] << 16);
-            w[2] = h[4] | (h[5] << 16);
-            w[3] = h[6] | (h[7] << 16);
-            st(reinterpret_cast<u32x4*>(p + e0), w);
-        } else {
-            store4x16<DV>(p + e0, h);
-            store4x16<DV>(p + e1, h + 4);
-        }
+        store4x16<DV>(p + e0, h);
+        store4x16<DV>(p + e1, h + 4);
     }
     __device__ static __forceinline__ void load32(const float* p, uint32_t e0, uint32_t e1, float* f) {
         const f32x4 a = ld(reinterpret_cast<const f32x4*>(p + e0));
@@ -258,7 +240,6 @@ struct Groups {
     }
 };
 
-template <bool SPLIT>
 __device__ __forceinline__ void load_rows(const StepArgs& a, int r, uint32_t e0, uint32_t e1, u32x4* buf) {
     // rows past the last one are clamped to it: every load is issued
     // unconditionally (so the compiler can count them) and the re-read row
@@ -266,7 +247,7 @@ __device__ __forceinline__ void load_rows(const StepArgs& a, int r, uint32_t e0,
 #pragma unroll
     for (int k = 0; k < kRowBatch; ++k) {
         const int rr = r + k < a.nrows ? r + k : a.nrows - 1;
-        buf[k] = Groups<SPLIT>::load16raw(a.grads + (int64_t)rr * a.row_stride, e0, e1);
+        buf[k] = Groups::load16raw(a.grads + (int64_t)rr * a.row_stride, e0, e1);
     }
 }
 
@@ -283,25 +264,12 @@ __device__ __forceinline__ void add_rows(const StepArgs& a, int r, const u32x4* 
     }
 }
 
-// Results of the fused step for one lane's 8 elements, when they are kept on
-// chip instead of being stored at once (the deferred-write kernel).
-struct Out8 {
-    float w[8], m[8], v[8];
-    uint32_t h[8];
-};
-
-template <bool SPLIT, int GDT, int PDT, int MODE, int DV, bool DEFER = false>
-__device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1, Out8* out = nullptr) {
-    static_assert(!DEFER || MODE == (M_REDUCE | M_ADAM | M_CAST), "only the fused step defers");
-    typedef Groups<SPLIT> G;
+// One lane's 8 elements (groups at e0 and e1) of the launch's MODE.
+template <int GDT, int PDT, int MODE, int DV>
+__device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1) {
+    typedef Groups G;
     float g[8];
     float w[8], m[8], v[8];
-    constexpr bool early = ZSMR_EARLY_STATE && (MODE & M_ADAM) && (MODE & M_REDUCE);
-    if constexpr (early) {
-        G::load32(a.master, e0, e1, w);
-        G::load32(a.m, e0, e1, m);
-        G::load32(a.v, e0, e1, v);
-    }
     if constexpr ((MODE & M_REDUCE) != 0) {
         // rows 1..N-1 in batches, double-buffered so that one batch is in
         // flight while the previous one is added; the sum itself runs
@@ -309,21 +277,21 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         u32x4 bufA[kRowBatch], bufB[kRowBatch];
         const u32x4 row0 = G::load16raw(a.grads, e0, e1);
         int r = 1;
-        if (a.nrows > 1) load_rows<SPLIT>(a, r, e0, e1, bufA);
+        if (a.nrows > 1) load_rows(a, r, e0, e1, bufA);
         unpack8<GDT>(row0, g);
         while (r < a.nrows) {
             if (r + kRowBatch >= a.nrows) {
                 add_rows<GDT>(a, r, bufA, g);
                 break;
             }
-            load_rows<SPLIT>(a, r + kRowBatch, e0, e1, bufB);
+            load_rows(a, r + kRowBatch, e0, e1, bufB);
             add_rows<GDT>(a, r, bufA, g);
             r += kRowBatch;
             if (r + kRowBatch >= a.nrows) {
                 add_rows<GDT>(a, r, bufB, g);
                 break;
             }
-            load_rows<SPLIT>(a, r + kRowBatch, e0, e1, bufA);
+            load_rows(a, r + kRowBatch, e0, e1, bufA);
             add_rows<GDT>(a, r, bufB, g);
             r += kRowBatch;
         }
@@ -337,25 +305,14 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
     }
 
     if constexpr ((MODE & M_ADAM) != 0) {
-        if constexpr (!early) {
-            G::load32(a.master, e0, e1, w);
-            G::load32(a.m, e0, e1, m);
-            G::load32(a.v, e0, e1, v);
-        }
+        G::load32(a.master, e0, e1, w);
+        G::load32(a.m, e0, e1, m);
+        G::load32(a.v, e0, e1, v);
 #pragma unroll
         for (int j = 0; j < 8; ++j) adam1(a.k, g[j], w[j], m[j], v[j]);
-        if constexpr (DEFER) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                out->w[j] = w[j];
-                out->m[j] = m[j];
-                out->v[j] = v[j];
-            }
-        } else {
-            G::store32(a.master, e0, e1, w);
-            G::store32(a.m, e0, e1, m);
-            G::store32(a.v, e0, e1, v);
-        }
+        G::store32(a.master, e0, e1, w);
+        G::store32(a.m, e0, e1, m);
+        G::store32(a.v, e0, e1, v);
     } else if constexpr ((MODE & M_INIT) != 0) {
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -371,12 +328,7 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = narrow<PDT>(w[j]);
-        if constexpr (DEFER) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) out->h[j] = h[j];
-        } else {
-            G::template store16<DV>(a.p16, e0, e1, h);
-        }
+        G::template store16<DV>(a.p16, e0, e1, h);
     }
 }
 
@@ -413,9 +365,8 @@ __device__ __forceinline__ void body1(const StepArgs& a, int64_t e) {
 }
 
 // ---------------------------------------------------------------- kernels --
-constexpr bool kSplit = ZSMR_SPLIT != 0;
-// elements the vector path covers: whole wave tiles (split) or whole 8s
-__host__ __device__ constexpr int64_t vec_elems(int64_t n) { return kSplit ? n / 512 * 512 : n / 8 * 8; }
+// elements the vector path covers: whole 512-element wave tiles
+__host__ __device__ constexpr int64_t vec_elems(int64_t n) { return n / 512 * 512; }
 
 // The elements outside whole tiles, one per lane of workgroup 0: those past
 // the last tile and the head before the first.
@@ -426,37 +377,18 @@ __device__ __forceinline__ void edges1(const StepArgs& a) {
     for (int64_t e = (int64_t)threadIdx.x - a.head; e < 0; e += kThreads) body1<GDT, PDT, MODE>(a, e);
 }
 
-// Aligned path over vector index i (8 elements each); the elements outside
-// whole tiles go one per lane to workgroup 0.
+// Aligned path over vector index i (8 elements each, grid-stride); the
+// elements outside whole tiles go one per lane to workgroup 0.
 template <int GDT, int PDT, int MODE, int DV>
 __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
-    const int64_t n_main = vec_elems(a.n);
-    const int64_t nvec = n_main >> 3;
     // a launch covers fewer than 2^31 elements (the host splits larger
     // pieces), so in-launch offsets are 32-bit
-    auto run = [&](uint32_t i) {
-        uint32_t e0, e1;
-        if constexpr (kSplit) {
-            e0 = (i >> 6) * 512u + (i & 63u) * 4u;   // wave tile, lane group
-            e1 = e0 + 256u;
-        } else {
-            e0 = i << 3;
-            e1 = e0 + 4u;
-        }
-        body8<kSplit, GDT, PDT, MODE, DV>(a, e0, e1);
-    };
-    const uint32_t nv = static_cast<uint32_t>(nvec);
-#if ZSMR_STEP_CHUNKED
-    // workgroup b streams vectors [b*chunk, (b+1)*chunk): each row, band and
-    // output is one sequential run per workgroup
-    const uint32_t chunk = ((nv + gridDim.x - 1) / gridDim.x + kThreads - 1) / kThreads * kThreads;
-    const uint32_t lo = blockIdx.x * chunk;
-    const uint32_t hi = lo + chunk < nv ? lo + chunk : nv;
-    for (uint32_t i = lo + threadIdx.x; i < hi; i += kThreads) run(i);
-#else
+    const uint32_t nv = static_cast<uint32_t>(vec_elems(a.n) >> 3);
     const uint32_t stride = gridDim.x * kThreads;
-    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) run(i);
-#endif
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
+        const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;   // wave tile, lane group
+        body8<GDT, PDT, MODE, DV>(a, e0, e0 + 256u);
+    }
     edges1<GDT, PDT, MODE>(a);
 }
 
@@ -503,7 +435,6 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 // fewer than 2^63 bytes.
 template <int GDT, int PDT, int DV, int KD>
 __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, Window win) {
-    static_assert(kSplit, "the deferred kernel uses the wave-contiguous element map");
     constexpr int kWaves = kThreads / 64;
     __shared__ float s_w[kWaves][KD][512];      // a tile's results in element order
     __shared__ float s_m[kWaves][KD][512];
@@ -536,10 +467,10 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) h[q] = narrow<PDT>(w[q]);   // the cast, at store time
-            Groups<true>::store32(a.master, e0, e0 + 256u, w);
-            Groups<true>::store32(a.m, e0, e0 + 256u, m);
-            Groups<true>::store32(a.v, e0, e0 + 256u, v);
-            Groups<true>::template store16<DV>(a.p16, e0, e0 + 256u, h);
+            Groups::store32(a.master, e0, e0 + 256u, w);
+            Groups::store32(a.m, e0, e0 + 256u, m);
+            Groups::store32(a.v, e0, e0 + 256u, v);
+            Groups::template store16<DV>(a.p16, e0, e0 + 256u, h);
         }
         flushed = done;
     };
@@ -607,9 +538,9 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
         }
         i_row += kRowBatch;
         if (i_row >= nrows) {      // the tile's last batch: its master/m/v come with it
-            Groups<false>::load32(a.master, e0, e0 + 4u, st.w);
-            Groups<false>::load32(a.m, e0, e0 + 4u, st.m);
-            Groups<false>::load32(a.v, e0, e0 + 4u, st.v);
+            Groups::load32(a.master, e0, e0 + 4u, st.w);   // contiguous map
+            Groups::load32(a.m, e0, e0 + 4u, st.m);
+            Groups::load32(a.v, e0, e0 + 4u, st.v);
             ++i_tile;
             i_row = 0;
             i_ptr = grads;
@@ -742,21 +673,22 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
             }
         }
     } else {
-    // one contiguous chunk per workgroup; kCopyUnroll consecutive groups of
-    // kThreads vectors are loaded before any is stored
-    constexpr int64_t group = (int64_t)kThreads * kCopyUnroll;
-    const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
-    const int64_t lo = part * chunk;
-    const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += group) {
-        V tmp[kCopyUnroll];
+        // 2-byte elements (source and destination an odd number of elements
+        // apart): one contiguous chunk per workgroup; kCopyUnroll consecutive
+        // groups of kThreads elements are loaded before any is stored
+        constexpr int64_t group = (int64_t)kThreads * kCopyUnroll;
+        const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
+        const int64_t lo = part * chunk;
+        const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
+        for (int64_t i = lo + threadIdx.x; i < hi; i += group) {
+            V tmp[kCopyUnroll];
 #pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            if (i + k * kThreads < hi) tmp[k] = ld(s + i + k * kThreads);
+            for (int k = 0; k < kCopyUnroll; ++k)
+                if (i + k * kThreads < hi) tmp[k] = ld(s + i + k * kThreads);
 #pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            if (i + k * kThreads < hi) st(d + i + k * kThreads, tmp[k]);
-    }
+            for (int k = 0; k < kCopyUnroll; ++k)
+                if (i + k * kThreads < hi) st(d + i + k * kThreads, tmp[k]);
+        }
     }
     if (part == 0) {
         const int t = static_cast<int>(threadIdx.x);
@@ -810,8 +742,9 @@ unsigned grid_for(int64_t work_items, int bpc) {
 
 inline bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// 16-bit elements per store the destination allows (a lane's groups are 4
+// elements, so at most 4)
 int dst_vec(const void* p) {
-    if (al(p, 16) && !kSplit) return 8;
     if (al(p, 8)) return 4;
     if (al(p, 4)) return 2;
     return 1;
@@ -865,11 +798,10 @@ hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
 
 template <int GDT, int PDT, int MODE>
 hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
-    if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST) && kSplit) {
+    if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST)) {
         if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows && al(a.grads, 16) &&
             a.row_stride % 8 == 0) {
             switch (dv) {
-                case 8:
                 case 4: return launch_deferred<GDT, PDT, 4>(a, s);
                 case 2: return launch_deferred<GDT, PDT, 2>(a, s);
                 default: return launch_deferred<GDT, PDT, 1>(a, s);
@@ -883,7 +815,6 @@ hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
     }
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc));
     switch (dv) {
-        case 8: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 8>), grid, dim3(kThreads), 0, s, a); break;
         case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
         case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
         default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
@@ -922,8 +853,7 @@ namespace {
 bool vec_ok(int mode, const StepArgs& a) {
     bool vec = true;
     if (mode & M_REDUCE)
-        vec = vec && (kSplit ? al(a.grads, 8) && (a.row_stride % 4) == 0
-                             : al(a.grads, 16) && (a.row_stride % 8) == 0);
+        vec = vec && al(a.grads, 8) && (a.row_stride % 4) == 0;
     if (mode & (M_ADAM | M_CAST | M_INIT)) vec = vec && al(a.master, 16);
     if (mode & (M_ADAM | M_INIT)) vec = vec && al(a.m, 16) && al(a.v, 16);
     if ((mode & M_INIT) || ((mode & M_ADAM) && !(mode & M_REDUCE))) vec = vec && al(a.g_in, 16);
@@ -969,11 +899,11 @@ int64_t line_head(int mode, const StepArgs& a) {
 hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
     const bool vec = vec_ok(mode, a);
     if (!vec && a.head) return hipErrorInvalidValue;   // the host gives a head to vector launches only
-    const int dv = (mode & M_CAST) ? dst_vec(a.p16) : 8;
+    const int dv = (mode & M_CAST) ? dst_vec(a.p16) : 4;   // (no 16-bit output: unused)
     switch (mode) {
         case M_REDUCE | M_ADAM | M_CAST: return launch_dt<M_REDUCE | M_ADAM | M_CAST>(gdt, pdt, a, vec, dv, s);
-        case M_REDUCE | M_GOUT: return launch_dt<M_REDUCE | M_GOUT>(gdt, ZSMR_BF16, a, vec, 8, s);
-        case M_ADAM: return launch_mode<ZSMR_BF16, ZSMR_BF16, M_ADAM>(a, vec, 8, s);
+        case M_REDUCE | M_GOUT: return launch_dt<M_REDUCE | M_GOUT>(gdt, ZSMR_BF16, a, vec, dv, s);
+        case M_ADAM: return launch_mode<ZSMR_BF16, ZSMR_BF16, M_ADAM>(a, vec, dv, s);
         case M_CAST: return launch_dt<M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
         case M_INIT | M_CAST: return launch_dt<M_INIT | M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
         default: return hipErrorInvalidValue;
