@@ -1,0 +1,46 @@
+"""Host-side parts of bench.py that run without a GPU: the one-GPU refusal,
+the CPU baseline's report, and the source hash that gates the counter
+figures."""
+import os
+import subprocess
+import sys
+import types
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_times_the_oracle_on_a_bounded_sample():
+    w = types.SimpleNamespace(seed=0, world=4, grad_sigma=1e-3, dtype="bf16", steps=2, lr=1e-4,
+                              betas=(0.9, 0.999), eps=1e-8)
+    out = bench.cpu_baseline(w, window=512, min_seconds=0.05)
+    assert out["kind"] == "oracle" and out["unit"] == "params/s" and out["cores"] == 1
+    assert out["value"] > 0
+    assert "window of 512" in out["sample"]
+
+
+def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch):
+    """A counter summary whose recorded hash differs from the current sources
+    gives no traffic figure; a matching one gives its bytes."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    path = prof / "k_w_pmc.txt"
+    path.write_text("# comment: 1\nhbm_bytes_per_launch: 1234\n"
+                    "kernel_and_workload_source_sha256_16: 0000000000000000\n")
+    assert bench.read_traffic("k", "w") is None
+    path.write_text("hbm_bytes_per_launch: 1234\n"
+                    f"kernel_and_workload_source_sha256_16: {bench.kernel_source_hash()}\n")
+    assert bench.read_traffic("k", "w") == 1234
+    assert bench.read_traffic("missing", "w") is None
