@@ -17,9 +17,11 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ast
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,13 +32,30 @@ TRAFFIC_SOURCES = (os.path.join(ROOT, "zero_sharded_mixed_reduce_amd", "csrc", "
                    os.path.join(ROOT, "workloads.py"))
 
 
+def _code_of(path: str) -> str:
+    """A source file's code without its comments (and, for Python, its
+    docstrings), whitespace normalised: what a comment edit leaves alone."""
+    with open(path) as f:
+        src = f.read()
+    if path.endswith(".py"):
+        tree = ast.parse(src)
+        for node in ast.walk(tree):
+            body = getattr(node, "body", None)
+            if (isinstance(body, list) and body and isinstance(body[0], ast.Expr)
+                    and isinstance(body[0].value, ast.Constant) and isinstance(body[0].value.value, str)):
+                node.body = body[1:] or [ast.Pass()]
+        return ast.dump(tree)
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
     """The measured traffic depends on the kernels and on the workloads'
-    buffer layout: hash both sources."""
+    buffer layout: hash the code of both sources (comments aside)."""
     h = hashlib.sha256()
     for path in TRAFFIC_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        h.update(_code_of(path).encode())
     return h.hexdigest()[:16]
 
 
@@ -326,7 +345,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="share64")
     ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
-    ap.add_argument("--copy-bpc", type=int, default=1, help="workgroups per CU, 16-byte copies")
+    ap.add_argument("--copy-bpc", type=int, default=0,
+                    help="burst copies: 0 = one 32 KB burst per wave, k = k workgroups per CU grid-stride")
     ap.add_argument("--defer-tiles", type=int, default=3, help="fused-step tiles kept in LDS per wave (0-5)")
     ap.add_argument("--defer-min-rows", type=int, default=16,
                     help="fewest gradient rows for which the fused step defers its writes")

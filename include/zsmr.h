@@ -277,9 +277,10 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
 
 /* Launch shape: workgroups per compute unit of the step kernels (reduce,
  * Adam, cast, and the fused step when it writes at once; default 2) and of
- * the copies (receive and ZeRO-3 gather; default 1; copies between
- * addresses that differ by an odd number of 2-byte elements run 4 per CU),
- * each 1..64; defer_tiles, 0..5 (default 3): how many completed 512-element
+ * the copies (receive and ZeRO-3 gather), 0..64, where 0 (the default)
+ * gives one 32 KB burst per wave and as many workgroups as the copy needs
+ * (copies between addresses that differ by an odd number of 2-byte elements
+ * run 4 per CU); step_bpc 1..64; defer_tiles, 0..5 (default 3): how many completed 512-element
  * tiles of fused-step results each wave keeps in LDS before it must write
  * them (0 = write at once; without write windows, that is below 16 rows or
  * with windows off, at most 2; with windows and at most 3, two workgroups

@@ -171,7 +171,13 @@ def test_stage3_state_errors_on_the_host():
         z.zsmr_set_launch_shape(2, 4, 6, 32)
     with pytest.raises(z.ZsmrError) as e:
         z.zsmr_set_launch_shape(2, 4, 5, 0)
+    with pytest.raises(z.ZsmrError) as e:
+        z.zsmr_set_launch_shape(2, -1, 3, 16)
+    with pytest.raises(z.ZsmrError) as e:
+        z.zsmr_set_launch_shape(2, 65, 3, 16)
     assert e.value.code == z.ZSMR_ERR_ARG
+    z.zsmr_set_launch_shape(2, 1, 3, 16)      # a grid-stride copy grid
+    z.zsmr_set_launch_shape()                 # back to the defaults (one burst per wave)
 
 
 def test_fused_range_bounds_are_checked_on_the_host():

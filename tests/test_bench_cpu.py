@@ -44,3 +44,20 @@ def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch
                     f"kernel_and_workload_source_sha256_16: {bench.kernel_source_hash()}\n")
     assert bench.read_traffic("k", "w") == 1234
     assert bench.read_traffic("missing", "w") is None
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    hip, py = tmp_path / "k.hip", tmp_path / "w.py"
+    hip.write_text("// a kernel\n__global__ void k(int* p) { p[0] = 1; }  /* tail */\n")
+    py.write_text('"""Doc."""\nX = 1  # comment\n\ndef f():\n    """Doc."""\n    return X\n')
+    monkeypatch.setattr(bench, "TRAFFIC_SOURCES", (str(hip), str(py)))
+    h0 = bench.kernel_source_hash()
+    hip.write_text("// another comment\n__global__ void k(int* p) {\n  p[0] = 1;\n}\n")
+    py.write_text('"""Other doc."""\nX = 1\n\ndef f():\n    return X  # other\n')
+    assert bench.kernel_source_hash() == h0
+    hip.write_text("__global__ void k(int* p) { p[0] = 2; }\n")
+    assert bench.kernel_source_hash() != h0
+    hip.write_text("__global__ void k(int* p) { p[0] = 1; }\n")
+    assert bench.kernel_source_hash() == h0
+    py.write_text("X = 2\n\ndef f():\n    return X\n")
+    assert bench.kernel_source_hash() != h0

@@ -26,7 +26,7 @@ def fused_path(request):
     with the kernel that writes at once; both must give the same bits.  The
     deferred kernel runs only for more than 8 gradient rows; with fewer both
     ids run the direct kernel."""
-    z.zsmr_set_launch_shape(2, 1, request.param, 1)
+    z.zsmr_set_launch_shape(2, 0, request.param, 1)
     yield request.param
     z.zsmr_set_launch_shape()
 
@@ -364,7 +364,7 @@ def test_deferred_kernel_many_rounds(tiles):
     """The deferred-write kernel with each wave's LDS ring filled several
     times over (1,024 waves, about 10 tiles each) and a ragged tail, 9 rows
     (one whole row batch and a batch of one row), against the oracle."""
-    z.zsmr_set_launch_shape(2, 1, tiles, 1)
+    z.zsmr_set_launch_shape(2, 0, tiles, 1)
     try:
         n = 1024 * 10 * 512 + 3 * 512 + 77
         world, T, lr = 9, 2, 1e-3
@@ -390,7 +390,7 @@ def _fused_run(n, rows, T, defer, window, guard=64):
     the device generator; returns the outputs with `guard` untouched
     elements on both sides of every buffer."""
     import synth.gpu as sgpu
-    z.zsmr_set_launch_shape(2, 1, defer, 1)
+    z.zsmr_set_launch_shape(2, 0, defer, 1)
     z.zsmr_set_write_window(*window)
     try:
         stride = n + 24
@@ -541,11 +541,21 @@ def test_gather_copy_alignments():
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 16_383, 16_384, 16_385, 3 * 16_384 + 5,
                                (1 << 24) + 777, 256 * 4 * 2 * 16_384 + 3])
 @pytest.mark.parametrize("off", [0, 3, 40])     # 40: a 24-element head to a 128-byte line
-def test_burst_copy_sizes(n, off):
+@pytest.mark.parametrize("shape", [0, 1, 3])   # one burst per wave; grid-stride 1 and 3 per CU
+def test_burst_copy_sizes(n, off, shape):
     """The 16-byte copy moves 2,048-vector chunks per wave (16,384 elements);
     sizes around one chunk, several chunks per wave and a partial last chunk,
-    with a head (off = 3: equal misalignment of source and destination)."""
-    say(f"[copy] n={n} off={off}")
+    with a head (off = 3: equal misalignment of source and destination), in
+    the default one-burst-per-wave grid and in grid-stride grids."""
+    say(f"[copy] n={n} off={off} shape={shape}")
+    z.zsmr_set_launch_shape(2, shape, 3, 16)
+    try:
+        _copy_case(n, off)
+    finally:
+        z.zsmr_set_launch_shape()
+
+
+def _copy_case(n, off):
     rng = np.random.default_rng(n + off)
     src = rng.integers(0, 1 << 16, n + 2 * off + 16, dtype=np.uint16)
     ctx = z.zero_init_shards(64, 2, 2, "bf16")

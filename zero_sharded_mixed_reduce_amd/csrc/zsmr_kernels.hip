@@ -54,11 +54,20 @@ constexpr int kThreads = 256;
 constexpr int kRowBatch = ZSMR_ROW_BATCH;
 constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // workgroups per compute unit of the grid-stride launches (measured on
-// MI355X: the step kernel streams best with 2, the burst copies with 1; the
-// 2-byte copies run 4 per CU)
+// MI355X: the step kernel streams best with 2; the 2-byte copies run 4 per
+// CU)
 int g_step_bpc = 2;
-int g_copy_bpc = 1;
 constexpr int kNarrowCopyBpc = 4;
+// The burst copies (receive and ZeRO-3 gather): 0 = one 32 KB burst per wave,
+// as many workgroups as the copy needs, handed out by the hardware in order as
+// earlier ones finish; k > 0 = a grid-stride grid of k workgroups per CU.
+// Measured on MI355X (each pair on one box): a 14.77 GB copy between fresh
+// buffers, one burst per wave 6.22 TB/s against 6.07 grid-stride at 1 per
+// CU; the share64 receive 6.00-6.03 against 5.82-5.84 (2 per CU 5.84-5.86,
+// 4 per CU 5.94-5.96).  The in-order
+// hand-out keeps the chunks in flight one contiguous window and leaves no
+// straggling waves at the end.
+int g_copy_bpc = 0;
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
 // write windows (0 = write at once with step_vec8_kernel).  With windows and
 // a ring of at most 3 tiles (72 KB per workgroup), two workgroups run per CU
@@ -925,6 +934,15 @@ hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream
     return hipSuccess;
 }
 
+// Workgroups of a burst copy whose lanes have `lane_bursts` bursts of work:
+// one burst per lane (one chunk per wave) by default, else the grid-stride
+// grid of g_copy_bpc workgroups per CU.
+static unsigned copy_blocks(int64_t lane_bursts) {
+    if (g_copy_bpc > 0) return grid_for(lane_bursts, g_copy_bpc);
+    const int64_t blocks = (lane_bursts + kThreads - 1) / kThreads;
+    return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
+}
+
 static int copy_width(uintptr_t a, uintptr_t b) {
     const uintptr_t d = a > b ? a - b : b - a;
     if (d % 16 == 0) return 16;
@@ -951,7 +969,7 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
     const int64_t head = head_for(dst, w, n);
     const int64_t vecs = (n - head) / (w / 2) + 1;
-    const dim3 grid(w >= 4 ? grid_for(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
+    const dim3 grid(w >= 4 ? copy_blocks(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1)
                            : grid_for(vecs, kNarrowCopyBpc));
     switch (w) {
         case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
@@ -981,11 +999,14 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
             g.head[i] = head_for(g.dst + (int64_t)i * each, w, each);
         }
         const int64_t per = each / (w / 2) + 1;
-        const int64_t cap = (int64_t)cu_count() * (w >= 4 ? g_copy_bpc : kNarrowCopyBpc);
         const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
         int64_t bx = (units + kThreads - 1) / kThreads;
-        const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
-        if (bx > lim) bx = lim;
+        const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
+        if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all sources
+            const int64_t cap = (int64_t)cu_count() * bpc;
+            const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
+            if (bx > lim) bx = lim;
+        }
         if (bx < 1) bx = 1;
         const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(cnt));
         switch (w) {
