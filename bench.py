@@ -344,11 +344,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="share64")
-    ap.add_argument("--step-bpc", type=int, default=2, help="workgroups per CU, step kernels")
+    ap.add_argument("--step-bpc", type=int, default=0,
+                    help="step kernels: 0 = one wave tile per wave, k = k workgroups per CU grid-stride")
     ap.add_argument("--copy-bpc", type=int, default=0,
                     help="burst copies: 0 = one 32 KB burst per wave, k = k workgroups per CU grid-stride")
     ap.add_argument("--defer-tiles", type=int, default=3, help="fused-step tiles kept in LDS per wave (0-5)")
-    ap.add_argument("--defer-min-rows", type=int, default=16,
+    ap.add_argument("--defer-min-rows", type=int, default=24,
                     help="fewest gradient rows for which the fused step defers its writes")
     ap.add_argument("--window-cycle-ns", type=int, default=None,
                     help="fused step: write-window cycle (0 = no windows)")

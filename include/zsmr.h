@@ -275,17 +275,19 @@ int32_t zero_stage3_unit_release(zsmr_ctx* ctx, int32_t unit);
 int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
                                int64_t* gathers, int64_t* releases);
 
-/* Launch shape: workgroups per compute unit of the step kernels (reduce,
- * Adam, cast, and the fused step when it writes at once; default 2) and of
- * the copies (receive and ZeRO-3 gather), 0..64, where 0 (the default)
- * gives one 32 KB burst per wave and as many workgroups as the copy needs
- * (copies between addresses that differ by an odd number of 2-byte elements
- * run 4 per CU); step_bpc 1..64; defer_tiles, 0..5 (default 3): how many completed 512-element
- * tiles of fused-step results each wave keeps in LDS before it must write
- * them (0 = write at once; without write windows, that is below 16 rows or
- * with windows off, at most 2; with windows and at most 3, two workgroups
- * run per CU); and defer_min_rows >= 1 (default 16): the fewest gradient
- * rows for which the fused step defers its writes.
+/* Launch shape.  step_bpc, 0..64: the grid of the step kernels (reduce,
+ * Adam, cast, and the fused step when it writes at once), where 0 (the
+ * default) gives one 512-element wave tile per wave and as many workgroups
+ * as the launch needs, and k > 0 a grid-stride grid of k workgroups per
+ * compute unit.  copy_bpc, 0..64: the same for the copies (receive and
+ * ZeRO-3 gather), 0 giving one 32 KB burst per wave (copies between
+ * addresses that differ by an odd number of 2-byte elements run 4 per CU
+ * whatever it is).  defer_tiles, 0..5 (default 3): how many completed
+ * 512-element tiles of fused-step results each wave keeps in LDS before it
+ * must write them (0 = write at once; without write windows, that is below
+ * 16 rows or with windows off, at most 2; with windows and at most 3, two
+ * workgroups run per CU).  defer_min_rows >= 1 (default 24): the fewest
+ * gradient rows for which the fused step defers its writes.
  * Process-wide.  Affects speed only, never results. */
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows);

@@ -166,7 +166,9 @@ def test_stage3_state_errors_on_the_host():
         z.zero_stage3_unit_release(nz, 0)
     assert e.value.code == z.ZSMR_ERR_ARG
     with pytest.raises(z.ZsmrError) as e:
-        z.zsmr_set_launch_shape(0, 4, 5, 32)
+        z.zsmr_set_launch_shape(-1, 4, 5, 32)
+    with pytest.raises(z.ZsmrError) as e:
+        z.zsmr_set_launch_shape(65, 4, 5, 32)
     with pytest.raises(z.ZsmrError) as e:
         z.zsmr_set_launch_shape(2, 4, 6, 32)
     with pytest.raises(z.ZsmrError) as e:

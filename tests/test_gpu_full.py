@@ -159,7 +159,7 @@ def test_piece_larger_than_one_launch(defer):
     around the cut and at the ends."""
     import synth
     import synth.gpu as sgpu
-    z.zsmr_set_launch_shape(2, 0, defer, 1)
+    z.zsmr_set_launch_shape(0, 0, defer, 1)
     try:
         n, world, T, lr = (1 << 30) + 1029, 9, 2, 1e-3
         say(f"[full] piece over 2^30: n={n} defer={defer}")

@@ -26,7 +26,7 @@ def fused_path(request):
     with the kernel that writes at once; both must give the same bits.  The
     deferred kernel runs only for more than 8 gradient rows; with fewer both
     ids run the direct kernel."""
-    z.zsmr_set_launch_shape(2, 0, request.param, 1)
+    z.zsmr_set_launch_shape(0, 0, request.param, 1)
     yield request.param
     z.zsmr_set_launch_shape()
 
@@ -260,6 +260,37 @@ def test_alignment_variants(shift16, shift32, gshift, n, fused_path):
     assert not host32(mb)[:s].any() and not host32(mb)[s + n:].any()
 
 
+
+@pytest.mark.parametrize("shape", [0, 1, 2, 5])
+@pytest.mark.parametrize("n", [512 * 300 + 77, 512 * 4000 + 5])
+def test_step_grid_shapes(shape, n):
+    """The step kernels' grid (one wave tile per wave, or grid-stride with
+    1, 2 or 5 workgroups per CU) changes nothing: the fused step (direct
+    kernel, 6 rows) and the reduce, Adam and cast launches all match the
+    oracle, with heads (the piece 24 elements into a line) and tails."""
+    world, gdt, lr, off = 6, "bf16", 1e-3, 24
+    say(f"[step grid] shape={shape} n={n}")
+    z.zsmr_set_launch_shape(shape, 0, 3, 16)
+    try:
+        rows, theta, G, stride, th, mb, mm, vb, gb, pb = _line_buffers(n, world, gdt, off, off, off)
+        ctx = z.zero_init_shards(n * world, world, 2, gdt)
+        z.zero_init_state(ctx, 0, 0, th[off:], mb[off:], mm[off:], vb[off:], pb[off:])
+        for t in (1, 2):
+            z.zero_fused_step(ctx, 0, 0, G[off:], stride, 0, mb[off:], mm[off:], vb[off:], pb[off:], t, lr)
+        z.zero_reduce_shard(ctx, 0, 0, G[off:], stride, 0, True, gb[off:])
+        z.zero_adam_step(mb[off:], mm[off:], vb[off:], gb[off:], n, 3, lr)
+        z.zero_gather_cast(ctx, 0, 0, mb[off:], pb[off:])
+        torch.cuda.synchronize()
+    finally:
+        z.zsmr_set_launch_shape()
+    master, m, v, p16 = _oracle_piece(rows, theta, gdt, gdt, 3, lr)
+    got16 = host16(pb)
+    compare({"master": host32(mb)[off:off + n], "m": host32(mm)[off:off + n], "v": host32(vb)[off:off + n]},
+            {"master": master, "m": m, "v": v}, got16[off:off + n], p16, f"step grid shape={shape} n={n}")
+    assert not got16[:off].any() and not got16[off + n:].any()
+    for b in (mb, mm, vb):
+        assert not host32(b)[:off].any() and not host32(b)[off + n:].any()
+
 # (gradient rows, fp32 state, 16-bit copy) offsets in elements from a 128-byte line
 LINE_OFFSETS = [
     (0, 0, 0),
@@ -364,7 +395,7 @@ def test_deferred_kernel_many_rounds(tiles):
     """The deferred-write kernel with each wave's LDS ring filled several
     times over (1,024 waves, about 10 tiles each) and a ragged tail, 9 rows
     (one whole row batch and a batch of one row), against the oracle."""
-    z.zsmr_set_launch_shape(2, 0, tiles, 1)
+    z.zsmr_set_launch_shape(0, 0, tiles, 1)
     try:
         n = 1024 * 10 * 512 + 3 * 512 + 77
         world, T, lr = 9, 2, 1e-3
@@ -390,7 +421,7 @@ def _fused_run(n, rows, T, defer, window, guard=64):
     the device generator; returns the outputs with `guard` untouched
     elements on both sides of every buffer."""
     import synth.gpu as sgpu
-    z.zsmr_set_launch_shape(2, 0, defer, 1)
+    z.zsmr_set_launch_shape(0, 0, defer, 1)
     z.zsmr_set_write_window(*window)
     try:
         stride = n + 24
@@ -548,7 +579,7 @@ def test_burst_copy_sizes(n, off, shape):
     with a head (off = 3: equal misalignment of source and destination), in
     the default one-burst-per-wave grid and in grid-stride grids."""
     say(f"[copy] n={n} off={off} shape={shape}")
-    z.zsmr_set_launch_shape(2, shape, 3, 16)
+    z.zsmr_set_launch_shape(0, shape, 3, 16)
     try:
         _copy_case(n, off)
     finally:

@@ -299,8 +299,8 @@ def zero_stage3_unit_state(ctx: Ctx, unit: int):
     return bool(live.value), g.value, r.value
 
 
-def zsmr_set_launch_shape(step_bpc: int = 2, copy_bpc: int = 0, defer_tiles: int = 3,
-                          defer_min_rows: int = 16) -> None:
+def zsmr_set_launch_shape(step_bpc: int = 0, copy_bpc: int = 0, defer_tiles: int = 3,
+                          defer_min_rows: int = 24) -> None:
     _check(_lib().zsmr_set_launch_shape(int(step_bpc), int(copy_bpc), int(defer_tiles),
                                         int(defer_min_rows)), "zsmr_set_launch_shape")
 

@@ -659,7 +659,7 @@ int32_t zero_unit_owner(const zsmr_ctx* c, int32_t unit, int32_t* owner) {
 
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows) {
-    if (step_bpc < 1 || step_bpc > 64 || copy_bpc < 0 || copy_bpc > 64 || defer_tiles < 0 ||
+    if (step_bpc < 0 || step_bpc > 64 || copy_bpc < 0 || copy_bpc > 64 || defer_tiles < 0 ||
         defer_tiles > 5 || defer_min_rows < 1)
         return ZSMR_ERR_ARG;
     zsmr::set_launch_shape(step_bpc, copy_bpc, defer_tiles, defer_min_rows);

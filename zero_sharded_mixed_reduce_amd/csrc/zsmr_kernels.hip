@@ -53,20 +53,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kRowBatch = ZSMR_ROW_BATCH;
 constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
-// workgroups per compute unit of the grid-stride launches (measured on
-// MI355X: the step kernel streams best with 2; the 2-byte copies run 4 per
-// CU)
-int g_step_bpc = 2;
-constexpr int kNarrowCopyBpc = 4;
-// The burst copies (receive and ZeRO-3 gather): 0 = one 32 KB burst per wave,
-// as many workgroups as the copy needs, handed out by the hardware in order as
-// earlier ones finish; k > 0 = a grid-stride grid of k workgroups per CU.
-// Measured on MI355X (each pair on one box): a 14.77 GB copy between fresh
-// buffers, one burst per wave 6.22 TB/s against 6.07 grid-stride at 1 per
-// CU; the share64 receive 6.00-6.03 against 5.82-5.84 (2 per CU 5.84-5.86,
-// 4 per CU 5.94-5.96).  The in-order
-// hand-out keeps the chunks in flight one contiguous window and leaves no
-// straggling waves at the end.
+// Grids.  0 = one unit of work per thread (a wave tile per wave for the step
+// kernels, a 32 KB burst per wave for the copies), as many workgroups as the
+// launch needs, handed out by the hardware in order as earlier ones finish:
+// the work in flight stays one contiguous window and no waves straggle at
+// the end.  k > 0 = a grid-stride grid of k workgroups per CU.
+// The direct step kernel, measured on MI355X (each pair on one box), one
+// tile per wave against 2 per CU grid-stride: 4 rows 5.89 against 5.28
+// TB/s, 8 rows 5.87-5.91 against 5.53, 12 rows 6.14-6.19 against 5.45;
+// GPT-2 small's 15.5M-element shard at 8 rows 6.05-6.09 against 5.62-5.69.
+int g_step_bpc = 0;
+constexpr int kNarrowCopyBpc = 4;   // the 2-byte copies: 4 per CU
+// The burst copies (receive and ZeRO-3 gather), measured the same way: a
+// 14.77 GB copy between fresh buffers, one burst per wave 6.22 TB/s against
+// 6.07 grid-stride at 1 per CU; the share64 receive 6.00-6.03 against
+// 5.82-5.84 (2 per CU 5.84-5.86, 4 per CU 5.94-5.96).
 int g_copy_bpc = 0;
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
 // write windows (0 = write at once with step_vec8_kernel).  With windows and
@@ -77,12 +78,13 @@ int g_copy_bpc = 0;
 // workgroup per CU is 5% faster (16-24 rows).
 int g_defer_tiles = 3;
 constexpr int kRingTwoPerCu = 3;
-// ... used when a step reduces at least this many rows.  Measured on MI355X
-// against the direct kernel: single long launches at 16 rows +7%, 24 rows
-// +8.5%, 64 rows +22% (with windows); the 1.558e9-element, 16-rank world
-// +7-9% per step; but the 8-rank worlds, whose steps are many short
-// launches, 2-4% slower, and 1-2 rows 5% slower.
-int g_defer_min_rows = 16;
+// ... used when a step reduces at least this many rows.  Measured on MI355X,
+// one box, 97,375,000 elements, against the direct kernel with one tile per
+// wave: 16 rows 5.57-5.62 against 5.74-5.81 TB/s, 20 rows 5.62-5.64 against
+// 5.90-5.99, 24 rows 5.99-6.09 against 5.66-5.69, 32 rows 6.12-6.15 against
+// 5.48-5.50, 64 rows 6.05 against 5.29; the 1.558e9-element, 16-rank world
+// 16.94 against 15.96-15.99 ms per step.
+int g_defer_min_rows = 24;
 // without windows the ring holds at most this many tiles: smaller bursts at
 // ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
 constexpr int kRingWithoutWindows = 2;
@@ -741,10 +743,11 @@ int cu_count() {
     return cus;
 }
 
+// Workgroups for `work_items` threads' worth of work: all of them (bpc 0),
+// or at most bpc per CU, each thread then striding over several items.
 unsigned grid_for(int64_t work_items, int bpc) {
-    const int64_t cap = (int64_t)cu_count() * bpc;
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
-    if (blocks > cap) blocks = cap;
+    if (bpc > 0 && blocks > (int64_t)cu_count() * bpc) blocks = (int64_t)cu_count() * bpc;
     if (blocks < 1) blocks = 1;
     return static_cast<unsigned>(blocks);
 }
@@ -934,15 +937,6 @@ hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream
     return hipSuccess;
 }
 
-// Workgroups of a burst copy whose lanes have `lane_bursts` bursts of work:
-// one burst per lane (one chunk per wave) by default, else the grid-stride
-// grid of g_copy_bpc workgroups per CU.
-static unsigned copy_blocks(int64_t lane_bursts) {
-    if (g_copy_bpc > 0) return grid_for(lane_bursts, g_copy_bpc);
-    const int64_t blocks = (lane_bursts + kThreads - 1) / kThreads;
-    return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
-}
-
 static int copy_width(uintptr_t a, uintptr_t b) {
     const uintptr_t d = a > b ? a - b : b - a;
     if (d % 16 == 0) return 16;
@@ -969,7 +963,7 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
     const int64_t head = head_for(dst, w, n);
     const int64_t vecs = (n - head) / (w / 2) + 1;
-    const dim3 grid(w >= 4 ? copy_blocks(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1)
+    const dim3 grid(w >= 4 ? grid_for(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
                            : grid_for(vecs, kNarrowCopyBpc));
     switch (w) {
         case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
