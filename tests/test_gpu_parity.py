@@ -455,11 +455,11 @@ WINDOWS = {
 
 @pytest.mark.parametrize("window", list(WINDOWS), ids=list(WINDOWS))
 @pytest.mark.parametrize("kd", [1, 2, 5])
-@pytest.mark.parametrize("rows", [1, 4, 8, 9, 16, 33, 64])
+@pytest.mark.parametrize("rows", [1, 4, 5, 8, 9, 16, 33, 64])
 def test_deferred_windows_match_direct_bits(window, kd, rows):
     """Write windows and ring sizes change only when results are stored:
     the deferred kernel gives the direct kernel's bits, and writes nothing
-    outside the piece.  With 8 rows or fewer a tile is one row batch (its
+    outside the piece.  With 4 rows or fewer a tile is one row batch (its
     first and last); windows apply from 16 rows, their cycle scaled to the
     row count."""
     n = 1024 * 6 * 512 + 2 * 512 + 131           # ~6 tiles per wave, a ragged tail

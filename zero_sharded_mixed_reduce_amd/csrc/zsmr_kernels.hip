@@ -33,8 +33,16 @@
 #ifndef ZSMR_NT_STORE
 #define ZSMR_NT_STORE 1         // non-temporal stores
 #endif
+// Gradient rows per double-buffered load batch.  Measured on MI355X,
+// alternating processes on one box: the deferred-write kernel on share64
+// (tuned windows) 2.694-2.730 ms with 4 against 2.742-2.769 with 8 (154
+// against 184 VGPRs); the direct kernel with 12 instead of 8: 97M-element
+// pieces at 8 and 16 rows +3%, but GPT-2 small's 15.5M-element shard -3%.
 #ifndef ZSMR_ROW_BATCH
-#define ZSMR_ROW_BATCH 8        // gradient rows in flight per lane
+#define ZSMR_ROW_BATCH 8        // direct kernel
+#endif
+#ifndef ZSMR_DEFER_BATCH
+#define ZSMR_DEFER_BATCH 4      // deferred-write kernel
 #endif
 #ifndef ZSMR_COPY_UNROLL
 #define ZSMR_COPY_UNROLL 1      // vectors in flight per lane in the 2-byte copy
@@ -52,6 +60,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRowBatch = ZSMR_ROW_BATCH;
+constexpr int kDeferBatch = ZSMR_DEFER_BATCH;
 constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // Grids.  0 = one unit of work per thread (a wave tile per wave for the step
 // kernels, a 32 KB burst per wave for the copies), as many workgroups as the
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
     const uint32_t nw = gridDim.x * kWaves;
     const uint32_t wid = blockIdx.x * kWaves + wv;
     const uint32_t mine = wid < tiles ? (tiles - 1 - wid) / nw + 1 : 0;
-    const uint32_t bps = (static_cast<uint32_t>(a.nrows) + kRowBatch - 1) / kRowBatch;
+    const uint32_t bps = (static_cast<uint32_t>(a.nrows) + kDeferBatch - 1) / kDeferBatch;
     const uint32_t nb = mine * bps;
     auto tile_of = [&](uint32_t j) { return (wid + j * nw) * 512u; };
 
@@ -537,17 +546,17 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
     struct State {
         float w[8], m[8], v[8];
     };
-    u32x4 bufA[kRowBatch], bufB[kRowBatch];
+    u32x4 bufA[kDeferBatch], bufB[kDeferBatch];
     State stA, stB;
     float g[8];
     auto issue = [&](u32x4* buf, State& st) {
         const uint32_t e0 = tile_of(i_tile) + lane * 8u, off = e0 * 2u;
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
+        for (int k = 0; k < kDeferBatch; ++k) {
             buf[k] = ld(reinterpret_cast<const u32x4*>(i_ptr + off));
             if (i_row + k + 1 < nrows) i_ptr += stride_b;
         }
-        i_row += kRowBatch;
+        i_row += kDeferBatch;
         if (i_row >= nrows) {      // the tile's last batch: its master/m/v come with it
             Groups::load32(a.master, e0, e0 + 4u, st.w);   // contiguous map
             Groups::load32(a.m, e0, e0 + 4u, st.m);
@@ -559,10 +568,10 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
     };
     auto consume = [&](const u32x4* buf, State& st) {
         // rows in rank order; the tile's sum starts from row 0 itself (for
-        // N <= 8 a tile's one batch is both its first and its last)
-        const bool full = c_row + kRowBatch <= nrows;
+        // N <= kDeferBatch a tile's one batch is both its first and its last)
+        const bool full = c_row + kDeferBatch <= nrows;
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
+        for (int k = 0; k < kDeferBatch; ++k) {
             if (full || c_row + k < nrows) {
                 float t[8];
                 unpack8<GDT>(buf[k], t);
@@ -575,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, 
                 }
             }
         }
-        c_row += kRowBatch;
+        c_row += kDeferBatch;
         if (c_row < nrows) return;
         c_row = 0;
         if (a.mean) {
