@@ -586,6 +586,30 @@ def test_burst_copy_sizes(n, off, shape):
         z.zsmr_set_launch_shape()
 
 
+@pytest.mark.parametrize("n", [100, 3 * 16_384 + 5, (1 << 20) + 77])
+@pytest.mark.parametrize("grid_off", [0, 128, 18_304, 65_536 - 128, 131_072 - 128])
+def test_copy_chunk_grid_offsets(n, grid_off):
+    """The burst copy lays its 32 KB chunks out from the destination's 128 KB
+    boundary below the vector body: destinations at chosen distances past
+    such a boundary (partial first chunks of every size), small and large
+    copies, a source at another offset modulo 128 KB; bytes exact, nothing
+    outside written."""
+    say(f"[copy grid] n={n} grid_off={grid_off}")
+    ctx = z.zero_init_shards(64, 2, 2, "bf16")
+    rng = np.random.default_rng(n + grid_off)
+    src = rng.integers(0, 1 << 16, n + 4096, dtype=np.uint16)
+    S = dev16(src)
+    D = torch.zeros(n + (1 << 17), dtype=torch.int16, device="cuda")
+    # element offset putting D[off] grid_off bytes past a 128 KB boundary
+    off = ((grid_off - D.data_ptr()) % (1 << 17)) // 2
+    soff = 1000                                   # source 16-byte aligned like the destination
+    soff += ((D.data_ptr() + 2 * off) - (S.data_ptr() + 2 * soff)) % 16 // 2
+    z.zero_gather_copy(ctx, 1, S[soff:], D[off:], n)
+    torch.cuda.synchronize()
+    got = host16(D)
+    assert np.array_equal(got[off:off + n], src[soff:soff + n])
+    assert not got[:off].any() and not got[off + n:].any()
+
 def _copy_case(n, off):
     rng = np.random.default_rng(n + off)
     src = rng.integers(0, 1 << 16, n + 2 * off + 16, dtype=np.uint16)

@@ -656,10 +656,12 @@ struct VecOf<2> { typedef uint16_t T; };
 // Copy n elements: `head` scalar elements bring dst (and src, which has the
 // same alignment modulo W) to a W-byte boundary, then W-byte vectors, then
 // the scalar tail.  Workgroup `part` of `parts` takes its share of the
-// vectors.
+// vectors.  The burst copies lay their chunks out from `pre` vectors before
+// the vector body (the body's offset from dst's last 128 KB boundary), so
+// that every whole chunk, and every workgroup's four, sits on that grid.
 template <int W>
 __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, int64_t n,
-                                           int64_t head, int64_t part, int64_t parts) {
+                                           int64_t head, int64_t pre, int64_t part, int64_t parts) {
     typedef typename VecOf<W>::T V;
     constexpr int E = W / 2;
     const int64_t nb = (n - head) / E;
@@ -670,17 +672,19 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
         // Register bursts: each wave loads kBurst vectors per lane (32 KB per
         // wave) before it stores any, so every wave alternates a read burst
         // and a write burst; wave w of the launch takes chunks w, w + waves,
-        // ... (neighbouring waves, neighbouring chunks).  The last, partial
-        // chunk goes one guarded vector at a time.
+        // ... (neighbouring waves, neighbouring chunks).  Chunk c covers body
+        // vectors [c * chunk - pre, (c + 1) * chunk - pre); the partial first
+        // and last chunks go one guarded vector at a time.
         constexpr int kBurst = ZSMR_COPY_BURST_BYTES / W;
-        constexpr uint64_t chunk = (uint64_t)kBurst * 64;
-        const uint64_t lane = threadIdx.x & 63u;
-        const uint64_t waves = (uint64_t)parts * (kThreads / 64);
-        const uint64_t wid = (uint64_t)part * (kThreads / 64) + (threadIdx.x >> 6);
-        const uint64_t nv = static_cast<uint64_t>(nb);
-        for (uint64_t c = wid; c * chunk < nv; c += waves) {
-            const uint64_t base = c * chunk + lane;
-            if (base + (chunk - 64) < nv) {
+        constexpr int64_t chunk = (int64_t)kBurst * 64;
+        const int64_t lane = threadIdx.x & 63u;
+        const int64_t waves = parts * (kThreads / 64);
+        const int64_t wid = part * (kThreads / 64) + (threadIdx.x >> 6);
+        const int64_t nv = nb;
+        for (int64_t c = wid; c * chunk < nv + pre; c += waves) {
+            const int64_t first = c * chunk - pre;   // the chunk's first body vector (may be < 0)
+            const int64_t base = first + lane;
+            if (first >= 0 && first + chunk <= nv) {
                 V r[kBurst];
 #pragma unroll
                 for (int i = 0; i < kBurst; ++i) r[i] = ld(s + base + i * 64);
@@ -688,8 +692,10 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
 #pragma unroll
                 for (int i = 0; i < kBurst; ++i) st(d + base + i * 64, r[i]);
             } else {
-                for (int i = 0; i < kBurst; ++i)
-                    if (base + i * 64 < nv) st(d + base + i * 64, ld(s + base + i * 64));
+                for (int i = 0; i < kBurst; ++i) {
+                    const int64_t v = base + i * 64;
+                    if (v >= 0 && v < nv) st(d + v, ld(s + v));
+                }
             }
         }
     } else {
@@ -720,14 +726,15 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
 
 template <int W>
 __global__ __launch_bounds__(kThreads) void copy16_kernel(const uint16_t* src, uint16_t* dst,
-                                                          int64_t n, int64_t head) {
-    copy_range<W>(src, dst, n, head, blockIdx.x, gridDim.x);
+                                                          int64_t n, int64_t head, int64_t pre) {
+    copy_range<W>(src, dst, n, head, pre, blockIdx.x, gridDim.x);
 }
 
 constexpr int kMaxGather = 64;
 struct GatherArgs {
     const uint16_t* src[kMaxGather];
     int64_t head[kMaxGather];
+    int64_t pre[kMaxGather];
     uint16_t* dst;
     int64_t each;
 };
@@ -735,7 +742,8 @@ struct GatherArgs {
 template <int W>
 __global__ __launch_bounds__(kThreads) void gather16_kernel(GatherArgs g) {
     const int r = blockIdx.y;
-    copy_range<W>(g.src[r], g.dst + (int64_t)r * g.each, g.each, g.head[r], blockIdx.x, gridDim.x);
+    copy_range<W>(g.src[r], g.dst + (int64_t)r * g.each, g.each, g.head[r], g.pre[r], blockIdx.x,
+                  gridDim.x);
 }
 
 // ------------------------------------------------------------------ host --
@@ -967,18 +975,32 @@ static int64_t head_for(const void* dst, int w, int64_t n) {
     return h < n ? h : n;
 }
 
+// Vectors between dst's last 128 KB boundary and the burst copy's vector body
+// (dst + head), where the chunk grid starts (0 for the 2-byte copy).  128 KB
+// is one workgroup's four 32 KB bursts.  Measured on MI355X, a 14.77 GB copy
+// with source and destination shifted alike: 6.22-6.25 TB/s at multiples of
+// 128 KB, 6.15-6.19 at 4-8 KB past one, 6.01-6.04 at 18 KB, 5.87-5.91 at 32-64
+// KB (destination alone at 64 KB: 5.99; source alone: 6.13).
+static int64_t pre_for(const void* dst, int w, int64_t head) {
+    constexpr uintptr_t kGrid = 128 * 1024;
+    if (w < 4) return 0;
+    const uintptr_t body = reinterpret_cast<uintptr_t>(dst) + static_cast<uintptr_t>(head) * 2;
+    return static_cast<int64_t>(body % kGrid / static_cast<uintptr_t>(w));
+}
+
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
     const int64_t head = head_for(dst, w, n);
+    const int64_t pre = pre_for(dst, w, head);
     const int64_t vecs = (n - head) / (w / 2) + 1;
-    const dim3 grid(w >= 4 ? grid_for(vecs / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
+    const dim3 grid(w >= 4 ? grid_for((vecs + pre) / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
                            : grid_for(vecs, kNarrowCopyBpc));
     switch (w) {
-        case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
-        case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
-        case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
-        default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head); break;
+        case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
+        case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
+        case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
+        default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
     }
     return hipGetLastError();
 }
@@ -997,11 +1019,14 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
                                       reinterpret_cast<uintptr_t>(g.dst + (int64_t)i * each));
             if (wi < w) w = wi;
         }
+        int64_t pre_max = 0;
         for (int32_t i = 0; i < cnt; ++i) {
             g.src[i] = srcs[r0 + i];
             g.head[i] = head_for(g.dst + (int64_t)i * each, w, each);
+            g.pre[i] = pre_for(g.dst + (int64_t)i * each, w, g.head[i]);
+            if (g.pre[i] > pre_max) pre_max = g.pre[i];
         }
-        const int64_t per = each / (w / 2) + 1;
+        const int64_t per = each / (w / 2) + 1 + pre_max;
         const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
         int64_t bx = (units + kThreads - 1) / kThreads;
         const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
