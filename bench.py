@@ -9,8 +9,10 @@ resident in HBM before timing starts.
 
 Prints one JSON line: params/s (owned fp32 elements updated per second),
 the roofline of the dominant kernel (algorithmic bytes / average launch time
-from HIP events on the launch stream, against 8 TB/s), and the CPU oracle
-timed on a bounded sample of the same workload.
+from HIP events on the launch stream, against 8 TB/s), each part's time
+against the least time its reads and writes could take at the pure read and
+write rates this device shows in the same run (``phased_bound``), and the
+CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload share64|gpt2s|gpt2xl|llama8b]
 """
@@ -28,6 +30,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 METRIC = "fused ZeRO shard-step params/sec and achieved HBM GB/s (% of peak), 1 GPU"
+# the pure-rate references run on buffers of the share64 receive's size (63
+# peer slices of 117,187,500 bf16 elements), rounded down to 16 bytes
+REFERENCE_BYTES = 14_765_624_992
 TRAFFIC_SOURCES = (os.path.join(ROOT, "zero_sharded_mixed_reduce_amd", "csrc", "zsmr_kernels.hip"),
                    os.path.join(ROOT, "workloads.py"))
 
@@ -169,11 +174,13 @@ def tune_write_window(share, reps: int = 6) -> dict:
             "tuned_over": n}
 
 
-def copy_reference(z, nbytes: int, reps: int = 5) -> float:
-    """GB/s (read + write) of the library's 128-bit copy between two fresh,
-    equally aligned buffers of ``nbytes``, measured in the same process: the
-    rate this machine gives a plain copy of the receive's size."""
+def references(z, nbytes: int, reps: int = 5) -> dict:
+    """Rates this device gives simple streams of the receive's size, measured
+    in the same process on two fresh, equally aligned buffers of ``nbytes``:
+    the library's 128-bit copy (GB/s of reads + writes), and the best pure
+    read and pure write rates of the reference streams in ``ceiling/``."""
     import torch
+    import ceiling
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     ctx = z.zero_init_shards(2, 2, 2, "bf16")
@@ -188,9 +195,24 @@ def copy_reference(z, nbytes: int, reps: int = 5) -> float:
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    pure = ceiling.measure(dst, nbytes, reps)
     del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / ms / 1e6
+    return {"copy_GBps": 2 * nbytes / ms / 1e6, "pure": pure}
+
+
+def phased(parts: dict, rw: dict, pure: dict) -> dict:
+    """Each part's time against the least time its reads and writes could take
+    at this device's pure read and write rates (``ceiling.phased_bound``)."""
+    import ceiling
+    out = {"read_GBps": pure["read_GBps"], "write_GBps": pure["write_GBps"],
+           "read_shapes_GBps": pure["read"], "write_shapes_GBps": pure["write"],
+           "reference_bytes": pure["bytes"]}
+    for name, (rb, wb, ms) in rw.items():
+        bound = ceiling.phased_bound(rb, wb, pure["read_GBps"], pure["write_GBps"])
+        out[name] = {"read_bytes": rb, "write_bytes": wb, "bound_ms": round(bound, 4),
+                     "measured_ms": round(ms, 4), "frac": round(bound / ms, 4)}
+    return out
 
 
 def bucketed_overlap(share, args, reps: int = 5) -> dict:
@@ -286,7 +308,10 @@ def bench_share64(args, w):
                   "unit": "GB/s", "frac": parts["fused_step"]["frac"],
                   "traffic": read_traffic(fused_kernel, w.key), "kernel": fused_kernel,
                   "algorithmic_bytes_per_launch": fused_bytes}
-    return S / (ms_step / 1e3), ms_step, roof, roof_fused, parts, {
+    half = recv_bytes // 2
+    rw = {"fused_step": (S * (2 * N + 12), 14 * S, fused_ms), "peer_receive": (half, half, recv_ms),
+          "step": (S * (2 * N + 12) + half, 14 * S + half, ms_step)}
+    return S / (ms_step / 1e3), ms_step, roof, roof_fused, parts, rw, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "owned_shard": S,
         "grad_dtype": w.dtype, "working_copy_elems": share.P, "steps_T": w.steps, "lr": w.lr,
         "rank": 0, "step_workgroups_per_cu": args.step_bpc,
@@ -332,7 +357,9 @@ def bench_world(args, w):
             "kernel": kname, "algorithmic_bytes_per_step": byts,
             "note": "whole step (every rank's fused launch" + (", and the unit gathers" if w.stage == 3 else "")
                     + ") timed with HIP events on the compute stream"}
-    return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, {
+    gather = 4 * w.numel if w.stage == 3 else 0      # two gathers: 2 B read + 2 B written each
+    rw = {"step": (w.numel * (2 * N + 12) + gather, 14 * w.numel + gather, ms_step)}
+    return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, rw, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
         "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3),
         "stage3_layout": ("owner_broadcast" if args.owner else "per_unit_split") if w.stage == 3 else None}
@@ -386,9 +413,9 @@ def main():
         sys.exit(2)
     w = wl.WORKLOADS[args.workload]
     if args.workload == "share64":
-        value, ms, roof, roof_fused, parts, cfg = bench_share64(args, w)
+        value, ms, roof, roof_fused, parts, rw, cfg = bench_share64(args, w)
     else:
-        value, ms, roof, roof_fused, parts, cfg = bench_world(args, w)
+        value, ms, roof, roof_fused, parts, rw, cfg = bench_world(args, w)
     torch.cuda.synchronize()
     line = {"metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -398,11 +425,14 @@ def main():
         line["roofline_fused_step"] = roof_fused
     if parts:
         line["parts"] = parts
-    if "peer_receive" in parts:
+    if rw:
         import zero_sharded_mixed_reduce_amd as z
-        ref = copy_reference(z, parts["peer_receive"]["bytes"] // 2 // 16 * 16)
-        line["copy_reference_GBps"] = round(ref, 1)
-        parts["peer_receive"]["frac_of_copy_reference"] = round(parts["peer_receive"]["GBps"] / ref, 4)
+        ref = references(z, REFERENCE_BYTES)
+        if "peer_receive" in parts:
+            line["copy_reference_GBps"] = round(ref["copy_GBps"], 1)
+            parts["peer_receive"]["frac_of_copy_reference"] = round(
+                parts["peer_receive"]["GBps"] / ref["copy_GBps"], 4)
+        line["phased_bound"] = phased(parts, rw, ref["pure"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

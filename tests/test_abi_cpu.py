@@ -35,6 +35,41 @@ def test_every_declared_symbol_is_exported():
     assert snames == ["zsmr_synth_fill16", "zsmr_synth_fill32"]
     for n in snames:
         assert hasattr(slib, n), n
+    import ceiling
+    clib = ctypes.CDLL(ceiling.LIB_PATH)
+    cnames = declared("zsmr_ceiling.h")
+    assert cnames == ["zsmr_ceiling_read", "zsmr_ceiling_write"]
+    for n in cnames:
+        assert hasattr(clib, n), n
+
+
+def test_ceiling_argument_errors_return_before_any_launch():
+    import ceiling
+    lib = ceiling._lib()
+    a16, a8 = 1 << 20, (1 << 20) + 8          # fake device addresses: never dereferenced
+    assert lib.zsmr_ceiling_read(None, 16, 0, a16, None) == 1
+    assert lib.zsmr_ceiling_read(a16, 16, 0, None, None) == 1
+    assert lib.zsmr_ceiling_read(a16, -16, 0, a16, None) == 1
+    assert lib.zsmr_ceiling_read(a16, 24, 0, a16, None) == 1
+    assert lib.zsmr_ceiling_read(a16, 16, 2, a16, None) == 1
+    assert lib.zsmr_ceiling_read(a8, 16, 0, a16, None) == 5
+    assert lib.zsmr_ceiling_read(a16, 16, 1, a8, None) == 5
+    assert lib.zsmr_ceiling_read(a16, 0, 1, a16, None) == 0
+    assert lib.zsmr_ceiling_write(None, 16, 0, 0, None) == 1
+    assert lib.zsmr_ceiling_write(a16, 8, 0, 0, None) == 1
+    assert lib.zsmr_ceiling_write(a16, 16, 3, 0, None) == 1
+    assert lib.zsmr_ceiling_write(a8, 16, 1, 0, None) == 5
+    assert lib.zsmr_ceiling_write(a16, 0, 0, 0, None) == 0
+    assert lib.zsmr_ceiling_write(None, 0, 0, 0, None) == 0        # nothing to touch
+    assert lib.zsmr_ceiling_read(None, 0, 0, None, None) == 0
+    assert lib.zsmr_ceiling_read(None, 0, 5, None, None) == 1      # the shape is still checked
+
+
+def test_phased_bound_is_read_time_plus_write_time():
+    import ceiling
+    # 7e9 bytes read at 7000 GB/s (1 ms) and 3e9 written at 6000 GB/s (0.5 ms)
+    assert ceiling.phased_bound(7_000_000_000, 3_000_000_000, 7000.0, 6000.0) == pytest.approx(1.5)
+    assert ceiling.phased_bound(0, 0, 1.0, 1.0) == 0
 
 
 CONFIGS = [

@@ -61,3 +61,12 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     py.write_text("X = 2\n\ndef f():\n    return X\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_phased_bound_report():
+    pure = {"read_GBps": 7000.0, "write_GBps": 6000.0, "read": {"bursts": 7000.0},
+            "write": {"bursts_nt": 6000.0}, "bytes": 16}
+    out = bench.phased({}, {"step": (7_000_000_000, 3_000_000_000, 2.0)}, pure)
+    assert out["step"]["bound_ms"] == 1.5 and out["step"]["measured_ms"] == 2.0
+    assert out["step"]["frac"] == 0.75
+    assert out["read_GBps"] == 7000.0 and out["write_GBps"] == 6000.0

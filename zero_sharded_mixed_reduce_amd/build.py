@@ -4,6 +4,8 @@
   ``include/zsmr.h``).
 * ``synth/libzsmr_synth.so`` -- the GPU fill kernels of the seeded input
   generator (C ABI in ``include/zsmr_synth.h``).
+* ``ceiling/libzsmr_ceiling.so`` -- pure-read and pure-write reference
+  streams for the benchmark (C ABI in ``include/zsmr_ceiling.h``).
 
 Every HIP source is compiled for gfx950 only, with floating-point contraction
 off (the method's Adam is specified one rounding per operation) and with
@@ -25,6 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 
 LIB = os.path.join(PKG, "libzsmr.so")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libzsmr_synth.so")
+CEILING_LIB = os.path.join(ROOT, "ceiling", "libzsmr_ceiling.so")
 
 
 def hipcc() -> str:
@@ -64,9 +67,15 @@ def build_synth(extra=()):
     return SYNTH_LIB
 
 
+def build_ceiling(extra=()):
+    _build(CEILING_LIB, [os.path.join(ROOT, "ceiling", "ceiling.hip")], extra)
+    return CEILING_LIB
+
+
 def build_all():
     build_lib()
     build_synth()
+    build_ceiling()
 
 
 if __name__ == "__main__":
