@@ -257,7 +257,9 @@ int32_t zero_stage3_set_max_live(zsmr_ctx* ctx, int32_t max_live);
 
 /* Gather unit `unit`: copy the N 16-bit shards shard_ptrs[0..N-1] (a host
  * array of N device pointers, shard r of S_u elements) into unit_buf (N*S_u
- * elements, shard r at r*S_u).  ZSMR_ERR_STATE if the unit is already live or
+ * elements, shard r at r*S_u).  A shard may not overlap unit_buf
+ * (ZSMR_ERR_ARG), except one that sits exactly at its own slot r*S_u, which
+ * is left as it is.  ZSMR_ERR_STATE if the unit is already live or
  * max_live units are live.  Counts one all-gather of (N-1)*S_u elements
  * received by every rank, and the live/peak gathered bytes.
  * Stage 4 (owner broadcast): shard_ptrs holds one pointer, the owner's 16-bit

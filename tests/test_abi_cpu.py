@@ -191,6 +191,14 @@ def test_stage3_state_errors_on_the_host():
     with pytest.raises(z.ZsmrError) as e:     # a null shard pointer is refused before launching
         z.zero_stage3_unit_gather(ctx, 0, [1 << 20, 0, 1 << 20, 1 << 20], 1 << 21, stream=0)
     assert e.value.code == z.ZSMR_ERR_ARG
+    U, slot = 1 << 21, 8 * 2                  # unit buffer; S_u = 8 bf16 elements per shard
+    far = [1 << 24, (1 << 24) + 4096, (1 << 24) + 8192, (1 << 24) + 12288]
+    for r, bad in ((1, U + 3 * slot), (0, U + 8), (3, U - 8)):
+        ptrs = list(far)
+        ptrs[r] = bad                         # overlaps the unit buffer, not at its own slot
+        with pytest.raises(z.ZsmrError) as e:
+            z.zero_stage3_unit_gather(ctx, 0, ptrs, U, stream=0)
+        assert e.value.code == z.ZSMR_ERR_ARG
     assert z.zero_stage3_unit_state(ctx, 0) == (False, 0, 0)
     z.zero_stage3_set_max_live(ctx, 2)
     with pytest.raises(z.ZsmrError) as e:

@@ -569,6 +569,31 @@ def test_gather_copy_alignments():
     assert z.zero_counters(ctx, 1)["ag_elems"] == 6 * n
 
 
+def test_stage3_gather_with_shards_already_in_their_slots():
+    """Shards that already sit at their own slots of the unit buffer (an
+    in-place gather) are left as they are; the others are copied in."""
+    world, units = 4, [40_000, 12_345]
+    ctx = z.zero_init_shards(sum(units), world, 3, "bf16", pad=True, units=units)
+    for u in range(len(units)):
+        each = z.zero_layout(ctx, 0, u)[1]
+        rng = np.random.default_rng(u)
+        want = rng.integers(0, 1 << 16, world * each, dtype=np.uint64).astype(np.uint16)
+        buf = torch.zeros(world * each + 64, dtype=torch.int16, device="cuda")
+        unit_buf = buf[32:32 + world * each]
+        inplace = {0, 2}
+        for r in inplace:                     # shards 0 and 2 are already in place
+            unit_buf[r * each:(r + 1) * each] = dev16(want[r * each:(r + 1) * each])
+        others = {r: dev16(want[r * each:(r + 1) * each]) for r in range(world) if r not in inplace}
+        ptrs = [unit_buf[r * each:] if r in inplace else others[r] for r in range(world)]
+        say(f"[gather in place] unit {u} each={each}")
+        z.zero_stage3_unit_gather(ctx, u, ptrs, unit_buf)
+        torch.cuda.synchronize()
+        got = host16(buf)
+        assert np.array_equal(got[32:32 + world * each], want)
+        assert not got[:32].any() and not got[32 + world * each:].any()
+        z.zero_stage3_unit_release(ctx, u)
+
+
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 16_383, 16_384, 16_385, 3 * 16_384 + 5,
                                (1 << 24) + 777, 256 * 4 * 2 * 16_384 + 3])
 @pytest.mark.parametrize("off", [0, 3, 40])     # 40: a 24-element head to a 128-byte line

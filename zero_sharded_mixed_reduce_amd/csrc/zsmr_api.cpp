@@ -604,12 +604,15 @@ int32_t zero_stage3_unit_gather(zsmr_ctx* c, int32_t unit, const void* const* sh
     if (!al(unit_buf, 2)) return ZSMR_ERR_ALIGN;
     if (c->live[unit] || c->live_units >= c->max_live) return ZSMR_ERR_STATE;
     const int64_t each = owner ? c->units[unit] : c->shard_u[unit];
-    if (owner) {
-        const uint16_t* src = static_cast<const uint16_t*>(shard_ptrs[0]);
-        uint16_t* dst = static_cast<uint16_t*>(unit_buf);
-        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
-        const uintptr_t bytes = static_cast<uintptr_t>(each) * 2;
-        if (s0 < d0 + bytes && d0 < s0 + bytes) return ZSMR_ERR_ARG;
+    // A source may not overlap the unit buffer, except a shard that already
+    // sits exactly in its own slot (copied onto itself, it stays as it is).
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(unit_buf);
+    const uintptr_t slot = static_cast<uintptr_t>(each) * 2;
+    const uintptr_t d1 = d0 + slot * static_cast<uintptr_t>(nsrc);
+    for (int32_t r = 0; r < nsrc; ++r) {
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(shard_ptrs[r]);
+        if (s0 == d0 + slot * static_cast<uintptr_t>(r)) continue;
+        if (s0 < d1 && d0 < s0 + slot) return ZSMR_ERR_ARG;
     }
     const hipError_t e = zsmr::launch_gather16(reinterpret_cast<const uint16_t* const*>(shard_ptrs),
                                                nsrc, each, static_cast<uint16_t*>(unit_buf), stream);
