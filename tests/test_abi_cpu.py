@@ -320,3 +320,24 @@ def test_owner_argument_errors():
     z.zero_fused_step(ctx, 1, 0, ok, 16, 0, ok, ok, ok, ok, 1, 1e-3, stream=0)
     assert z.zero_counters(ctx, 0)["traffic_elems"] == 0
     assert z.zero_stage3_unit_state(ctx, 0) == (False, 0, 0)
+
+
+def test_a_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    import ceiling
+    import synth.gpu as sg
+    gone = str(tmp_path / "libgone.so")
+    monkeypatch.setattr(z, "LIB_PATH", gone)
+    monkeypatch.setattr(z, "_LIB", None)
+    with pytest.raises(ImportError):
+        z.load()
+    with pytest.raises(ImportError):
+        z.zero_init_shards(64, 4, 2, "bf16")
+    monkeypatch.setattr(sg, "LIB_PATH", gone)
+    monkeypatch.setattr(sg, "_LIB", None)
+    with pytest.raises(ImportError):
+        sg.fill32(1 << 20, 4, 0, 4, 0, 0, 0, 1, 1.0, stream=0)
+    monkeypatch.setattr(ceiling, "LIB_PATH", gone)
+    monkeypatch.setattr(ceiling, "_LIB", None)
+    with pytest.raises(ImportError):
+        ceiling.write(1 << 20, 16, 0, 0, stream=0)
