@@ -454,7 +454,7 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
 // Any number of rows; rows 16-byte aligned (the host checks); a row stride of
 // fewer than 2^63 bytes.
 template <int GDT, int PDT, int DV, int KD>
-__global__ __launch_bounds__(kThreads, 2) void step_deferred_kernel(StepArgs a, Window win) {
+__global__ __launch_bounds__(kThreads, KD <= kRingTwoPerCu ? 2 : 1) void step_deferred_kernel(StepArgs a, Window win) {
     constexpr int kWaves = kThreads / 64;
     __shared__ float s_w[kWaves][KD][512];      // a tile's results in element order
     __shared__ float s_m[kWaves][KD][512];
