@@ -249,6 +249,21 @@ int32_t zero_fused_step_range(zsmr_ctx* ctx, int32_t rank, int32_t unit, int64_t
 int32_t zero_gather_copy(zsmr_ctx* ctx, int32_t recv_rank, const void* src, void* dst,
                          int64_t n, hipStream_t stream);
 
+/* All-gather receive of one bucket: copy `count` blocks of n 16-bit elements,
+ * block k from src + k*stride to dst + k*stride (elements).  With buckets
+ * over the ranks' shards (see zero_fused_step_range), bucket [b0, b1) of
+ * every peer q sits at q*S + b0 of the working copy, so the peers' pieces of
+ * one bucket are such blocks with n = b1 - b0 and stride = S, and each
+ * bucket's receive can follow its update while the backward pass goes on
+ * ("ZeRO, annotated" section 5.2, the bucketed all-gather).  Blocks are
+ * copied as zero_gather_copy would copy each (results identical).  Counted
+ * as count*n elements of all-gather traffic received by recv_rank.
+ * ZSMR_ERR_ARG if count > 65535, if blocks overlap (count > 1 and stride <
+ * n), or if the spans [src, src + (count-1)*stride + n) and the same of dst
+ * overlap; n == 0 or count == 0 does nothing. */
+int32_t zero_gather_copy_blocks(zsmr_ctx* ctx, int32_t recv_rank, const void* src, void* dst,
+                                int64_t n, int32_t count, int64_t stride, hipStream_t stream);
+
 /* ZeRO-3 schedule ("The four schemes", where the third P comes from; "ZeRO
  * and FSDP", "ZeRO-3 and FSDP").  Units gathered at once may not exceed
  * max_live (default 1, i.e. no prefetch; 2 allows gathering unit i+1 while

@@ -174,6 +174,22 @@ def test_argument_errors_return_before_any_launch():
     with pytest.raises(z.ZsmrError) as e:     # overlapping copy
         z.zero_gather_copy(ctx, 0, ok, ok + 8, 100, stream=0)
     assert e.value.code == z.ZSMR_ERR_ARG
+    far = ok + (1 << 30)
+    for args in ((ok, far, 100, 2, 99),          # blocks overlap (stride < n)
+                 (ok, ok + 8, 10, 3, 100),        # source and destination spans overlap
+                 (ok, far, 10, 65536, 100),       # more blocks than a grid holds
+                 (ok, far, 10, 3, 1 << 62),       # the span overflows
+                 (ok, far, -1, 3, 100),
+                 (ok, far, 10, -1, 100),
+                 (0, far, 10, 3, 100)):
+        with pytest.raises(z.ZsmrError) as e:
+            z.zero_gather_copy_blocks(ctx, 0, *args, stream=0)
+        assert e.value.code == z.ZSMR_ERR_ARG, args
+    with pytest.raises(z.ZsmrError) as e:         # odd address of a 16-bit block
+        z.zero_gather_copy_blocks(ctx, 0, ok + 1, far, 10, 3, 100, stream=0)
+    assert e.value.code == z.ZSMR_ERR_ALIGN
+    z.zero_gather_copy_blocks(ctx, 0, ok, far, 0, 3, 100, stream=0)    # nothing to copy
+    z.zero_gather_copy_blocks(ctx, 0, ok, far, 10, 0, 100, stream=0)
     z.zero_adam_step(ok, ok, ok, ok, 0, 1, 1e-3, stream=0)       # n = 0 is a no-op
     z.zero_gather_copy(ctx, 0, ok, ok, 0, stream=0)
     for rank in range(4):                                          # nothing was counted

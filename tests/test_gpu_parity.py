@@ -569,6 +569,34 @@ def test_gather_copy_alignments():
     assert z.zero_counters(ctx, 1)["ag_elems"] == 6 * n
 
 
+@pytest.mark.parametrize("n,count,stride", [
+    (1, 1, 1), (7, 3, 7), (2_000_003, 5, 2_000_003),     # blocks end to end; every block aligned differently
+    (100_003, 63, 117_003), (1_048_576, 4, 1_048_580),   # gaps between blocks
+    (16_384, 2, 16_384 + 64), (33, 17, 40),
+])
+@pytest.mark.parametrize("off", [0, 3, 40])
+def test_gather_copy_blocks(n, count, stride, off):
+    """count blocks of n elements, block k at k*stride: the same bytes as
+    count single copies, nothing written between or around the blocks, and
+    count*n elements counted."""
+    say(f"[copy blocks] n={n} count={count} stride={stride} off={off}")
+    span = (count - 1) * stride + n
+    rng = np.random.default_rng(n + count)
+    src = rng.integers(1, 1 << 16, span + 2 * off + 64, dtype=np.uint64).astype(np.uint16)
+    S = dev16(src)
+    D = torch.zeros(span + 2 * off + 64, dtype=torch.int16, device="cuda")
+    ctx = z.zero_init_shards(64, 2, 2, "bf16")
+    z.zero_gather_copy_blocks(ctx, 1, S[off:], D[off:], n, count, stride)
+    torch.cuda.synchronize()
+    got = host16(D)
+    want = np.zeros_like(src)
+    for k in range(count):
+        lo = off + k * stride
+        want[lo:lo + n] = src[lo:lo + n]
+    assert np.array_equal(got, want)
+    assert z.zero_counters(ctx, 1)["ag_elems"] == count * n
+
+
 def test_stage3_gather_with_shards_already_in_their_slots():
     """Shards that already sit at their own slots of the unit buffer (an
     in-place gather) are left as they are; the others are copied in."""

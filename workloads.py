@@ -219,6 +219,17 @@ class RankShare:
         if rest:
             z.zero_gather_copy(self.ctx, self.rank, self.staged[off + S:], self.wc[off + S:], rest)
 
+    def receive_range(self, b0: int, b1: int):
+        """The receive of bucket [b0, b1) alone: every peer q's piece of it
+        sits at q*S + b0 of the working copy (and of the staged buffer), so
+        the peers below and above this rank are two runs of blocks."""
+        r, S, N, n = self.rank, self.S, self.w.world, b1 - b0
+        if r > 0:
+            z.zero_gather_copy_blocks(self.ctx, r, self.staged[b0:], self.wc[b0:], n, r, S)
+        if r + 1 < N:
+            o = (r + 1) * S + b0
+            z.zero_gather_copy_blocks(self.ctx, r, self.staged[o:], self.wc[o:], n, N - r - 1, S)
+
     def step(self, t: int, timer: Optional[Timer] = None):
         if timer:
             timer.start()
@@ -244,7 +255,9 @@ class RankShare:
         """One step whose gradients arrive in buckets: the simulated backward
         (the input generator, on ``backward_stream``) fills one bucket of all
         N rows at a time, and the fused step consumes each bucket on the
-        current stream as soon as it is ready, overlapping the two."""
+        current stream as soon as it is ready, followed by the receive of the
+        peers' pieces of the same bucket, overlapping both with the
+        backward."""
         w = self.w
         compute = torch.cuda.current_stream()
         start = torch.cuda.Event()
@@ -262,7 +275,7 @@ class RankShare:
             z.zero_fused_step_range(self.ctx, self.rank, 0, b0, b1 - b0, self.grads, self.row_stride,
                                     0, self.master, self.m, self.v, self.wc[self.off:], t, w.lr,
                                     w.betas, w.eps)
-        self.receive()
+            self.receive_range(b0, b1)
 
 
 # ---------------------------------------------------------------- stage 3 --

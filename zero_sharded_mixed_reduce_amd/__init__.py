@@ -81,6 +81,7 @@ SIGNATURES = {
     "zero_fused_step_range": (_i32, [_vp, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _i32, ctypes.POINTER(zsmr_adam), _vp]),
     "zero_gather_copy": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
+    "zero_gather_copy_blocks": (_i32, [_vp, _i32, _vp, _vp, _i64, _i32, _i64, _vp]),
     "zero_stage3_set_max_live": (_i32, [_vp, _i32]),
     "zero_stage3_unit_gather": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _vp, _vp]),
     "zero_stage3_unit_release": (_i32, [_vp, _i32]),
@@ -276,6 +277,13 @@ def zero_fused_step_range(ctx: Ctx, rank: int, unit: int, begin: int, count: int
 def zero_gather_copy(ctx: Ctx, recv_rank: int, src, dst, n: int, stream=None):
     _check(_lib().zero_gather_copy(ctx.handle, recv_rank, _ptr(src), _ptr(dst), int(n),
                                    _stream(stream)), "zero_gather_copy")
+
+
+def zero_gather_copy_blocks(ctx: Ctx, recv_rank: int, src, dst, n: int, count: int, stride: int,
+                            stream=None):
+    _check(_lib().zero_gather_copy_blocks(ctx.handle, recv_rank, _ptr(src), _ptr(dst), int(n),
+                                          int(count), int(stride), _stream(stream)),
+           "zero_gather_copy_blocks")
 
 
 def zero_stage3_set_max_live(ctx: Ctx, max_live: int) -> None:

@@ -5,6 +5,7 @@
 // compute the fp32 Adam constants, launch through zsmr_launch.h on the
 // caller's stream and only then update the per-rank counters.
 #include <algorithm>
+#include <cstdint>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -581,6 +582,26 @@ int32_t zero_gather_copy(zsmr_ctx* c, int32_t recv_rank, const void* src, void* 
                                              static_cast<uint16_t*>(dst), n, stream);
     if (e != hipSuccess) return hip_fail(e);
     c->ag[recv_rank] += n;
+    return ZSMR_OK;
+}
+
+int32_t zero_gather_copy_blocks(zsmr_ctx* c, int32_t recv_rank, const void* src, void* dst,
+                                int64_t n, int32_t count, int64_t stride, hipStream_t stream) {
+    if (!c || recv_rank < 0 || recv_rank >= c->world || n < 0 || count < 0 || count > 65535)
+        return ZSMR_ERR_ARG;
+    if (n == 0 || count == 0) return ZSMR_OK;
+    if (count > 1 && (stride < n || stride > (INT64_MAX - n) / (count - 1)))
+        return ZSMR_ERR_ARG;   // blocks would overlap, or the span would overflow
+    if (!src || !dst) return ZSMR_ERR_ARG;
+    if (!al(src, 2) || !al(dst, 2)) return ZSMR_ERR_ALIGN;
+    const int64_t span = (int64_t)(count - 1) * (count > 1 ? stride : 0) + n;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t bytes = static_cast<uintptr_t>(span) * 2;
+    if (s < d + bytes && d < s + bytes) return ZSMR_ERR_ARG;
+    const hipError_t e = zsmr::launch_copy_blocks(static_cast<const uint16_t*>(src),
+                                                  static_cast<uint16_t*>(dst), n, count, stride, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c->ag[recv_rank] += (int64_t)count * n;
     return ZSMR_OK;
 }
 

@@ -737,10 +737,59 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
     }
 }
 
+// Widest copy vector (bytes) for source and destination addresses a and b:
+// the vectors need both equally aligned, so the width divides b - a.
+__host__ __device__ inline int copy_width(uintptr_t a, uintptr_t b) {
+    const uintptr_t d = a > b ? a - b : b - a;
+    if (d % 16 == 0) return 16;
+    if (d % 8 == 0) return 8;
+    if (d % 4 == 0) return 4;
+    return 2;
+}
+
+// Elements copied one by one before the vector body.  W-byte vectors need dst
+// (and src, equal to it modulo W) W-aligned; the burst copies (W >= 4) also
+// start their body on a 128-byte line of dst: HBM writes that cover part of a
+// line cost far more than their bytes (measured on MI355X: a copy whose
+// destination starts 16-96 bytes into a line runs about 8% slower, whatever
+// the source's offset).  At most 63 elements, within one workgroup.
+__host__ __device__ inline int64_t head_for(const void* dst, int w, int64_t n) {
+    const uintptr_t align = w >= 4 ? 128 : static_cast<uintptr_t>(w);
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(dst) % align;
+    int64_t h = mis ? static_cast<int64_t>((align - mis) / 2) : 0;
+    return h < n ? h : n;
+}
+
+// Vectors between dst's last 128 KB boundary and the burst copy's vector body
+// (dst + head), where the chunk grid starts (0 for the 2-byte copy).  128 KB
+// is one workgroup's four 32 KB bursts.  Measured on MI355X, a 14.77 GB copy
+// with source and destination shifted alike: 6.22-6.25 TB/s at multiples of
+// 128 KB, 6.15-6.19 at 4-8 KB past one, 6.01-6.04 at 18 KB, 5.87-5.91 at 32-64
+// KB (destination alone at 64 KB: 5.99; source alone: 6.13).
+__host__ __device__ inline int64_t pre_for(const void* dst, int w, int64_t head) {
+    constexpr uintptr_t kGrid = 128 * 1024;
+    if (w < 4) return 0;
+    const uintptr_t body = reinterpret_cast<uintptr_t>(dst) + static_cast<uintptr_t>(head) * 2;
+    return static_cast<int64_t>(body % kGrid / static_cast<uintptr_t>(w));
+}
+
 template <int W>
 __global__ __launch_bounds__(kThreads) void copy16_kernel(const uint16_t* src, uint16_t* dst,
                                                           int64_t n, int64_t head, int64_t pre) {
     copy_range<W>(src, dst, n, head, pre, blockIdx.x, gridDim.x);
+}
+
+// Block k of `count` (blockIdx.y): n elements from src + k * stride to
+// dst + k * stride, each block with the head and chunk grid a copy of its own
+// would have (the blocks' destinations need not share their alignment).
+template <int W>
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const uint16_t* src, uint16_t* dst,
+                                                               int64_t n, int64_t stride) {
+    const int64_t k = blockIdx.y;
+    const uint16_t* s = src + k * stride;
+    uint16_t* d = dst + k * stride;
+    const int64_t head = head_for(d, W, n);
+    copy_range<W>(s, d, n, head, pre_for(d, W, head), blockIdx.x, gridDim.x);
 }
 
 constexpr int kMaxGather = 64;
@@ -967,40 +1016,6 @@ hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream
     return hipSuccess;
 }
 
-static int copy_width(uintptr_t a, uintptr_t b) {
-    const uintptr_t d = a > b ? a - b : b - a;
-    if (d % 16 == 0) return 16;
-    if (d % 8 == 0) return 8;
-    if (d % 4 == 0) return 4;
-    return 2;
-}
-
-// Elements copied one by one before the vector body.  W-byte vectors need dst
-// (and src, equal to it modulo W) W-aligned; the burst copies (W >= 4) also
-// start their body on a 128-byte line of dst: HBM writes that cover part of a
-// line cost far more than their bytes (measured on MI355X: a copy whose
-// destination starts 16-96 bytes into a line runs about 8% slower, whatever
-// the source's offset).  At most 63 elements, within one workgroup.
-static int64_t head_for(const void* dst, int w, int64_t n) {
-    const uintptr_t align = w >= 4 ? 128 : static_cast<uintptr_t>(w);
-    const uintptr_t mis = reinterpret_cast<uintptr_t>(dst) % align;
-    int64_t h = mis ? static_cast<int64_t>((align - mis) / 2) : 0;
-    return h < n ? h : n;
-}
-
-// Vectors between dst's last 128 KB boundary and the burst copy's vector body
-// (dst + head), where the chunk grid starts (0 for the 2-byte copy).  128 KB
-// is one workgroup's four 32 KB bursts.  Measured on MI355X, a 14.77 GB copy
-// with source and destination shifted alike: 6.22-6.25 TB/s at multiples of
-// 128 KB, 6.15-6.19 at 4-8 KB past one, 6.01-6.04 at 18 KB, 5.87-5.91 at 32-64
-// KB (destination alone at 64 KB: 5.99; source alone: 6.13).
-static int64_t pre_for(const void* dst, int w, int64_t head) {
-    constexpr uintptr_t kGrid = 128 * 1024;
-    if (w < 4) return 0;
-    const uintptr_t body = reinterpret_cast<uintptr_t>(dst) + static_cast<uintptr_t>(head) * 2;
-    return static_cast<int64_t>(body % kGrid / static_cast<uintptr_t>(w));
-}
-
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
@@ -1014,6 +1029,33 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
         case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
         case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
         default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const uint16_t* src, uint16_t* dst, int64_t n, int32_t count,
+                              int64_t stride, hipStream_t s) {
+    if (n <= 0 || count <= 0) return hipSuccess;
+    // src - dst is the same for every block, and so is the vector width
+    const int w = copy_width(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst));
+    const int64_t pre_max = w >= 4 ? int64_t(128 * 1024) / w : 0;   // a block's chunk-grid offset
+    const int64_t per = n / (w / 2) + 1 + pre_max;
+    const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
+    int64_t bx = (units + kThreads - 1) / kThreads;
+    if (w >= 4) bx = (bx + kXcds - 1) / kXcds * kXcds;   // each block's row starts on XCD 0
+    const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
+    if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all blocks
+        const int64_t cap = (int64_t)cu_count() * bpc;
+        const int64_t lim = cap / count > 0 ? cap / count : 1;
+        if (bx > lim) bx = lim;
+    }
+    if (bx < 1) bx = 1;
+    const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(count));
+    switch (w) {
+        case 16: hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
+        case 8: hipLaunchKernelGGL(copy_blocks_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
+        case 4: hipLaunchKernelGGL(copy_blocks_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
+        default: hipLaunchKernelGGL(copy_blocks_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
     }
     return hipGetLastError();
 }

@@ -45,6 +45,9 @@ struct StepArgs {
 hipError_t launch_step(int mode, int grad_dtype, int param_dtype, const StepArgs& a,
                        hipStream_t stream);
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t stream);
+// dst[k*stride + j] = src[k*stride + j], j < n, k < count (count <= 65535)
+hipError_t launch_copy_blocks(const uint16_t* src, uint16_t* dst, int64_t n, int32_t count,
+                              int64_t stride, hipStream_t stream);
 // dst[r*each + j] = srcs[r][j], r < nsrc
 hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t each,
                            uint16_t* dst, hipStream_t stream);
