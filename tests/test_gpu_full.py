@@ -120,6 +120,32 @@ def test_rank_share_full_size(rank):
     free()
 
 
+@pytest.mark.parametrize("rank", [0, 63])
+def test_bucketed_step_full_size(rank):
+    """The share64 step as ``bench.py --buckets 8`` runs it (each bucket's
+    gradients filled on a second stream, its fused launch, then the receive
+    of the 63 peers' pieces of the bucket as blocks S apart): the same bits
+    as the unbucketed step, in every element of master, m, v and the 7.5e9-
+    element working copy, and the same counters."""
+    w = wl.WORKLOADS["share64"]
+    say(f"[full] share64 bucketed rank={rank}")
+    ref = wl.RankShare(w, rank=rank)
+    ref.gen_grads(1)
+    ref.step(1)
+    bk = wl.RankShare(w, rank=rank)
+    side = torch.cuda.Stream()
+    bk.step_bucketed(1, 8, side)
+    torch.cuda.synchronize()
+    for a, b in ((ref.master, bk.master), (ref.m, bk.m), (ref.v, bk.v)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    for c in range(0, ref.P, 1 << 28):
+        e = min(ref.P, c + (1 << 28))
+        assert torch.equal(ref.wc[c:e].view(torch.int16), bk.wc[c:e].view(torch.int16))
+    assert z.zero_counters(ref.ctx, rank) == z.zero_counters(bk.ctx, rank)
+    del ref, bk
+    free()
+
+
 def test_stage3_llama8b_full_size():
     w = wl.WORKLOADS["llama8b"]
     say(f"[full] llama8b: units={len(w.units)} numel={w.numel}")
