@@ -43,7 +43,13 @@ def _stream(stream):
 
 
 def _ptr(x):
-    return x if isinstance(x, int) else x.data_ptr()
+    """Device address of a tensor or a raw address; host tensors are refused."""
+    if isinstance(x, int):
+        return x
+    dev = getattr(x, "device", None)
+    if dev is not None and getattr(dev, "type", "cuda") != "cuda":
+        raise ValueError(f"a {dev.type} tensor was passed where device memory is required")
+    return x.data_ptr()
 
 
 def read(src, nbytes: int, shape: int, sink, stream=None) -> None:

@@ -37,7 +37,13 @@ def _stream(stream):
 
 
 def _ptr(x):
-    return x if isinstance(x, int) else x.data_ptr()
+    """Device address of a tensor or a raw address; host tensors are refused."""
+    if isinstance(x, int):
+        return x
+    dev = getattr(x, "device", None)
+    if dev is not None and getattr(dev, "type", "cuda") != "cuda":
+        raise ValueError(f"a {dev.type} tensor was passed where device memory is required")
+    return x.data_ptr()
 
 
 def fill16(dst, rows: int, row_stride: int, n: int, p0: int, p_valid: int, seed: int, tag: int,

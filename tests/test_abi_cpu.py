@@ -357,3 +357,25 @@ def test_a_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ceiling, "_LIB", None)
     with pytest.raises(ImportError):
         ceiling.write(1 << 20, 16, 0, 0, stream=0)
+
+
+def test_host_tensors_are_refused_before_any_call():
+    """A CPU tensor's address must never reach a kernel as a device address."""
+    import torch
+    import ceiling
+    import synth.gpu as sg
+    ctx = z.zero_init_shards(64, 4, 2, "bf16")
+    h16 = torch.zeros(64, dtype=torch.bfloat16)
+    h32 = torch.zeros(64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        z.zero_gather_copy(ctx, 0, h16, 1 << 20, 10, stream=0)
+    with pytest.raises(ValueError):
+        z.zero_fused_step(ctx, 0, 0, 1 << 20, 64, 0, h32, 1 << 21, 1 << 22, 1 << 23, 1, 1e-3, stream=0)
+    with pytest.raises(ValueError):
+        z.zero_init_state(ctx, 0, 0, h32, h32, h32, h32, h16, stream=0)
+    with pytest.raises(ValueError):
+        sg.fill16(h16, 1, 64, 64, 0, 64, 0, 0, 0, 1, 1.0, "bf16", stream=0)
+    with pytest.raises(ValueError):
+        ceiling.write(h32, 16, 0, 0, stream=0)
+    for rank in range(4):
+        assert z.zero_counters(ctx, rank)["traffic_elems"] == 0

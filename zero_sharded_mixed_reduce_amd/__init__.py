@@ -120,10 +120,16 @@ def _check(code: int, where: str) -> None:
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor (or a raw address, passed as it is).  A
+    tensor in host memory is refused: a kernel would take its address for a
+    device one."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    dev = getattr(x, "device", None)
+    if dev is not None and getattr(dev, "type", "cuda") != "cuda":
+        raise ValueError(f"a {dev.type} tensor was passed where device memory is required")
     return x.data_ptr()
 
 
