@@ -379,3 +379,58 @@ def test_host_tensors_are_refused_before_any_call():
         ceiling.write(h32, 16, 0, 0, stream=0)
     for rank in range(4):
         assert z.zero_counters(ctx, rank)["traffic_elems"] == 0
+
+
+class _FakeDeviceTensor:
+    """Stands in for a device tensor of `nbytes` bytes at a never-dereferenced
+    address (the binding's size checks run before any library call)."""
+
+    def __init__(self, elems, elem_bytes=2, contiguous=True):
+        import types
+        self.device = types.SimpleNamespace(type="cuda")
+        self._n, self._b, self._c = elems, elem_bytes, contiguous
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._b
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+def test_undersized_or_strided_tensors_are_refused_before_any_call():
+    F = _FakeDeviceTensor
+    ctx = z.zero_init_shards(64, 4, 2, "bf16")                  # S = 16 per rank
+    with pytest.raises(ValueError, match="dst"):
+        z.zero_gather_copy(ctx, 0, F(100), F(99), 100, stream=0)
+    with pytest.raises(ValueError, match="not contiguous"):
+        z.zero_gather_copy(ctx, 0, F(100, contiguous=False), F(100), 100, stream=0)
+    with pytest.raises(ValueError, match="src"):
+        z.zero_gather_copy_blocks(ctx, 0, F(3 * 50 + 9), F(1000), 10, 4, 50, stream=0)
+    with pytest.raises(ValueError, match="grads"):                # rows 0..3 of stride 16 from base 16
+        z.zero_fused_step(ctx, 1, 0, F(16 + 3 * 16 + 15), 16, 16, F(16, 4), F(16, 4), F(16, 4),
+                          F(16), 1, 1e-3, stream=0)
+    with pytest.raises(ValueError, match="master"):
+        z.zero_fused_step(ctx, 1, 0, F(16 + 3 * 16 + 16), 16, 16, F(15, 4), F(16, 4), F(16, 4),
+                          F(16), 1, 1e-3, stream=0)
+    with pytest.raises(ValueError, match="p16_dst"):               # an fp32 master where bytes count
+        z.zero_gather_cast(ctx, 0, 0, F(16, 4), F(8, 2), stream=0)
+    with pytest.raises(ValueError, match="g_out"):
+        z.zero_reduce_shard(ctx, 0, 0, F(64), 16, 0, True, F(15, 4), stream=0)
+    with pytest.raises(ValueError, match="p16_dst"):               # a range reaching element 16
+        z.zero_fused_step_range(ctx, 0, 0, 10, 6, F(64), 16, 0, F(16, 4), F(16, 4), F(16, 4),
+                                F(15), 1, 1e-3, stream=0)
+    s3 = z.zero_init_shards(64, 4, 3, "bf16", units=[32, 32])      # S_u = 8
+    with pytest.raises(ValueError, match="unit_buf"):
+        z.zero_stage3_unit_gather(s3, 1, [F(8)] * 4, F(31), stream=0)
+    with pytest.raises(ValueError, match="shard 2"):
+        z.zero_stage3_unit_gather(s3, 1, [F(8), F(8), F(7), F(8)], F(32), stream=0)
+    for c in (ctx, s3):
+        for rank in range(4):
+            assert z.zero_counters(c, rank)["traffic_elems"] == 0
+    assert z.zero_stage3_unit_state(s3, 1) == (False, 0, 0)

@@ -133,6 +133,37 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+def _fits(x, elems: int, elem_bytes: int, what: str) -> None:
+    """A tensor argument must be contiguous and hold the elems * elem_bytes
+    bytes the call touches from its first element: the library sees only the
+    address and cannot check.  Raw addresses are the caller's to check."""
+    if x is None or isinstance(x, int) or elems <= 0:
+        return
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: the tensor is not contiguous")
+    have = x.numel() * x.element_size()
+    if have < elems * elem_bytes:
+        raise ValueError(f"{what}: {have} bytes, the call touches {elems * elem_bytes}")
+
+
+def _piece_len(ctx, rank: int, unit: int) -> int:
+    """Elements of the (rank, unit) piece, or 0 where the layout refuses the
+    pair (the call itself then reports the error)."""
+    off, ln, loc = _i64(), _i64(), _i64()
+    if _lib().zero_layout(ctx.handle, rank, unit, ctypes.byref(off), ctypes.byref(ln),
+                          ctypes.byref(loc)) != ZSMR_OK:
+        return 0
+    return ln.value
+
+
+def _rows_fit(ctx, grads, row_stride: int, base: int, end: int, what: str) -> None:
+    """The N gradient rows: row r covers [base + r*row_stride, ... + end)."""
+    if grads is None or isinstance(grads, int) or end <= 0:
+        return
+    world = zero_layout_info(ctx)["world"]
+    _fits(grads, int(base) + (world - 1) * max(int(row_stride), 0) + end, 2, what)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -238,12 +269,19 @@ def zero_reset_counters(ctx: Ctx) -> None:
 
 
 def zero_init_state(ctx: Ctx, rank: int, unit: int, theta0, master, m, v, p16, stream=None):
+    n = _piece_len(ctx, rank, unit)
+    for x, what in ((theta0, "theta0"), (master, "master"), (m, "m"), (v, "v")):
+        _fits(x, n, 4, what)
+    _fits(p16, n, 2, "p16")
     _check(_lib().zero_init_state(ctx.handle, rank, unit, _ptr(theta0), _ptr(master), _ptr(m),
                                   _ptr(v), _ptr(p16), _stream(stream)), "zero_init_state")
 
 
 def zero_reduce_shard(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base_elem: int,
                       mean: bool, g_out, stream=None):
+    n = _piece_len(ctx, rank, unit)
+    _rows_fit(ctx, grads, row_stride, base_elem, n, "grads")
+    _fits(g_out, n, 4, "g_out")
     _check(_lib().zero_reduce_shard(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
                                     int(base_elem), int(bool(mean)), _ptr(g_out), _stream(stream)),
            "zero_reduce_shard")
@@ -251,12 +289,17 @@ def zero_reduce_shard(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, ba
 
 def zero_adam_step(master, m, v, g, n: int, t: int, lr: float, betas=(0.9, 0.999),
                    eps: float = 1e-8, stream=None):
+    for x, what in ((master, "master"), (m, "m"), (v, "v"), (g, "g")):
+        _fits(x, int(n), 4, what)
     hp = _hp(lr, betas, eps)
     _check(_lib().zero_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(g), int(n), int(t),
                                  ctypes.byref(hp), _stream(stream)), "zero_adam_step")
 
 
 def zero_gather_cast(ctx: Ctx, rank: int, unit: int, master, p16_dst, stream=None):
+    n = _piece_len(ctx, rank, unit)
+    _fits(master, n, 4, "master")
+    _fits(p16_dst, n, 2, "p16_dst")
     _check(_lib().zero_gather_cast(ctx.handle, rank, unit, _ptr(master), _ptr(p16_dst),
                                    _stream(stream)), "zero_gather_cast")
 
@@ -264,6 +307,11 @@ def zero_gather_cast(ctx: Ctx, rank: int, unit: int, master, p16_dst, stream=Non
 def zero_fused_step(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base_elem: int,
                     master, m, v, p16_dst, t: int, lr: float, betas=(0.9, 0.999),
                     eps: float = 1e-8, stream=None):
+    n = _piece_len(ctx, rank, unit)
+    _rows_fit(ctx, grads, row_stride, base_elem, n, "grads")
+    for x, what in ((master, "master"), (m, "m"), (v, "v")):
+        _fits(x, n, 4, what)
+    _fits(p16_dst, n, 2, "p16_dst")
     hp = _hp(lr, betas, eps)
     _check(_lib().zero_fused_step(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
                                   int(base_elem), _ptr(master), _ptr(m), _ptr(v), _ptr(p16_dst),
@@ -273,6 +321,11 @@ def zero_fused_step(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base
 def zero_fused_step_range(ctx: Ctx, rank: int, unit: int, begin: int, count: int, grads,
                           row_stride: int, base_elem: int, master, m, v, p16_dst, t: int,
                           lr: float, betas=(0.9, 0.999), eps: float = 1e-8, stream=None):
+    end = int(begin) + int(count) if int(begin) >= 0 and int(count) >= 0 else 0
+    _rows_fit(ctx, grads, row_stride, base_elem, end, "grads")
+    for x, what in ((master, "master"), (m, "m"), (v, "v")):
+        _fits(x, end, 4, what)
+    _fits(p16_dst, end, 2, "p16_dst")
     hp = _hp(lr, betas, eps)
     _check(_lib().zero_fused_step_range(ctx.handle, rank, unit, int(begin), int(count), _ptr(grads),
                                         int(row_stride), int(base_elem), _ptr(master), _ptr(m),
@@ -281,12 +334,18 @@ def zero_fused_step_range(ctx: Ctx, rank: int, unit: int, begin: int, count: int
 
 
 def zero_gather_copy(ctx: Ctx, recv_rank: int, src, dst, n: int, stream=None):
+    _fits(src, int(n), 2, "src")
+    _fits(dst, int(n), 2, "dst")
     _check(_lib().zero_gather_copy(ctx.handle, recv_rank, _ptr(src), _ptr(dst), int(n),
                                    _stream(stream)), "zero_gather_copy")
 
 
 def zero_gather_copy_blocks(ctx: Ctx, recv_rank: int, src, dst, n: int, count: int, stride: int,
                             stream=None):
+    if int(n) > 0 and int(count) > 0:
+        span = (int(count) - 1) * max(int(stride), 0) + int(n)
+        _fits(src, span, 2, "src")
+        _fits(dst, span, 2, "dst")
     _check(_lib().zero_gather_copy_blocks(ctx.handle, recv_rank, _ptr(src), _ptr(dst), int(n),
                                           int(count), int(stride), _stream(stream)),
            "zero_gather_copy_blocks")
@@ -297,6 +356,17 @@ def zero_stage3_set_max_live(ctx: Ctx, max_live: int) -> None:
 
 
 def zero_stage3_unit_gather(ctx: Ctx, unit: int, shard_ptrs: Sequence, unit_buf, stream=None):
+    info = zero_layout_info(ctx)
+    if info["stage"] in (ZSMR_ZERO3, ZSMR_ZERO3_OWNER) and 0 <= unit < info["n_units"]:
+        if info["stage"] == ZSMR_ZERO3_OWNER:
+            each = _piece_len(ctx, zero_unit_owner(ctx, unit), unit)
+            nsrc = 1
+        else:
+            each = _piece_len(ctx, 0, unit)
+            nsrc = info["world"]
+        for r, p in enumerate(list(shard_ptrs)[:nsrc]):
+            _fits(p, each, 2, f"shard {r}")
+        _fits(unit_buf, nsrc * each, 2, "unit_buf")
     arr = (_vp * len(shard_ptrs))(*[_ptr(p) for p in shard_ptrs])
     _check(_lib().zero_stage3_unit_gather(ctx.handle, unit, arr, _ptr(unit_buf), _stream(stream)),
            "zero_stage3_unit_gather")
