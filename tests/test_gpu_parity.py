@@ -574,25 +574,26 @@ def test_gather_copy_alignments():
     (100_003, 63, 117_003), (1_048_576, 4, 1_048_580),   # gaps between blocks
     (16_384, 2, 16_384 + 64), (33, 17, 40),
 ])
-@pytest.mark.parametrize("off", [0, 3, 40])
-def test_gather_copy_blocks(n, count, stride, off):
+@pytest.mark.parametrize("soff,doff", [(0, 0), (3, 3), (40, 40),   # 16-byte vectors
+                                       (4, 0), (2, 0), (1, 0), (0, 7)])   # 8-, 4-, 2-byte
+def test_gather_copy_blocks(n, count, stride, soff, doff):
     """count blocks of n elements, block k at k*stride: the same bytes as
     count single copies, nothing written between or around the blocks, and
-    count*n elements counted."""
-    say(f"[copy blocks] n={n} count={count} stride={stride} off={off}")
+    count*n elements counted; source and destination equally aligned or not
+    (the copy's vector width follows their distance)."""
+    say(f"[copy blocks] n={n} count={count} stride={stride} soff={soff} doff={doff}")
     span = (count - 1) * stride + n
     rng = np.random.default_rng(n + count)
-    src = rng.integers(1, 1 << 16, span + 2 * off + 64, dtype=np.uint64).astype(np.uint16)
+    src = rng.integers(1, 1 << 16, span + 128, dtype=np.uint64).astype(np.uint16)
     S = dev16(src)
-    D = torch.zeros(span + 2 * off + 64, dtype=torch.int16, device="cuda")
+    D = torch.zeros(span + 128, dtype=torch.int16, device="cuda")
     ctx = z.zero_init_shards(64, 2, 2, "bf16")
-    z.zero_gather_copy_blocks(ctx, 1, S[off:], D[off:], n, count, stride)
+    z.zero_gather_copy_blocks(ctx, 1, S[soff:], D[doff:], n, count, stride)
     torch.cuda.synchronize()
     got = host16(D)
     want = np.zeros_like(src)
     for k in range(count):
-        lo = off + k * stride
-        want[lo:lo + n] = src[lo:lo + n]
+        want[doff + k * stride:doff + k * stride + n] = src[soff + k * stride:soff + k * stride + n]
     assert np.array_equal(got, want)
     assert z.zero_counters(ctx, 1)["ag_elems"] == count * n
 
