@@ -64,9 +64,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel and workload sources; else None."""
+def read_traffic(kernel: str, workload: str, field: str = "hbm_bytes_per_launch"):
+    """HBM bytes (per launch, or per step for the world workloads) from a
+    committed rocprofv3 --pmc summary, if it was taken on the current kernel
+    and workload sources; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -79,7 +80,7 @@ def read_traffic(kernel: str, workload: str):
     if vals.get("kernel_and_workload_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        return int(float(vals[field]))
     except (KeyError, ValueError):
         return None
 
@@ -353,7 +354,8 @@ def bench_world(args, w):
     kname = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
              else "step_vec8_kernel")
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": read_traffic(kname, w.key),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": read_traffic(kname, w.key, "hbm_bytes_per_step"),
             "kernel": kname, "algorithmic_bytes_per_step": byts,
             "note": "whole step (every rank's fused launch" + (", and the unit gathers" if w.stage == 3 else "")
                     + ") timed with HIP events on the compute stream"}
