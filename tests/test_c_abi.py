@@ -1,0 +1,57 @@
+"""The C ABI from C: a plain C99 program compiled against include/zsmr.h and
+linked to libzsmr.so computes, through the host-only entry points, the pages'
+tiny example (Psi = 8 parameters on N = 4 ranks: 128, 56, 44 and 32 bytes
+per rank under data parallelism and ZeRO-1/2/3, "One Poem Suffices: ZeRO"
+section 4.1; 12 and 18 elements of traffic) and refuses an indivisible
+count.  No GPU call is made."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import zero_sharded_mixed_reduce_amd as z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+PROGRAM = r"""
+#include <stdio.h>
+#include "zsmr.h"
+int main(void) {
+    const int64_t resident[4] = {128, 56, 44, 32};
+    const int64_t traffic[4] = {12, 12, 12, 18};
+    for (int32_t stage = 0; stage < 4; ++stage) {
+        zsmr_ctx* c = NULL;
+        zsmr_bytes b;
+        if (zero_init_shards(&c, 8, 4, stage, ZSMR_FP16, ZSMR_FP16, 0, NULL, 0) != ZSMR_OK) return 2;
+        if (zero_bytes_per_rank(c, 0, 0, &b) != ZSMR_OK) return 3;
+        printf("stage %d resident %lld traffic %lld\n", stage, (long long)b.resident,
+               (long long)b.traffic_elems);
+        if (b.resident != resident[stage] || b.traffic_elems != traffic[stage]) return 4;
+        zero_destroy(c);
+    }
+    zsmr_ctx* bad = NULL;
+    if (zero_init_shards(&bad, 10, 4, 1, ZSMR_BF16, ZSMR_BF16, 0, NULL, 0) != ZSMR_ERR_INDIVISIBLE)
+        return 5;
+    if (bad != NULL) return 6;
+    printf("%s\n", zsmr_strerror(ZSMR_ERR_INDIVISIBLE));
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs a C compiler")
+def test_a_c_program_uses_the_library(tmp_path):
+    src = tmp_path / "zsmr_from_c.c"
+    src.write_text(PROGRAM)
+    exe = tmp_path / "zsmr_from_c"
+    pkg = os.path.dirname(z.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), str(src),
+           "-L", pkg, "-lzsmr", f"-Wl,-rpath,{pkg}", f"-Wl,-rpath-link,{os.path.join(ROCM, 'lib')}",
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "stage 3 resident 32 traffic 18" in r.stdout
