@@ -178,8 +178,9 @@ def tune_write_window(share, reps: int = 6) -> dict:
 def references(z, nbytes: int, reps: int = 5) -> dict:
     """Rates this device gives simple streams of the receive's size, measured
     in the same process on two fresh, equally aligned buffers of ``nbytes``:
-    the library's 128-bit copy (GB/s of reads + writes), and the best pure
-    read and pure write rates of the reference streams in ``ceiling/``."""
+    the library's 128-bit copy and the runtime's device-to-device copy (GB/s
+    of reads + writes), and the best pure read and pure write rates of the
+    reference streams in ``ceiling/``."""
     import torch
     import ceiling
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
@@ -196,10 +197,21 @@ def references(z, nbytes: int, reps: int = 5) -> dict:
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # the runtime's own device-to-device copy (hipMemcpyAsync, behind torch's
+    # copy_) on the same buffers, for comparison only
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_vendor = e0.elapsed_time(e1) / reps
     pure = ceiling.measure(dst, nbytes, reps)
     del src, dst
     torch.cuda.empty_cache()
-    return {"copy_GBps": 2 * nbytes / ms / 1e6, "pure": pure}
+    return {"copy_GBps": 2 * nbytes / ms / 1e6, "runtime_copy_GBps": 2 * nbytes / ms_vendor / 1e6,
+            "pure": pure}
 
 
 def phased(parts: dict, rw: dict, pure: dict) -> dict:
@@ -432,6 +444,7 @@ def main():
         ref = references(z, REFERENCE_BYTES)
         if "peer_receive" in parts:
             line["copy_reference_GBps"] = round(ref["copy_GBps"], 1)
+            line["runtime_d2d_copy_GBps"] = round(ref["runtime_copy_GBps"], 1)
             parts["peer_receive"]["frac_of_copy_reference"] = round(
                 parts["peer_receive"]["GBps"] / ref["copy_GBps"], 4)
         line["phased_bound"] = phased(parts, rw, ref["pure"])
