@@ -262,6 +262,37 @@ def bucketed_overlap(share, args, reps: int = 5) -> dict:
             "hidden_fraction_of_step": round((seq - buck) / (seq - fill), 4) if seq > fill else None}
 
 
+def unfused_step(share, args, reps: int = 10) -> dict:
+    """The fused pass's work done by the three unfused calls (reduce to an
+    fp32 gradient, Adam, cast), timed with HIP events on the launch stream:
+    12 more bytes per element (the gradient written and read back, the
+    master read again) and three launches."""
+    import torch
+    stream = torch.cuda.current_stream()
+    g_tmp = torch.empty(share.S, dtype=torch.float32, device=share.master.device)
+    import zero_sharded_mixed_reduce_amd as z
+    w, S = share.w, share.S
+
+    def step(t):
+        z.zero_reduce_shard(share.ctx, share.rank, 0, share.grads, share.row_stride, 0, True, g_tmp)
+        z.zero_adam_step(share.master, share.m, share.v, g_tmp, S, t, w.lr, w.betas, w.eps)
+        z.zero_gather_cast(share.ctx, share.rank, 0, share.master, share.wc[share.off:])
+
+    t0 = args.warmup + args.steps + 1
+    step(t0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        step(t0 + 1 + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    byts = share.S * (2 * share.w.world + 26 + 12)
+    del g_tmp
+    return {"ms": round(ms, 4), "bytes": byts, "GBps": round(byts / ms / 1e6, 1)}
+
+
 def bench_share64(args, w):
     import torch
     import workloads as wl
@@ -296,6 +327,7 @@ def bench_share64(args, w):
 
     S, N = share.S, w.world
     bucketed = bucketed_overlap(share, args) if args.buckets else None
+    unfused = unfused_step(share, args) if args.unfused else None
     fused_bytes = S * (2 * N + 26)              # N x 2 B grads, 24 B master/m/v r+w, 2 B cast
     recv_bytes = (share.P - S) * 4              # 2 B read + 2 B written per peer element
     parts = {
@@ -309,6 +341,9 @@ def bench_share64(args, w):
     }
     if bucketed:
         parts["bucketed_with_backward"] = bucketed
+    if unfused:
+        unfused["fused_over_unfused_time"] = round(fused_ms / unfused["ms"], 4)
+        parts["unfused_step"] = unfused
     dom = "fused_step" if fused_ms >= recv_ms else "peer_receive"
     fused_kernel = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
                     else "step_vec8_kernel")
@@ -404,6 +439,8 @@ def main():
                     help="ZeRO-3 workload: gather the next unit while the current one is in use")
     ap.add_argument("--owner", action="store_true",
                     help="ZeRO-3 workload: whole units owned by single ranks (owner broadcast)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="share64: also time the same update by the three unfused calls")
     ap.add_argument("--buckets", type=int, default=0,
                     help="share64: also measure steps with the simulated backward, bucketed")
     args = ap.parse_args()
