@@ -21,6 +21,7 @@ from tests.gpu_helpers import compare, host16, say
 pytestmark = pytest.mark.gpu
 
 WINDOW = 2048
+N_RANDOM = 1 << 20          # random indices sampled per full-size check
 
 
 def windows(starts_ends, lo, hi, n_random, seed):
@@ -75,7 +76,7 @@ def test_sharded_world_full_size(key):
         marks += [r * S, (r + 1) * S - 1]
     # fp32 byte offsets 2^31 and 2^32 (elements 2^29, 2^30) where they exist
     marks += [P - 1, P // 2] + [e for e in (1 << 29, 1 << 30) if e < w.numel]
-    pos = windows(marks, 0, w.numel, 1 << 16, seed=len(key))
+    pos = windows(marks, 0, w.numel, N_RANDOM, seed=len(key))
     check_sampled(w, pos, gather_at(world.master, pos).cpu().numpy(), gather_at(world.m, pos).cpu().numpy(),
                   gather_at(world.v, pos).cpu().numpy(), host16(gather_at(world.wc, pos)), f"{key} sampled")
     assert cast_matches(world.master, world.wc, w.dtype) == 0
@@ -100,7 +101,7 @@ def test_rank_share_full_size(rank):
     share.run(w.steps)
     torch.cuda.synchronize()
     S, off, P = share.S, share.off, share.P
-    pos = windows([0, S - 1, S // 2, (S // 512) * 512, S - 600], 0, S, 1 << 16, seed=rank)
+    pos = windows([0, S - 1, S // 2, (S // 512) * 512, S - 600], 0, S, N_RANDOM, seed=rank)
     check_sampled(w, off + pos, gather_at(share.master, pos).cpu().numpy(),
                   gather_at(share.m, pos).cpu().numpy(), gather_at(share.v, pos).cpu().numpy(),
                   host16(gather_at(share.wc, off + pos)), f"share64 rank {rank} sampled")
@@ -160,7 +161,7 @@ def test_stage3_llama8b_full_size():
             off, n = lay.owned(r, u)
             marks += [off, off + n - 1]
     marks += [(1 << 31), (1 << 32), lay.padded_numel - 1]
-    pos = windows(marks, 0, lay.padded_numel, 1 << 16, seed=8)
+    pos = windows(marks, 0, lay.padded_numel, N_RANDOM, seed=8)
     par, ok = lay.padded_to_param(pos)
     assert ok.all()                                   # every unit divides by 8: no pad
     check_sampled(w, par, gather_at(s3.master, pos).cpu().numpy(), gather_at(s3.m, pos).cpu().numpy(),
@@ -380,7 +381,7 @@ def test_owner_broadcast_llama8b_full_size():
     for u in range(lay.n_units):
         marks += [lay.unit_start[u], lay.unit_start[u] + lay.units[u] - 1]
     marks += [(1 << 31), (1 << 32), w.numel - 1]
-    pos = windows(marks, 0, w.numel, 1 << 16, seed=9)
+    pos = windows(marks, 0, w.numel, N_RANDOM, seed=9)
     check_sampled(w, pos, gather_at(s3.master, pos).cpu().numpy(), gather_at(s3.m, pos).cpu().numpy(),
                   gather_at(s3.v, pos).cpu().numpy(), host16(gather_at(s3.p16, pos)),
                   "llama8b owner sampled")
