@@ -112,11 +112,20 @@ def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0):
         reps += 1
         elapsed = time.perf_counter() - t0
     params = reps * w.steps * window
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": params / elapsed, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"window of {window} owned elements of rank 0 (of {117_187_500}), all "
                       f"{w.world} bf16 contributions, {w.steps} Adam steps + cast + the same "
                       f"window of the {w.world - 1} peer slices, repeated {reps}x "
-                      f"({elapsed:.1f} s); NumPy single-threaded"}
+                      f"({elapsed:.1f} s); NumPy single-threaded on one core of {cpu}"}
 
 
 def warm(step, warmup: int, min_seconds: float = 1.0) -> None:
