@@ -85,33 +85,55 @@ def read_traffic(kernel: str, workload: str, field: str = "hbm_bytes_per_launch"
         return None
 
 
-def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0):
-    """The oracle, untuned, on a window of the rank's shard (all N
-    contributions, T Adam steps and the same window of the 63 peer slices),
-    repeated until at least ``min_seconds`` of CPU work.  Inputs are made
-    before the clock starts; one gradient set serves every step."""
+def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0, threads: int = 0):
+    """The oracle, untuned, timed on the host's cores: each of ``threads``
+    threads (default: the cores this process may use, at most 16) runs it on
+    its own window of the rank's shard (all N contributions, T Adam steps and
+    the same window of the 63 peer slices), repeated until ``min_seconds``
+    have passed; NumPy releases the interpreter lock inside its array
+    operations, so the threads run in parallel.  Inputs are made before the
+    clock starts; one gradient set serves every step."""
+    import threading
+
     import numpy as np
     import synth
     from oracle import numerics as nm
 
-    p = np.arange(window, dtype=np.int64)
-    rows16 = [synth.grad16(w.seed, r, 1, p, w.grad_sigma, w.dtype) for r in range(w.world)]
-    peers = np.stack(rows16[1:])          # 63 slices of 16-bit values to copy
-    theta = synth.theta0(w.seed, p)
-    wc = np.zeros((w.world, window), np.uint16)
-    reps, elapsed = 0, 0.0
-    t0 = time.perf_counter()
-    while elapsed < min_seconds:
-        master, m, v = theta.copy(), np.zeros(window, np.float32), np.zeros(window, np.float32)
-        for t in range(1, w.steps + 1):
-            g = nm.reduce_rank_order([nm.widen16(r, w.dtype) for r in rows16])
-            k = nm.adam_consts(w.lr, w.betas[0], w.betas[1], w.eps, t)
-            master, m, v = nm.adam_update(master, m, v, g, k)
-            wc[0] = nm.cast16(master, w.dtype)
-            wc[1:] = peers
-        reps += 1
-        elapsed = time.perf_counter() - t0
-    params = reps * w.steps * window
+    if threads <= 0:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    start = threading.Barrier(threads + 1)
+    reps = [0] * threads
+    ends = [0.0] * threads
+    t0 = [0.0]
+
+    def run(k):
+        p = np.arange(k * window, (k + 1) * window, dtype=np.int64)
+        rows16 = [synth.grad16(w.seed, r, 1, p, w.grad_sigma, w.dtype) for r in range(w.world)]
+        peers = np.stack(rows16[1:])          # 63 slices of 16-bit values to copy
+        theta = synth.theta0(w.seed, p)
+        wc = np.zeros((w.world, window), np.uint16)
+        start.wait()
+        while time.perf_counter() - t0[0] < min_seconds:
+            master, m, v = theta.copy(), np.zeros(window, np.float32), np.zeros(window, np.float32)
+            for t in range(1, w.steps + 1):
+                g = nm.reduce_rank_order([nm.widen16(r, w.dtype) for r in rows16])
+                c = nm.adam_consts(w.lr, w.betas[0], w.betas[1], w.eps, t)
+                master, m, v = nm.adam_update(master, m, v, g, c)
+                wc[0] = nm.cast16(master, w.dtype)
+                wc[1:] = peers
+            reps[k] += 1
+        ends[k] = time.perf_counter()
+
+    pool = [threading.Thread(target=run, args=(k,)) for k in range(threads)]
+    for th in pool:
+        th.start()
+    t0[0] = time.perf_counter()
+    start.wait()
+    t0[0] = time.perf_counter()
+    for th in pool:
+        th.join()
+    elapsed = max(ends) - t0[0]
+    params = sum(reps) * w.steps * window
     cpu = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
@@ -121,11 +143,11 @@ def cpu_baseline(w, window: int = 1 << 19, min_seconds: float = 10.0):
                     break
     except OSError:
         pass
-    return {"value": params / elapsed, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"window of {window} owned elements of rank 0 (of {117_187_500}), all "
-                      f"{w.world} bf16 contributions, {w.steps} Adam steps + cast + the same "
-                      f"window of the {w.world - 1} peer slices, repeated {reps}x "
-                      f"({elapsed:.1f} s); NumPy single-threaded on one core of {cpu}"}
+    return {"value": params / elapsed, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"{threads} windows of {window} owned elements of rank 0 (of {117_187_500}), "
+                      f"all {w.world} bf16 contributions, {w.steps} Adam steps + cast + the same "
+                      f"window of the {w.world - 1} peer slices, {sum(reps)} repetitions in all "
+                      f"({elapsed:.1f} s); NumPy, one thread per window, on {cpu}"}
 
 
 def warm(step, warmup: int, min_seconds: float = 1.0) -> None:

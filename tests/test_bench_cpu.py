@@ -24,10 +24,10 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_cpu_baseline_times_the_oracle_on_a_bounded_sample():
     w = types.SimpleNamespace(seed=0, world=4, grad_sigma=1e-3, dtype="bf16", steps=2, lr=1e-4,
                               betas=(0.9, 0.999), eps=1e-8)
-    out = bench.cpu_baseline(w, window=512, min_seconds=0.05)
-    assert out["kind"] == "oracle" and out["unit"] == "params/s" and out["cores"] == 1
+    out = bench.cpu_baseline(w, window=512, min_seconds=0.05, threads=2)
+    assert out["kind"] == "oracle" and out["unit"] == "params/s" and out["cores"] == 2
     assert out["value"] > 0
-    assert "window of 512" in out["sample"]
+    assert "2 windows of 512" in out["sample"]
 
 
 def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch):
