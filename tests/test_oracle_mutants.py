@@ -61,6 +61,9 @@ ACCOUNTING_PINS = [
     ("owned ranges tile the vector", pa.test_layout_owned_ranges_tile_the_padded_vector),
     ("owner partitions", pa.test_owner_rule_gives_the_pages_contiguous_partitions),
     ("owner per-rank forms", pa.test_owner_accounting_per_rank_closed_forms),
+    ("owner peak 2/64", pa.test_owner_peak_two_64ths_either_reading),
+    ("owner = split when balanced", lambda: [pa.test_owner_balanced_equals_split_layout(w, k)
+                                             for w, k in [(4, 1), (4, 3), (8, 4), (64, 3)]]),
 ]
 
 SCHEME_PINS = [
@@ -325,6 +328,77 @@ LAYOUT_MUTANTS = {
     "shorter last shard": (lo.Layout, "owned", owned_short_last),
     "padding by floor, not ceil": (lo, "_ceil_div", lambda a, b: a // b),
 }
+
+# owner broadcast (stage 3 with whole units owned by single ranks)
+_owner_bytes = acc._owner_bytes
+
+
+def _owner_with(change):
+    def f(lay, rank, gather_bytes, max_live):
+        return change(lay, rank, _owner_bytes(lay, rank, gather_bytes, max_live), gather_bytes, max_live)
+    return f
+
+
+def _own_units_counted_as_borrowed(lay, rank, b, gather_bytes, max_live):
+    k = max(1, min(max_live, len(lay.units)))
+    g = gather_bytes * max(sum(lay.units[i:i + k]) for i in range(len(lay.units) - k + 1))
+    return dataclasses.replace(b, gathered=g, peak=b.resident + g)
+
+
+def _receives_whole_vector(lay, rank, b, gather_bytes, max_live):
+    ag = 2 * lay.numel
+    te = b.rs_elems + ag
+    return dataclasses.replace(b, ag_elems=ag, traffic_elems=te, traffic_bytes=te * acc.WIRE_BYTES)
+
+
+def _gradients_sent_twice(lay, rank, b, gather_bytes, max_live):
+    rs = 2 * b.rs_elems
+    te = rs + b.ag_elems
+    return dataclasses.replace(b, rs_elems=rs, traffic_elems=te, traffic_bytes=te * acc.WIRE_BYTES)
+
+
+def _resident_of_the_largest_owner(lay, rank, b, gather_bytes, max_live):
+    big = 16 * max(lay.own_numel(r) for r in range(lay.world))
+    return dataclasses.replace(b, resident=big, peak=big + b.gathered)
+
+
+_unit_owners = lo.unit_owners
+
+
+def owners_by_start(units, world):
+    numel, out, start = sum(units), [], 0
+    for size in units:
+        out.append(min(world - 1, world * start // numel))
+        start += size
+    return tuple(out)
+
+
+def owners_shifted(units, world):
+    return tuple(min(world - 1, o + 1) for o in _unit_owners(units, world))
+
+
+ACCOUNTING_MUTANTS.update({
+    "owner: its own units counted as borrowed": ("_owner_bytes", _owner_with(_own_units_counted_as_borrowed)),
+    "owner: every rank receives the whole vector": ("_owner_bytes", _owner_with(_receives_whole_vector)),
+    "owner: gradients sent twice": ("_owner_bytes", _owner_with(_gradients_sent_twice)),
+    "owner: resident of the largest owner": ("_owner_bytes", _owner_with(_resident_of_the_largest_owner)),
+})
+
+LAYOUT_MUTANTS.update({
+    "owners shifted by one rank": (lo, "unit_owners", owners_shifted),
+})
+
+
+def test_owner_rule_for_unequal_units_is_a_reading_not_a_pin(monkeypatch):
+    """The pages show owner broadcast only on equal partitions, where taking
+    a unit's owner from its start instead of its midpoint assigns the same
+    ranks; so every pin accepts that rule too.  For unequal units the
+    midpoint rule is a reading, and this records that no pin fixes it."""
+    monkeypatch.setattr(lo, "unit_owners", owners_by_start)
+    assert first_failing(ACCOUNTING_PINS + SCHEME_PINS) is None
+    units = [1_050_677_248] + [218_112_000] * 32            # the Llama-3-8B shape's units
+    assert owners_by_start(units, 8) != _unit_owners(units, 8)
+
 
 SCHEME_MUTANTS = {
     "ranks own each other's shards": (lo.Layout, "owned", owned_ranks_reversed),
