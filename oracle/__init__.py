@@ -30,4 +30,9 @@ gradients), so the oracle computes in fp32 with one NumPy operation per
 arithmetic step and no fused multiply-add.  Every function is pinned by
 ``tests/test_oracle_*.py`` against values printed on the pages, closed forms,
 library routines (torch casts, ``torch.optim.Adam``) or brute force.
+
+Parity unpinned: which rank owns a unit of unequal size under owner
+broadcast (``layout.unit_owners`` on unequal units).  The pages show only
+equal partitions, where the rule is pinned; for unequal units it is a
+reading (the unit's midpoint decides) that no passage fixes.
 """

@@ -135,7 +135,10 @@ class Layout:
 
 def unit_owners(units: Sequence[int], world: int) -> tuple:
     """Owner of each unit under owner broadcast: the rank whose equal share of
-    the vector holds the unit's midpoint, floor(N * (start + size/2) / Psi)."""
+    the vector holds the unit's midpoint, floor(N * (start + size/2) / Psi).
+    On equal partitions this gives the pages' k consecutive units per rank
+    ("One Poem Suffices: ZeRO" section 4.1.4; "ZeRO, annotated" section 7);
+    on unequal units it is a reading, parity unpinned."""
     numel = sum(units)
     owners, start = [], 0
     for size in units:
