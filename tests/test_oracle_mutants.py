@@ -21,6 +21,7 @@ import test_oracle_schemes as ps
 from oracle import accounting as acc
 from oracle import layout as lo
 from oracle import numerics as nm
+from oracle import sampled
 from oracle import schemes as sc
 
 # ------------------------------------------------------------ the pins ------
@@ -400,9 +401,34 @@ def test_owner_rule_for_unequal_units_is_a_reading_not_a_pin(monkeypatch):
     assert owners_by_start(units, 8) != _unit_owners(units, 8)
 
 
+def trajectory_variant(drop_last_rank=False, grads_of_step_before=False):
+    """The sampled oracle's per-element trajectory with one planted mistake."""
+    import synth
+
+    def trajectory(p_idx, world, steps, dtype16, grad_sigma, lr, betas=(0.9, 0.999), eps=1e-8,
+                   seed=0, outlier_permyriad=0, theta_sigma=0.02):
+        p_idx = np.asarray(p_idx, dtype=np.int64)
+        master = synth.theta0(seed, p_idx, theta_sigma)
+        m = np.zeros(p_idx.shape, np.float32)
+        v = np.zeros(p_idx.shape, np.float32)
+        for t in range(1, steps + 1):
+            gs = max(1, t - 1) if grads_of_step_before else t
+            ranks = range(world - 1) if drop_last_rank and world > 1 else range(world)
+            rows = [nm.widen16(synth.grad16(seed, r, gs, p_idx, grad_sigma, dtype16, outlier_permyriad),
+                               dtype16) for r in ranks]
+            g = nm.reduce_rank_order(rows)
+            k = nm.adam_consts(lr, betas[0], betas[1], eps, t)
+            master, m, v = nm.adam_update(master, m, v, g, k)
+        return master, m, v, nm.cast16(master, dtype16)
+    return trajectory
+
+
 SCHEME_MUTANTS = {
     "ranks own each other's shards": (lo.Layout, "owned", owned_ranks_reversed),
     "step counter advances per call of Adam": (sc._Scheme, "_consts", consts_per_unit_clock),
+    "sampled oracle drops the last rank": (sampled, "trajectory", trajectory_variant(drop_last_rank=True)),
+    "sampled oracle reuses the previous step's gradients":
+        (sampled, "trajectory", trajectory_variant(grads_of_step_before=True)),
 }
 
 
