@@ -98,7 +98,7 @@ typedef struct zsmr_layout_info {
  * peak_bytes_per_param; "ZeRO and FSDP": the three-stage table).  Sharded
  * bands count the padded shard, unsharded bands the true Psi.  Traffic is
  * the elements one rank sends per step: DP one all-reduce of 2(N-1)
- * chunks of ceil(Psi/N); stages 1-2 a reduce-scatter plus an all-gather of
+ * chunks of ceil(Psi/N); stages 1-2 one reduce-scatter and one all-gather of
  * (N-1)*S each; stage 3 a reduce-scatter plus two all-gathers of
  * (N-1)*sum(S_u) each ("ZeRO, annotated" section 7).  Stage 4, rank r owning
  * own(r) elements: 16*own(r) resident; it receives the Psi - own(r) elements

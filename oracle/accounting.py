@@ -44,12 +44,21 @@ from dataclasses import dataclass
 
 from .layout import Layout
 
-B_P16, B_GRAD, B_MASTER, B_M, B_V = 2, 2, 4, 4, 4
+# Bytes one element occupies in each band: the 16-bit working parameters and
+# gradients, and the fp32 master copy and Adam's two moments (16 in all).
+BAND_BYTES = {"p16": 2, "grad": 2, "master": 4, "m": 4, "v": 4}
+BANDS = tuple(BAND_BYTES)
+
+# Bytes per element on the wire: the collectives move 16-bit values.
 WIRE_BYTES = 2
 
-# (shard_opt, shard_grad, shard_param) per stage
-FLAGS = {0: (False, False, False), 1: (True, False, False),
-         2: (True, True, False), 3: (True, True, True)}
+# The bands each stage splits N ways (the others every rank holds whole):
+# stage 1 the optimizer state, stage 2 also the gradients, stage 3 also the
+# working parameters.
+SHARDED_BANDS = {0: frozenset(),
+                 1: frozenset({"master", "m", "v"}),
+                 2: frozenset({"master", "m", "v", "grad"}),
+                 3: frozenset(BANDS)}
 
 
 @dataclass(frozen=True)
@@ -76,20 +85,20 @@ def _ceil_div(a: int, b: int) -> int:
 
 def _owner_bytes(lay: Layout, rank: int, gather_bytes: int, max_live: int) -> Bytes:
     own = lay.own_numel(rank)
-    p16, grad, master, m, v = B_P16 * own, B_GRAD * own, B_MASTER * own, B_M * own, B_V * own
-    resident = p16 + grad + master + m + v
+    res = {band: BAND_BYTES[band] * own for band in BANDS}
+    resident = sum(res.values())
     borrowed = [0 if o == rank else size for size, o in zip(lay.units, lay.owners)]
     k = max(1, min(max_live, len(borrowed)))
     gathered = gather_bytes * max(sum(borrowed[i:i + k]) for i in range(len(borrowed) - k + 1))
-    unit_grad = B_GRAD * max(lay.units)
+    unit_grad = BAND_BYTES["grad"] * max(lay.units)
     rs = lay.numel - own
     ag = 2 * (lay.numel - own)
     elems = rs + ag
-    return Bytes(p16, grad, master, m, v, resident, gathered, resident + gathered, unit_grad,
+    return Bytes(*(res[band] for band in BANDS), resident, gathered, resident + gathered, unit_grad,
                  rs, ag, 0, elems, elems * WIRE_BYTES)
 
 
-def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1,
+def bytes_per_rank(lay: Layout, gather_bytes: int = 2, max_live: int = 1,
                    rank=None) -> Bytes:
     if lay.owner_broadcast:
         if rank is not None:
@@ -97,13 +106,10 @@ def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1,
         per = [_owner_bytes(lay, r, gather_bytes, max_live) for r in range(lay.world)]
         return max(per, key=lambda b: b.peak)        # max() keeps the first (lowest) rank on ties
     n, w = lay.numel, lay.world
-    shard_opt, shard_grad, shard_param = FLAGS[lay.stage]
+    sharded = SHARDED_BANDS[lay.stage]
     s_tot = lay.shard_numel if lay.stage else n
-    p16 = B_P16 * (s_tot if shard_param else n)
-    grad = B_GRAD * (s_tot if shard_grad else n)
-    opt_elems = s_tot if shard_opt else n
-    master, m, v = B_MASTER * opt_elems, B_M * opt_elems, B_V * opt_elems
-    resident = p16 + grad + master + m + v
+    res = {band: BAND_BYTES[band] * (s_tot if band in sharded else n) for band in BANDS}
+    resident = sum(res.values())
 
     gathered = 0
     unit_grad = 0
@@ -111,7 +117,7 @@ def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1,
         widths = [w * s for s in lay.shard_u]
         k = max(1, min(max_live, len(widths)))
         gathered = gather_bytes * max(sum(widths[i:i + k]) for i in range(len(widths) - k + 1))
-        unit_grad = B_GRAD * max(widths)
+        unit_grad = BAND_BYTES["grad"] * max(widths)
     peak = resident + gathered
 
     rs = ag = ar = 0
@@ -124,11 +130,11 @@ def bytes_per_rank(lay: Layout, gather_bytes: int = B_P16, max_live: int = 1,
         rs = (w - 1) * s_tot
         ag = 2 * (w - 1) * s_tot
     elems = rs + ag + ar
-    return Bytes(p16, grad, master, m, v, resident, gathered, peak, unit_grad,
+    return Bytes(*(res[band] for band in BANDS), resident, gathered, peak, unit_grad,
                  rs, ag, ar, elems, elems * WIRE_BYTES)
 
 
-def bytes_per_param(lay: Layout, gather_bytes: int = B_P16):
+def bytes_per_param(lay: Layout, gather_bytes: int = 2):
     """(resident, peak) per parameter, as the prototype prints them."""
     b = bytes_per_rank(lay, gather_bytes)
     return b.resident / lay.numel, b.peak / lay.numel

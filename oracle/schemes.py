@@ -1,4 +1,5 @@
-"""Data parallel and ZeRO stages 1-3 over N simulated ranks, on the CPU.
+"""The four schemes (plain data parallelism, ZeRO-1, ZeRO-2, ZeRO-3) run for
+N ranks simulated on the CPU.
 
 Test infrastructure only (see the package header).
 

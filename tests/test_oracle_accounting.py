@@ -58,7 +58,7 @@ def quantity(pin):
     if q == "traffic_bytes_x_n_over_psi":
         return Decimal(b.traffic_bytes) * pin["world"] / ((pin["world"] - 1) * Decimal(pin["numel"]))
     if q == "peak_params_x_n_over_psi":
-        held = Decimal(b.res_p16) / acc.B_P16 + Decimal(b.gathered) / pin["gather_bytes"]
+        held = Decimal(b.res_p16) / acc.BAND_BYTES["p16"] + Decimal(b.gathered) / pin["gather_bytes"]
         return held * pin["world"] / Decimal(pin["numel"])
     raise KeyError(q)
 
@@ -75,7 +75,8 @@ def test_page_printed_value(pin):
 
 def test_sixteen_bytes_per_parameter():
     # "One Poem Suffices: ZeRO" s3.1: 2 + 2 + 3*4 = 16 bytes per parameter
-    assert acc.B_P16 + acc.B_GRAD + acc.B_MASTER + acc.B_M + acc.B_V == 16
+    assert sum(acc.BAND_BYTES.values()) == 16
+    assert acc.BAND_BYTES == {"p16": 2, "grad": 2, "master": 4, "m": 4, "v": 4}
 
 
 @pytest.mark.parametrize("numel,world", [(8, 4), (65536, 4), (124439808, 8), (7_500_000_000, 64),

@@ -40,7 +40,7 @@ NUMERIC_PINS = [
     ("adam t=1 closed form", pn.test_adam_first_step_closed_form),
     ("adam constant-g closed form", pn.test_adam_constant_gradient_closed_form),
     ("adam vs torch.optim.Adam", pn.test_adam_matches_torch_optim_adam),
-    ("zero_check replay", pn.test_zero_check_replay),
+    ("small MLP against torch.optim.Adam", pn.test_sharded_adam_on_a_small_mlp_matches_torch_adam),
 ]
 
 
@@ -236,7 +236,7 @@ _bytes_per_rank = acc.bytes_per_rank
 
 def _bytes_with(change):
     """bytes_per_rank with one field rule changed after the fact."""
-    def f(lay, gather_bytes=acc.B_P16, max_live=1, rank=None):
+    def f(lay, gather_bytes=2, max_live=1, rank=None):
         b = _bytes_per_rank(lay, gather_bytes, max_live, rank)
         b2 = change(lay, b)
         if b2 is not b:
@@ -278,12 +278,12 @@ ACCOUNTING_MUTANTS = {
     "collectives send N shards, not N - 1": ("bytes_per_rank", _bytes_with(_traffic_all_n)),
     "stage-3 peak omits the gathered unit": ("bytes_per_rank", _bytes_with(_peak_without_gather)),
     "gradient band not counted": ("bytes_per_rank", _bytes_with(_resident_drops_grad)),
-    "stage 2 keeps full gradients": ("FLAGS", {**acc.FLAGS, 2: (True, False, False)}),
-    "stage 1 shards gradients": ("FLAGS", {**acc.FLAGS, 1: (True, True, False)}),
-    "stage 3 keeps full parameters": ("FLAGS", {**acc.FLAGS, 3: (True, True, False)}),
+    "stage 2 keeps full gradients": ("SHARDED_BANDS", {**acc.SHARDED_BANDS, 2: frozenset({"master", "m", "v"})}),
+    "stage 1 shards gradients": ("SHARDED_BANDS", {**acc.SHARDED_BANDS, 1: frozenset({"master", "m", "v", "grad"})}),
+    "stage 3 keeps full parameters": ("SHARDED_BANDS", {**acc.SHARDED_BANDS, 3: acc.SHARDED_BANDS[2]}),
     "fp32 on the wire": ("WIRE_BYTES", 4),
-    "master counted at 2 bytes": ("B_MASTER", 2),
-    "gradients counted at 4 bytes": ("B_GRAD", 4),
+    "master counted at 2 bytes": ("BAND_BYTES", {**acc.BAND_BYTES, "master": 2}),
+    "gradients counted at 4 bytes": ("BAND_BYTES", {**acc.BAND_BYTES, "grad": 4}),
 }
 
 
