@@ -164,12 +164,12 @@ def make_layout(numel: int, world: int, stage: int, units: Optional[Sequence[int
         shard_u = (numel,)
     elif stage in (1, 2):
         if numel % world and not pad:
-            raise IndivisibleError("parameter count must divide by world size")
+            raise IndivisibleError(f"{numel} parameters do not split into {world} equal shards (pad=True pads)")
         shard_u = (_ceil_div(numel, world),)
     else:
         for u in unit_list:
             if u % world and not pad:
-                raise IndivisibleError("unit size must divide by world size")
+                raise IndivisibleError(f"a unit of {u} parameters does not split into {world} equal shards")
         shard_u = tuple(_ceil_div(u, world) for u in unit_list)
     if stage == 3:
         pstarts = tuple(sum(world * s for s in shard_u[:i]) for i in range(len(shard_u)))

@@ -134,7 +134,7 @@ class _Scheme:
         if theta0.shape != (lay.numel,):
             raise ValueError("theta0 must hold Psi fp32 values")
         self.lay, self.dtype = lay, dtype16
-        self.lr, self.b1, self.b2, self.eps = lr, betas[0], betas[1], eps
+        self.hyper = (float(lr), float(betas[0]), float(betas[1]), float(eps))   # lr, beta1, beta2, eps
         self.t = 0
         self.rs_elems = [0] * lay.world     # received per rank
         self.ag_elems = [0] * lay.world
@@ -161,7 +161,7 @@ class _Scheme:
                                for u in range(lay.n_units)])
 
     def _consts(self) -> nm.AdamConsts:
-        return nm.adam_consts(self.lr, self.b1, self.b2, self.eps, self.t)
+        return nm.adam_consts(*self.hyper, self.t)
 
     def _rows(self, grads16: Sequence[np.ndarray]) -> List[np.ndarray]:
         if len(grads16) != self.lay.world:

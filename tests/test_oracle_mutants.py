@@ -321,7 +321,7 @@ def consts_per_unit_clock(self):
     # t advanced by one more each time the constants are taken: as if the step
     # counter moved per unit or per rank instead of once per step
     self._extra = getattr(self, "_extra", 0) + 1
-    return nm.adam_consts(self.lr, self.b1, self.b2, self.eps, self.t + self._extra - 1)
+    return nm.adam_consts(*self.hyper, self.t + self._extra - 1)
 
 
 LAYOUT_MUTANTS = {
