@@ -25,13 +25,12 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m zero_sharded_mixed_reduce_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
+        from zero_sharded_mixed_reduce_amd import checked_library
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-        lib.zsmr_ceiling_read.restype = i32
-        lib.zsmr_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
-        lib.zsmr_ceiling_write.restype = i32
-        lib.zsmr_ceiling_write.argtypes = [vp, i64, i32, ctypes.c_uint32, vp]
-        _LIB = lib
+        _LIB = checked_library(LIB_PATH, {
+            "zsmr_ceiling_read": (i32, [vp, i64, i32, vp, vp]),
+            "zsmr_ceiling_write": (i32, [vp, i64, i32, ctypes.c_uint32, vp]),
+        })
     return _LIB
 
 

@@ -60,6 +60,16 @@ extern "C" {
 #define ZSMR_ERR_ALIGN       5  /* pointer not aligned to its element size    */
 #define ZSMR_ERR_HIP         6  /* a HIP runtime call or launch failed        */
 
+/* Size limits of a context.  Within them every element count, byte count
+ * and traffic figure the library computes fits in int64_t with room to
+ * spare: 2^56 elements is over 7e16 parameters, a world of 2^20 ranks and
+ * 2^20 units exceed anything the pages consider. */
+#define ZSMR_MAX_NUMEL ((int64_t)1 << 56)
+#define ZSMR_MAX_WORLD (1 << 20)
+#define ZSMR_MAX_UNITS (1 << 20)
+/* largest bytes per gathered element an accounting call accepts (8: fp64) */
+#define ZSMR_MAX_GATHER_BYTES 8
+
 /* 16-bit formats of gradients and of the working copy */
 #define ZSMR_FP16 1
 #define ZSMR_BF16 2
@@ -146,7 +156,9 @@ const char* zsmr_last_hip_error(void);
  * their natural order: unit u goes to the rank whose equal share
  * [r*Psi/N, (r+1)*Psi/N) holds the unit's midpoint (with U = k*N equal units
  * the pages' k consecutive units per rank); pad is ignored.  *out receives a
- * context to free with zero_destroy(). */
+ * context to free with zero_destroy().  ZSMR_ERR_ARG if numel exceeds
+ * ZSMR_MAX_NUMEL, world ZSMR_MAX_WORLD or n_units ZSMR_MAX_UNITS, or if the
+ * host allocation of the context fails; *out is then NULL. */
 int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
                          int32_t grad_dtype, int32_t param_dtype, int32_t pad,
                          const int64_t* unit_numel, int32_t n_units);
@@ -172,7 +184,9 @@ int32_t zero_unit_owner(const zsmr_ctx* ctx, int32_t unit, int32_t* owner);
  * gathered element of the stage-3 peak (0 = the 16-bit working copy's 2; the
  * prototype's fp32 gather is 4).  max_live: units gathered at once (0 = 1;
  * 2 = prefetch of the next unit).  Ranks are alike at stages 0-3; at stage 4
- * this reports the rank with the largest peak (the lowest such rank). */
+ * this reports the rank with the largest peak (the lowest such rank).
+ * ZSMR_ERR_ARG if gather_bytes is negative or above ZSMR_MAX_GATHER_BYTES,
+ * or max_live is negative. */
 int32_t zero_bytes_per_rank(const zsmr_ctx* ctx, int32_t gather_bytes, int32_t max_live,
                             zsmr_bytes* out);
 

@@ -29,6 +29,20 @@ def _lib():
     return _LIB
 
 
+# ctypes truncates a Python int that does not fit its C type; refuse instead
+_RANGE = {ctypes.c_int32: (-(1 << 31), (1 << 31) - 1), ctypes.c_int64: (-(1 << 63), (1 << 63) - 1),
+          ctypes.c_uint32: (0, (1 << 32) - 1)}
+
+
+def _call(name: str, *args):
+    fn = getattr(_lib(), name)
+    for i, (x, t) in enumerate(zip(args, fn.argtypes)):
+        r = _RANGE.get(t)
+        if r is not None and isinstance(x, int) and not r[0] <= x <= r[1]:
+            raise ValueError(f"{name}: argument {i} = {x} is outside [{r[0]}, {r[1]}]")
+    return fn(*args)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -49,15 +63,15 @@ def _ptr(x):
 def fill16(dst, rows: int, row_stride: int, n: int, p0: int, p_valid: int, seed: int, tag: int,
            rank0: int, step: int, sigma: float, dtype: str, outlier_permyriad: int = 0,
            stream=None) -> None:
-    code = _lib().zsmr_synth_fill16(_ptr(dst), rows, row_stride, n, p0, p_valid, seed, tag, rank0,
-                                    step, sigma, _CODES[dtype], outlier_permyriad, _stream(stream))
+    code = _call("zsmr_synth_fill16", _ptr(dst), rows, row_stride, n, p0, p_valid, seed, tag,
+                 rank0, step, sigma, _CODES[dtype], outlier_permyriad, _stream(stream))
     if code:
         raise RuntimeError(f"zsmr_synth_fill16 failed with code {code}")
 
 
 def fill32(dst, n: int, p0: int, p_valid: int, seed: int, tag: int, rank: int, step: int,
            sigma: float, stream=None) -> None:
-    code = _lib().zsmr_synth_fill32(_ptr(dst), n, p0, p_valid, seed, tag, rank, step, sigma,
-                                    _stream(stream))
+    code = _call("zsmr_synth_fill32", _ptr(dst), n, p0, p_valid, seed, tag, rank, step, sigma,
+                 _stream(stream))
     if code:
         raise RuntimeError(f"zsmr_synth_fill32 failed with code {code}")

@@ -434,3 +434,50 @@ def test_undersized_or_strided_tensors_are_refused_before_any_call():
         for rank in range(4):
             assert z.zero_counters(c, rank)["traffic_elems"] == 0
     assert z.zero_stage3_unit_state(s3, 1) == (False, 0, 0)
+
+
+def test_integers_that_do_not_fit_their_c_type_are_refused():
+    """ctypes would pass 2**32 + 4 as an int32_t 4: the bindings refuse it."""
+    import ceiling
+    import synth.gpu as sg
+    with pytest.raises(ValueError, match="argument 2"):
+        z.zero_init_shards(64, (1 << 32) + 4, 2, "bf16")
+    with pytest.raises(ValueError, match="argument 1"):
+        z.zero_init_shards(1 << 64, 4, 2, "bf16")
+    ctx = z.zero_init_shards(64, 4, 2, "bf16")
+    with pytest.raises(ValueError, match="argument 1"):
+        z.zero_layout(ctx, (1 << 32) + 1, 0)
+    with pytest.raises(ValueError, match="argument 10"):           # t
+        z.zero_fused_step(ctx, 0, 0, 1 << 20, 64, 0, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                          (1 << 32) + 1, 1e-3, stream=0)
+    with pytest.raises(ValueError, match="argument 5"):            # count of blocks
+        z.zero_gather_copy_blocks(ctx, 0, 1 << 20, 1 << 40, 10, (1 << 32) + 2, 100, stream=0)
+    with pytest.raises(ValueError, match="argument 4"):            # seed
+        sg.fill32(1 << 20, 4, 0, 4, 1 << 32, 0, 0, 1, 1.0, stream=0)
+    with pytest.raises(ValueError, match="argument 1"):
+        ceiling.read(1 << 20, -(1 << 63) - 1, 0, 1 << 21, stream=0)
+    for rank in range(4):
+        assert z.zero_counters(ctx, rank)["traffic_elems"] == 0
+
+
+def test_size_limits_of_a_context():
+    """Sizes past the documented limits are refused before anything is
+    allocated; at the limits every byte and traffic figure is exact."""
+    MAX_NUMEL, MAX_WORLD, MAX_UNITS = 1 << 56, 1 << 20, 1 << 20
+    for numel, world in ((MAX_NUMEL + 1, 4), ((1 << 63) - 1, 3), (8, MAX_WORLD + 1)):
+        for stage in range(5):
+            with pytest.raises(z.ZsmrError) as e:
+                z.zero_init_shards(numel, world, stage, "bf16", pad=True)
+            assert e.value.code == z.ZSMR_ERR_ARG
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 1)(8)
+    assert z.load().zero_init_shards(ctypes.byref(h), 8, 1, 3, 2, 2, 0, arr, MAX_UNITS + 1) \
+        == z.ZSMR_ERR_ARG and not h.value
+    ctx = z.zero_init_shards(MAX_NUMEL, 64, 3, "bf16")
+    b = z.zero_bytes_per_rank(ctx, gather_bytes=8, max_live=2)
+    S = MAX_NUMEL // 64
+    assert b["resident"] == 16 * S and b["gathered"] == 8 * MAX_NUMEL
+    assert b["traffic_bytes"] == 2 * 3 * 63 * S
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_bytes_per_rank(ctx, gather_bytes=9)
+    assert e.value.code == z.ZSMR_ERR_ARG

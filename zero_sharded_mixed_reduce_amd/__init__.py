@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import types
 from typing import Optional, Sequence
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,39 @@ SIGNATURES = {
 
 _LIB = None
 
+# ctypes converts a Python int to a C integer by truncation (2**32 + 4 passed
+# as int32_t arrives as 4), so every integer argument is range-checked first.
+_INT_RANGE = {ctypes.c_int32: (-(1 << 31), (1 << 31) - 1),
+              ctypes.c_int64: (-(1 << 63), (1 << 63) - 1),
+              ctypes.c_uint32: (0, (1 << 32) - 1)}
+
+
+class CheckedFunction:
+    """A ctypes function whose integer arguments must fit their C types."""
+
+    def __init__(self, name: str, fn, argtypes):
+        self.name, self.fn = name, fn
+        self.ranges = [_INT_RANGE.get(t) for t in argtypes]
+
+    def __call__(self, *args):
+        for i, (x, r) in enumerate(zip(args, self.ranges)):
+            if r is not None and isinstance(x, int) and not r[0] <= x <= r[1]:
+                raise ValueError(f"{self.name}: argument {i} = {x} is outside [{r[0]}, {r[1]}]")
+        return self.fn(*args)
+
+
+def checked_library(path: str, signatures: dict):
+    """Load a shared library and give it the (restype, argtypes) of each
+    named function; returns a namespace of CheckedFunction."""
+    lib = ctypes.CDLL(path)
+    fns = {}
+    for name, (res, args) in signatures.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+        fns[name] = CheckedFunction(name, fn, args)
+    return types.SimpleNamespace(**fns)
+
 
 def _lib():
     global _LIB
@@ -100,12 +134,7 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m zero_sharded_mixed_reduce_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _LIB = lib
+        _LIB = checked_library(LIB_PATH, SIGNATURES)
     return _LIB
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cmath>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <string>
 #include <vector>
@@ -137,36 +138,12 @@ void count_cast(zsmr_ctx* c, int32_t rank, int64_t len) {
             if (q != rank) c->ag[q] += len;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* zsmr_strerror(int32_t s) {
-    switch (s) {
-        case ZSMR_OK: return "ok";
-        case ZSMR_ERR_ARG: return "invalid argument";
-        case ZSMR_ERR_INDIVISIBLE: return "parameter count (or unit) not divisible by world size";
-        case ZSMR_ERR_STATE: return "ZeRO-3 gather/release out of order";
-        case ZSMR_ERR_DTYPE: return "unknown 16-bit format";
-        case ZSMR_ERR_ALIGN: return "pointer not aligned to its element size";
-        case ZSMR_ERR_HIP: return "HIP runtime error";
-        default: return "unknown status";
-    }
-}
-
-const char* zsmr_last_hip_error(void) { return g_hip_error.c_str(); }
-
-int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
-                         int32_t grad_dtype, int32_t param_dtype, int32_t pad,
-                         const int64_t* unit_numel, int32_t n_units) {
-    if (!out) return ZSMR_ERR_ARG;
-    *out = nullptr;
-    if (numel < 1 || world < 1 || stage < ZSMR_DP || stage > ZSMR_ZERO3_OWNER ||
-        (pad != 0 && pad != 1))
-        return ZSMR_ERR_ARG;
-    if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZSMR_ERR_DTYPE;
-    if (n_units < 0 || (n_units > 0 && !unit_numel) || (n_units == 0 && unit_numel))
-        return ZSMR_ERR_ARG;
+// The body of zero_init_shards once the scalar arguments are checked; the
+// vectors it fills may throw std::bad_alloc, which the caller turns into a
+// status (an exception may not cross the C ABI).
+int32_t build_ctx(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
+                  int32_t grad_dtype, int32_t param_dtype, int32_t pad,
+                  const int64_t* unit_numel, int32_t n_units) {
     std::vector<int64_t> units;
     if (n_units == 0) {
         units.push_back(numel);
@@ -179,8 +156,7 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
         }
         if (sum != numel) return ZSMR_ERR_ARG;
     }
-    zsmr_ctx* c = new (std::nothrow) zsmr_ctx;
-    if (!c) return ZSMR_ERR_ARG;
+    std::unique_ptr<zsmr_ctx> c(new zsmr_ctx);
     c->numel = numel;
     c->world = world;
     c->stage = stage;
@@ -211,7 +187,6 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
         c->shard_total = *std::max_element(c->own.begin(), c->own.end());
     } else if (stage != ZSMR_ZERO3) {
         if (numel % world && !pad) {
-            delete c;
             return ZSMR_ERR_INDIVISIBLE;
         }
         const int64_t s = ceil_div(numel, world);
@@ -224,7 +199,6 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
         int64_t q = 0, loc = 0;
         for (int64_t u : units) {
             if (u % world && !pad) {
-                delete c;
                 return ZSMR_ERR_INDIVISIBLE;
             }
             const int64_t s = ceil_div(u, world);
@@ -245,8 +219,47 @@ int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t s
     c->live.assign(units.size(), 0);
     c->live_bytes.assign(world, 0);
     c->peak_live_bytes.assign(world, 0);
-    *out = c;
+    *out = c.release();
     return ZSMR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zsmr_strerror(int32_t s) {
+    switch (s) {
+        case ZSMR_OK: return "ok";
+        case ZSMR_ERR_ARG: return "invalid argument";
+        case ZSMR_ERR_INDIVISIBLE: return "parameter count (or unit) not divisible by world size";
+        case ZSMR_ERR_STATE: return "ZeRO-3 gather/release out of order";
+        case ZSMR_ERR_DTYPE: return "unknown 16-bit format";
+        case ZSMR_ERR_ALIGN: return "pointer not aligned to its element size";
+        case ZSMR_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* zsmr_last_hip_error(void) { return g_hip_error.c_str(); }
+
+int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
+                         int32_t grad_dtype, int32_t param_dtype, int32_t pad,
+                         const int64_t* unit_numel, int32_t n_units) {
+    if (!out) return ZSMR_ERR_ARG;
+    *out = nullptr;
+    if (numel < 1 || numel > ZSMR_MAX_NUMEL || world < 1 || world > ZSMR_MAX_WORLD ||
+        stage < ZSMR_DP || stage > ZSMR_ZERO3_OWNER || (pad != 0 && pad != 1))
+        return ZSMR_ERR_ARG;
+    if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZSMR_ERR_DTYPE;
+    if (n_units < 0 || n_units > ZSMR_MAX_UNITS || (n_units > 0 && !unit_numel) ||
+        (n_units == 0 && unit_numel))
+        return ZSMR_ERR_ARG;
+    try {
+        return build_ctx(out, numel, world, stage, grad_dtype, param_dtype, pad, unit_numel,
+                         n_units);
+    } catch (const std::bad_alloc&) {
+        return ZSMR_ERR_ARG;
+    }
 }
 
 void zero_destroy(zsmr_ctx* ctx) { delete ctx; }
@@ -363,7 +376,8 @@ void even_bytes(const zsmr_ctx* c, int64_t gather_bytes, int64_t max_live, zsmr_
 
 int32_t zero_bytes_of_rank(const zsmr_ctx* c, int32_t rank, int32_t gather_bytes,
                            int32_t max_live, zsmr_bytes* o) {
-    if (!c || !o || rank < 0 || rank >= c->world || gather_bytes < 0 || max_live < 0)
+    if (!c || !o || rank < 0 || rank >= c->world || gather_bytes < 0 ||
+        gather_bytes > ZSMR_MAX_GATHER_BYTES || max_live < 0)
         return ZSMR_ERR_ARG;
     if (gather_bytes == 0) gather_bytes = 2;
     if (max_live == 0) max_live = 1;
@@ -376,7 +390,8 @@ int32_t zero_bytes_of_rank(const zsmr_ctx* c, int32_t rank, int32_t gather_bytes
 
 int32_t zero_bytes_per_rank(const zsmr_ctx* c, int32_t gather_bytes, int32_t max_live,
                             zsmr_bytes* o) {
-    if (!c || !o || gather_bytes < 0 || max_live < 0) return ZSMR_ERR_ARG;
+    if (!c || !o || gather_bytes < 0 || gather_bytes > ZSMR_MAX_GATHER_BYTES || max_live < 0)
+        return ZSMR_ERR_ARG;
     if (c->stage != ZSMR_ZERO3_OWNER) return zero_bytes_of_rank(c, 0, gather_bytes, max_live, o);
     // stage 4: the rank with the largest peak (the lowest such rank)
     zsmr_bytes best{}, cur{};
