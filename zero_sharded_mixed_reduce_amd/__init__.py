@@ -106,12 +106,13 @@ class CheckedFunction:
 
     def __init__(self, name: str, fn, argtypes):
         self.name, self.fn = name, fn
-        self.ranges = [_INT_RANGE.get(t) for t in argtypes]
+        self.ints = [(i, *_INT_RANGE[t]) for i, t in enumerate(argtypes) if t in _INT_RANGE]
 
     def __call__(self, *args):
-        for i, (x, r) in enumerate(zip(args, self.ranges)):
-            if r is not None and isinstance(x, int) and not r[0] <= x <= r[1]:
-                raise ValueError(f"{self.name}: argument {i} = {x} is outside [{r[0]}, {r[1]}]")
+        for i, lo, hi in self.ints:
+            x = args[i] if i < len(args) else None
+            if isinstance(x, int) and not lo <= x <= hi:
+                raise ValueError(f"{self.name}: argument {i} = {x} is outside [{lo}, {hi}]")
         return self.fn(*args)
 
 
