@@ -342,6 +342,7 @@ def bench_share64(args, w):
     if not args.window_explicit:
         window = tune_write_window(share)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()                    # the timed region starts with an idle device
     t0 = time.perf_counter()
     for i in range(args.steps):
         t = args.warmup + 1 + i
@@ -508,7 +509,6 @@ def main():
     if parts:
         line["parts"] = parts
     if rw:
-        import zero_sharded_mixed_reduce_amd as z
         ref = references(z, REFERENCE_BYTES)
         if "peer_receive" in parts:
             line["copy_reference_GBps"] = round(ref["copy_GBps"], 1)
