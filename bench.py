@@ -206,14 +206,49 @@ def tune_write_window(share, reps: int = 6) -> dict:
             "tuned_over": n}
 
 
-def references(z, nbytes: int, reps: int = 5) -> dict:
+def tune_xcd_balance(share, reps: int = 3) -> dict:
+    """Pick the copies' work split between even and odd XCDs for this device
+    (the even XCDs of MI355X move data faster): the receive is timed at a
+    few splits, each over a few launches after an untimed one, the two
+    fastest again, and the fastest of those is kept."""
+    import torch
+    import zero_sharded_mixed_reduce_amd as z
+    stream = torch.cuda.current_stream()
+    tried = []
+
+    def timed(permille):
+        z.zsmr_set_xcd_balance(permille)
+        share.receive()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            share.receive()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tried.append((e0.elapsed_time(e1) / reps, permille))
+        return tried[-1]
+
+    for permille in (1000, 1100, 1150, 1200, 1250, 1300):
+        timed(permille)
+    n = len(tried)
+    finalists = [p for _, p in sorted(tried)[:2]]
+    del tried[:]
+    best = min(timed(p) for p in finalists)
+    z.zsmr_set_xcd_balance(best[1])
+    return {"even_permille": best[1], "tuned_over": n}
+
+
+def references(z, nbytes: int, reps: int = 5, balance: int = 1200) -> dict:
     """Rates this device gives simple streams of the receive's size, measured
     in the same process on two fresh, equally aligned buffers of ``nbytes``:
     the library's 128-bit copy and the runtime's device-to-device copy (GB/s
     of reads + writes), and the best pure read and pure write rates of the
-    reference streams in ``ceiling/``."""
+    reference streams in ``ceiling/`` (their balanced shapes weighted like
+    the library's copies, ``balance`` thousandths per even XCD)."""
     import torch
     import ceiling
+    ceiling.set_balance(balance)
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     ctx = z.zero_init_shards(2, 2, 2, "bf16")
@@ -341,6 +376,11 @@ def bench_share64(args, w):
               "margin": args.window_margin_ns, "lead": args.window_lead_ns, "tuned_over": 0}
     if not args.window_explicit:
         window = tune_write_window(share)
+    balance = {"even_permille": args.xcd_balance, "tuned_over": 0}
+    if args.xcd_balance is None:
+        balance = tune_xcd_balance(share)
+    else:
+        z.zsmr_set_xcd_balance(args.xcd_balance)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()                    # the timed region starts with an idle device
     t0 = time.perf_counter()
@@ -397,7 +437,7 @@ def bench_share64(args, w):
         "rank": 0, "step_workgroups_per_cu": args.step_bpc,
         "copy_workgroups_per_cu": args.copy_bpc, "fused_defer_tiles": args.defer_tiles,
         "fused_defer_min_rows": args.defer_min_rows,
-        "fused_write_window_ns": window}
+        "fused_write_window_ns": window, "copy_xcd_balance": balance}
 
 
 def bench_world(args, w):
@@ -410,6 +450,7 @@ def bench_world(args, w):
     z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
     z.zsmr_set_write_window(args.window_cycle_ns, args.window_write_ns, args.window_margin_ns,
                             args.window_lead_ns)
+    z.zsmr_set_xcd_balance(args.xcd_balance if args.xcd_balance is not None else z.XCD_BALANCE_DEFAULT)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
         # each unit size's gradients are made once, so that whole steps --
@@ -443,7 +484,8 @@ def bench_world(args, w):
     return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, rw, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
         "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3),
-        "stage3_layout": ("owner_broadcast" if args.owner else "per_unit_split") if w.stage == 3 else None}
+        "stage3_layout": ("owner_broadcast" if args.owner else "per_unit_split") if w.stage == 3 else None,
+        "copy_xcd_balance": {"even_permille": args.xcd_balance or z.XCD_BALANCE_DEFAULT, "tuned_over": 0}}
 
 
 def main():
@@ -466,6 +508,9 @@ def main():
                     help="fused step: no loads issued this long before a window")
     ap.add_argument("--window-lead-ns", type=int, default=None,
                     help="fused step: loads resume this long before a window ends")
+    ap.add_argument("--xcd-balance", type=int, default=None,
+                    help="copies: each even XCD's share against an odd one's, in thousandths "
+                         "(default: tuned on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefetch", action="store_true",
                     help="ZeRO-3 workload: gather the next unit while the current one is in use")
@@ -509,7 +554,8 @@ def main():
     if parts:
         line["parts"] = parts
     if rw:
-        ref = references(z, REFERENCE_BYTES)
+        bal = cfg.get("copy_xcd_balance", {}).get("even_permille") or z.XCD_BALANCE_DEFAULT
+        ref = references(z, REFERENCE_BYTES, balance=bal)
         if "peer_receive" in parts:
             line["copy_reference_GBps"] = round(ref["copy_GBps"], 1)
             line["runtime_d2d_copy_GBps"] = round(ref["runtime_copy_GBps"], 1)

@@ -13,9 +13,10 @@ import os
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libzsmr_ceiling.so")
-BURSTS, REGIONS, PLAIN = 0, 1, 1
-READ_SHAPES = {"bursts": BURSTS, "regions": REGIONS}
-WRITE_SHAPES = {"bursts_nt": BURSTS, "bursts_plain": PLAIN}
+BURSTS, REGIONS, PLAIN, BURSTS_BALANCED, PLAIN_BALANCED = 0, 1, 1, 2, 3
+READ_SHAPES = {"bursts": BURSTS, "regions": REGIONS, "bursts_balanced": BURSTS_BALANCED}
+WRITE_SHAPES = {"bursts_nt": BURSTS, "bursts_plain": PLAIN, "bursts_nt_balanced": BURSTS_BALANCED,
+                "bursts_plain_balanced": PLAIN_BALANCED}
 _LIB = None
 
 
@@ -30,6 +31,7 @@ def _lib():
         _LIB = checked_library(LIB_PATH, {
             "zsmr_ceiling_read": (i32, [vp, i64, i32, vp, vp]),
             "zsmr_ceiling_write": (i32, [vp, i64, i32, ctypes.c_uint32, vp]),
+            "zsmr_ceiling_set_balance": (i32, [i32]),
         })
     return _LIB
 
@@ -61,6 +63,14 @@ def write(dst, nbytes: int, shape: int, value: int, stream=None) -> None:
     code = _lib().zsmr_ceiling_write(_ptr(dst), nbytes, shape, value & 0xFFFFFFFF, _stream(stream))
     if code:
         raise RuntimeError(f"zsmr_ceiling_write failed with code {code}")
+
+
+def set_balance(even_permille: int) -> None:
+    """Weight of each even XCD against each odd one in the balanced shapes
+    (thousandths, 500..2000)."""
+    code = _lib().zsmr_ceiling_set_balance(even_permille)
+    if code:
+        raise RuntimeError(f"zsmr_ceiling_set_balance failed with code {code}")
 
 
 def phased_bound(read_bytes: int, write_bytes: int, read_gbps: float, write_gbps: float) -> float:

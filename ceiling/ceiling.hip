@@ -17,6 +17,30 @@ constexpr int kRegionBurst = 8;    // contiguous-region reads: 8 KB per wave per
 constexpr int64_t kChunk = int64_t(kBurst) * 64;
 constexpr int64_t kRegionChunk = int64_t(kRegionBurst) * 64;
 
+// Balanced shapes: the hardware hands workgroup i to XCD i % 8, and on
+// MI355X the even-numbered XCDs stream faster than the odd ones, so equal
+// shares leave the even ones idle at the end.  A split gives XCD x the
+// contiguous run of chunk blocks [start[x], start[x] + count[x]), each even
+// XCD weighted g_even_permille / 1000 against 1 for each odd one.
+constexpr int kXcds = 8;
+struct Split {
+    int64_t start[kXcds];
+    int64_t count[kXcds];
+};
+int g_even_permille = 1200;
+
+// The chunk block of this workgroup (whose waves take its kWaves chunks):
+// its index, or under a split the (i / 8)-th of XCD i % 8's run (-1 past it).
+template <bool BAL>
+__device__ __forceinline__ int64_t block_of(const Split& sp) {
+    if constexpr (!BAL) {
+        return blockIdx.x;
+    } else {
+        const int64_t x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+        return j < sp.count[x] ? sp.start[x] + j : -1;
+    }
+}
+
 // the read streams store only if the XOR of what they read equals this value
 __device__ __forceinline__ void keep(u32x4 acc, u32x4* sink) {
     if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && acc[2] == 0xf39cc060u &&
@@ -24,11 +48,16 @@ __device__ __forceinline__ void keep(u32x4 acc, u32x4* sink) {
         sink[0] = acc;
 }
 
-// Wave w reads vectors [w * kChunk, (w + 1) * kChunk) as one burst; the last,
-// partial chunk goes vector by vector.
-__global__ __launch_bounds__(kThreads) void read_bursts(const u32x4* src, int64_t nvec, u32x4* sink) {
+// Wave w of chunk block b reads vectors [c * kChunk, (c + 1) * kChunk),
+// c = b * kWaves + w, as one burst; the last, partial chunk goes vector by
+// vector.
+template <bool BAL>
+__global__ __launch_bounds__(kThreads) void read_bursts(const u32x4* src, int64_t nvec, u32x4* sink,
+                                                        Split sp) {
+    const int64_t b = block_of<BAL>(sp);
+    if (b < 0) return;
     const int64_t lane = threadIdx.x & 63;
-    const int64_t first = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kChunk;
+    const int64_t first = (b * kWaves + (threadIdx.x >> 6)) * kChunk;
     u32x4 acc = {0u, 0u, 0u, 0u};
     if (first + kChunk <= nvec) {
         u32x4 r[kBurst];
@@ -64,10 +93,13 @@ __global__ __launch_bounds__(kThreads) void read_regions(const u32x4* src, int64
     keep(acc, sink);
 }
 
-template <bool NT>
-__global__ __launch_bounds__(kThreads) void write_bursts(u32x4* dst, int64_t nvec, uint32_t value) {
+template <bool NT, bool BAL>
+__global__ __launch_bounds__(kThreads) void write_bursts(u32x4* dst, int64_t nvec, uint32_t value,
+                                                         Split sp) {
+    const int64_t b = block_of<BAL>(sp);
+    if (b < 0) return;
     const int64_t lane = threadIdx.x & 63;
-    const int64_t first = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kChunk;
+    const int64_t first = (b * kWaves + (threadIdx.x >> 6)) * kChunk;
     const u32x4 x = {value, value, value, value};
     if (first + kChunk <= nvec) {
 #pragma unroll
@@ -103,22 +135,53 @@ unsigned blocks_for(int64_t waves) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// `blocks` chunk blocks split between the XCDs by weight (floors, then the
+// remainder one at a time from XCD 0 on); *grid gets 8 x the largest run
+// (0 if that does not fit a grid).
+Split split_blocks(int64_t blocks, unsigned* grid) {
+    Split sp{};
+    const int64_t we = g_even_permille, wo = 1000, wsum = (kXcds / 2) * (we + wo);
+    int64_t given = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        sp.count[x] = blocks * (x % 2 == 0 ? we : wo) / wsum;
+        given += sp.count[x];
+    }
+    for (int x = 0; given < blocks; x = (x + 1) % kXcds, ++given) sp.count[x] += 1;
+    int64_t at = 0, most = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        sp.start[x] = at;
+        at += sp.count[x];
+        most = sp.count[x] > most ? sp.count[x] : most;
+    }
+    *grid = most * kXcds > 0x7fffffff ? 0u : static_cast<unsigned>(most * kXcds);
+    return sp;
+}
+
 }  // namespace
 
 extern "C" int32_t zsmr_ceiling_read(const void* src, int64_t bytes, int32_t shape, void* sink,
                                      hipStream_t stream) {
     if (bytes < 0 || bytes % 16 != 0) return 1;
-    if (shape != ZSMR_CEILING_BURSTS && shape != ZSMR_CEILING_REGIONS) return 1;
+    if (shape != ZSMR_CEILING_BURSTS && shape != ZSMR_CEILING_REGIONS &&
+        shape != ZSMR_CEILING_BURSTS_BALANCED)
+        return 1;
     const int64_t nvec = bytes / 16;
     if (nvec == 0) return 0;   // nothing is touched, whatever the pointers
     if (!src || !sink) return 1;
     if (!aligned16(src) || !aligned16(sink)) return 5;
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* k = static_cast<u32x4*>(sink);
-    if (shape == ZSMR_CEILING_BURSTS) {
-        const unsigned grid = blocks_for((nvec + kChunk - 1) / kChunk);
+    if (shape == ZSMR_CEILING_BURSTS || shape == ZSMR_CEILING_BURSTS_BALANCED) {
+        unsigned grid = blocks_for((nvec + kChunk - 1) / kChunk);
         if (!grid) return 1;
-        hipLaunchKernelGGL(read_bursts, dim3(grid), dim3(kThreads), 0, stream, s, nvec, k);
+        Split sp{};
+        if (shape == ZSMR_CEILING_BURSTS) {
+            hipLaunchKernelGGL(read_bursts<false>, dim3(grid), dim3(kThreads), 0, stream, s, nvec, k, sp);
+        } else {
+            sp = split_blocks(grid, &grid);
+            if (!grid) return 1;
+            hipLaunchKernelGGL(read_bursts<true>, dim3(grid), dim3(kThreads), 0, stream, s, nvec, k, sp);
+        }
     } else {
         const int64_t waves = int64_t(cu_count()) * kWaves;
         const int64_t each = (nvec + waves - 1) / waves;
@@ -132,17 +195,38 @@ extern "C" int32_t zsmr_ceiling_read(const void* src, int64_t bytes, int32_t sha
 extern "C" int32_t zsmr_ceiling_write(void* dst, int64_t bytes, int32_t shape, uint32_t value,
                                       hipStream_t stream) {
     if (bytes < 0 || bytes % 16 != 0) return 1;
-    if (shape != ZSMR_CEILING_BURSTS && shape != ZSMR_CEILING_PLAIN) return 1;
+    if (shape < ZSMR_CEILING_BURSTS || shape > ZSMR_CEILING_PLAIN_BALANCED) return 1;
     const int64_t nvec = bytes / 16;
     if (nvec == 0) return 0;
     if (!dst) return 1;
     if (!aligned16(dst)) return 5;
     u32x4* d = static_cast<u32x4*>(dst);
-    const unsigned grid = blocks_for((nvec + kChunk - 1) / kChunk);
+    unsigned grid = blocks_for((nvec + kChunk - 1) / kChunk);
     if (!grid) return 1;
-    if (shape == ZSMR_CEILING_BURSTS)
-        hipLaunchKernelGGL(write_bursts<true>, dim3(grid), dim3(kThreads), 0, stream, d, nvec, value);
-    else
-        hipLaunchKernelGGL(write_bursts<false>, dim3(grid), dim3(kThreads), 0, stream, d, nvec, value);
+    Split sp{};
+    if (shape == ZSMR_CEILING_BURSTS_BALANCED || shape == ZSMR_CEILING_PLAIN_BALANCED) {
+        sp = split_blocks(grid, &grid);
+        if (!grid) return 1;
+    }
+    switch (shape) {
+        case ZSMR_CEILING_BURSTS:
+            hipLaunchKernelGGL((write_bursts<true, false>), dim3(grid), dim3(kThreads), 0, stream, d, nvec, value, sp);
+            break;
+        case ZSMR_CEILING_PLAIN:
+            hipLaunchKernelGGL((write_bursts<false, false>), dim3(grid), dim3(kThreads), 0, stream, d, nvec, value, sp);
+            break;
+        case ZSMR_CEILING_BURSTS_BALANCED:
+            hipLaunchKernelGGL((write_bursts<true, true>), dim3(grid), dim3(kThreads), 0, stream, d, nvec, value, sp);
+            break;
+        default:
+            hipLaunchKernelGGL((write_bursts<false, true>), dim3(grid), dim3(kThreads), 0, stream, d, nvec, value, sp);
+            break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+extern "C" int32_t zsmr_ceiling_set_balance(int32_t even_permille) {
+    if (even_permille < 500 || even_permille > 2000) return 1;
+    g_even_permille = even_permille;
+    return 0;
 }

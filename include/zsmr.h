@@ -344,6 +344,17 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
 int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin_ns,
                               int32_t lead_ns);
 
+/* Work split of the copies (zero_gather_copy, zero_gather_copy_blocks,
+ * zero_stage3_unit_gather): the regions a copy is cut into go to the eight
+ * XCDs in contiguous runs, each even-numbered XCD taking even_permille / 1000
+ * times the regions of each odd one.  On MI355X the even XCDs move data
+ * faster than the odd ones, so equal shares leave them idle at the end of a
+ * copy.  500 <= even_permille <= 2000 (1000: equal shares), else
+ * ZSMR_ERR_ARG.  Default 1200, the best measured for the 14.77 GB receive of
+ * one rank's share of a 64-rank world.  Process-wide.  Affects speed only,
+ * never results. */
+int32_t zsmr_set_xcd_balance(int32_t even_permille);
+
 #ifdef __cplusplus
 }
 #endif

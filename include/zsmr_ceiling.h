@@ -18,7 +18,13 @@
  *                         non-temporal loads or stores;
  *   ZSMR_CEILING_REGIONS  reads only: each wave of one workgroup per CU
  *                         streams one contiguous region in 8 KB bursts;
- *   ZSMR_CEILING_PLAIN    writes only: as BURSTS with ordinary stores.
+ *   ZSMR_CEILING_PLAIN    writes only: as BURSTS with ordinary stores;
+ *   ZSMR_CEILING_BURSTS_BALANCED   as BURSTS (reads or non-temporal writes),
+ *                         the chunks split between the eight XCDs in
+ *                         contiguous runs, each even-numbered XCD taking
+ *                         zsmr_ceiling_set_balance()'s thousandths of an odd
+ *                         one's (on MI355X the even XCDs stream faster);
+ *   ZSMR_CEILING_PLAIN_BALANCED    writes only: as PLAIN, split the same way.
  *
  * Arguments: `bytes` >= 0 and a multiple of 16; `src` / `dst` 16-byte
  * aligned device pointers covering `bytes`; `sink` a 16-byte aligned device
@@ -45,6 +51,8 @@ extern "C" {
 #define ZSMR_CEILING_BURSTS 0
 #define ZSMR_CEILING_REGIONS 1
 #define ZSMR_CEILING_PLAIN 1
+#define ZSMR_CEILING_BURSTS_BALANCED 2
+#define ZSMR_CEILING_PLAIN_BALANCED 3
 
 /* Read [src, src + bytes) once. */
 int32_t zsmr_ceiling_read(const void* src, int64_t bytes, int32_t shape, void* sink,
@@ -53,6 +61,10 @@ int32_t zsmr_ceiling_read(const void* src, int64_t bytes, int32_t shape, void* s
 /* Write `value` to every 32-bit word of [dst, dst + bytes). */
 int32_t zsmr_ceiling_write(void* dst, int64_t bytes, int32_t shape, uint32_t value,
                            hipStream_t stream);
+
+/* Weight of each even-numbered XCD against each odd one in the balanced
+ * shapes, in thousandths: 500..2000 (default 1200), else 1.  Process-wide. */
+int32_t zsmr_ceiling_set_balance(int32_t even_permille);
 
 #ifdef __cplusplus
 }

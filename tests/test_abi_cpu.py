@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
     import ceiling
     clib = ctypes.CDLL(ceiling.LIB_PATH)
     cnames = declared("zsmr_ceiling.h")
-    assert cnames == ["zsmr_ceiling_read", "zsmr_ceiling_write"]
+    assert cnames == ["zsmr_ceiling_read", "zsmr_ceiling_set_balance", "zsmr_ceiling_write"]
     for n in cnames:
         assert hasattr(clib, n), n
 
@@ -51,13 +51,16 @@ def test_ceiling_argument_errors_return_before_any_launch():
     assert lib.zsmr_ceiling_read(a16, 16, 0, None, None) == 1
     assert lib.zsmr_ceiling_read(a16, -16, 0, a16, None) == 1
     assert lib.zsmr_ceiling_read(a16, 24, 0, a16, None) == 1
-    assert lib.zsmr_ceiling_read(a16, 16, 2, a16, None) == 1
+    assert lib.zsmr_ceiling_read(a16, 16, 3, a16, None) == 1
     assert lib.zsmr_ceiling_read(a8, 16, 0, a16, None) == 5
     assert lib.zsmr_ceiling_read(a16, 16, 1, a8, None) == 5
     assert lib.zsmr_ceiling_read(a16, 0, 1, a16, None) == 0
     assert lib.zsmr_ceiling_write(None, 16, 0, 0, None) == 1
     assert lib.zsmr_ceiling_write(a16, 8, 0, 0, None) == 1
-    assert lib.zsmr_ceiling_write(a16, 16, 3, 0, None) == 1
+    assert lib.zsmr_ceiling_write(a16, 16, 4, 0, None) == 1
+    assert lib.zsmr_ceiling_write(a16, 16, -1, 0, None) == 1
+    assert lib.zsmr_ceiling_set_balance(499) == 1 and lib.zsmr_ceiling_set_balance(2001) == 1
+    assert lib.zsmr_ceiling_set_balance(1000) == 0 and lib.zsmr_ceiling_set_balance(1200) == 0
     assert lib.zsmr_ceiling_write(a8, 16, 1, 0, None) == 5
     assert lib.zsmr_ceiling_write(a16, 0, 0, 0, None) == 0
     assert lib.zsmr_ceiling_write(None, 0, 0, 0, None) == 0        # nothing to touch
@@ -264,6 +267,16 @@ def test_write_window_arguments():
     z.zsmr_set_write_window(0, 0, 0, 0)
     z.zsmr_set_write_window(1000, 2, 997, 1)
     z.zsmr_set_write_window()                 # back to the defaults
+
+
+def test_xcd_balance_arguments():
+    for bad in (0, 499, 2001, -1000):
+        with pytest.raises(z.ZsmrError) as e:
+            z.zsmr_set_xcd_balance(bad)
+        assert e.value.code == z.ZSMR_ERR_ARG, bad
+    for good in (500, 1000, 2000):
+        z.zsmr_set_xcd_balance(good)
+    z.zsmr_set_xcd_balance()                  # back to the default
 
 
 

@@ -92,6 +92,8 @@ void set_launch_shape(int32_t a, int32_t b, int32_t c, int32_t d) {
 void set_write_window(int64_t a, int64_t b, int64_t c, int64_t d) {
     g_window[0] = a; g_window[1] = b; g_window[2] = c; g_window[3] = d;
 }
+static int32_t g_balance;
+void set_xcd_balance(int32_t even_permille) { g_balance = even_permille; }
 }  // namespace zsmr
 
 const char* hipGetErrorString(hipError_t) { return "launch refused by the stand-in"; }
@@ -412,6 +414,9 @@ static void limits() {
     CHECK(zsmr_set_write_window(INT32_MAX, INT32_MAX - 1, INT32_MAX, 0) == ZSMR_ERR_ARG);
     CHECK(zsmr_set_write_window(72000, 11000, 1000, 4000) == ZSMR_OK && zsmr::g_window[0] == 72000);
     CHECK(zsmr_set_write_window(0, 0, 0, 0) == ZSMR_OK && zsmr::g_window[0] == 0);
+    CHECK(zsmr_set_xcd_balance(499) == ZSMR_ERR_ARG && zsmr_set_xcd_balance(2001) == ZSMR_ERR_ARG);
+    CHECK(zsmr_set_xcd_balance(1000) == ZSMR_OK && zsmr::g_balance == 1000);
+    CHECK(zsmr_set_xcd_balance(1200) == ZSMR_OK && zsmr::g_balance == 1200);
 }
 
 int main() {

@@ -90,6 +90,7 @@ SIGNATURES = {
                                       ctypes.POINTER(_i64)]),
     "zsmr_set_launch_shape": (_i32, [_i32, _i32, _i32, _i32]),
     "zsmr_set_write_window": (_i32, [_i32, _i32, _i32, _i32]),
+    "zsmr_set_xcd_balance": (_i32, [_i32]),
 }
 
 _LIB = None
@@ -428,3 +429,10 @@ def zsmr_set_write_window(cycle_ns: int = WRITE_WINDOW_DEFAULT[0],
                           lead_ns: int = WRITE_WINDOW_DEFAULT[3]) -> None:
     _check(_lib().zsmr_set_write_window(int(cycle_ns), int(write_ns), int(margin_ns), int(lead_ns)),
            "zsmr_set_write_window")
+
+
+XCD_BALANCE_DEFAULT = 1200
+
+
+def zsmr_set_xcd_balance(even_permille: int = XCD_BALANCE_DEFAULT) -> None:
+    _check(_lib().zsmr_set_xcd_balance(int(even_permille)), "zsmr_set_xcd_balance")

@@ -716,4 +716,10 @@ int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin
     return ZSMR_OK;
 }
 
+int32_t zsmr_set_xcd_balance(int32_t even_permille) {
+    if (even_permille < 500 || even_permille > 2000) return ZSMR_ERR_ARG;
+    zsmr::set_xcd_balance(even_permille);
+    return ZSMR_OK;
+}
+
 }  // extern "C"

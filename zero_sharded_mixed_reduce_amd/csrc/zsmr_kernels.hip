@@ -78,6 +78,9 @@ constexpr int kNarrowCopyBpc = 4;   // the 2-byte copies: 4 per CU
 // 6.07 grid-stride at 1 per CU; the share64 receive 6.00-6.03 against
 // 5.82-5.84 (2 per CU 5.84-5.86, 4 per CU 5.94-5.96).
 int g_copy_bpc = 0;
+// The copies' share of regions for each even-numbered XCD against each odd
+// one, in thousandths (the measurements are beside XcdSplit below).
+int g_xcd_even_permille = 1200;
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
 // write windows (0 = write at once with step_vec8_kernel).  With windows and
 // a ring of at most 3 tiles (72 KB per workgroup), two workgroups run per CU
@@ -653,28 +656,44 @@ struct VecOf<4> { typedef uint32_t T; };
 template <>
 struct VecOf<2> { typedef uint16_t T; };
 
-// The hardware hands workgroup i of a launch to XCD i % 8.  Region of
-// workgroup i of g such that each XCD takes one contiguous eighth of the
-// regions, in order, instead of every eighth one (a bijection of [0, g)).
-// Measured on MI355X, a 14 GB copy with one 32 KB burst per wave: 6.21 TB/s
-// against 6.05-6.06 with workgroup i on region i; the share64 receive
-// 4.68-4.69 ms against 4.78.  (The direct step kernel ran 4-10% slower
-// remapped, and the deferred kernel no faster, so only the copies use it.)
+// The hardware hands workgroup i of a launch to XCD i % 8.  A copy's
+// regions (one workgroup's work each) are split between the XCDs in
+// contiguous runs, XCD x taking regions [start[x], start[x] + count[x]) in
+// order: workgroup i is the (i / 8)-th of XCD i % 8, and one past its XCD's
+// count has nothing to do.  Measured on MI355X, a 14 GB copy with one 32 KB
+// burst per wave: one contiguous eighth per XCD 6.21 TB/s against 6.05-6.06
+// with workgroup i on region i; the share64 receive 4.68-4.69 ms against
+// 4.78.  (The direct step kernel ran 4-10% slower remapped, and the deferred
+// kernel no faster, so only the copies use it.)
+//
+// The counts are not equal.  On MI355X the even-numbered XCDs move data
+// faster than the odd ones: with equal eighths of the share64 receive the
+// even XCDs finished 450-490 us (10%) before the odd ones, whichever
+// addresses each copied (eighths swapped between neighbours, or interleaved,
+// gave the same split).  The odd XCDs then speed up, so most of that comes
+// back on its own, but not all: giving each even XCD r times an odd one's
+// regions, the receive took 4.689 ms at r = 1.0, 4.652 at 1.1, 4.603 at 1.2,
+// 4.621 at 1.25, 4.645 at 1.3 and 4.732 at 0.9 (three passes, one box).
 constexpr uint32_t kXcds = 8;
-__device__ __forceinline__ int64_t xcd_region(int64_t i, int64_t g) {
-    const int64_t x = i % kXcds, q = g / kXcds, rem = g % kXcds;
-    return x * q + (x < rem ? x : rem) + i / kXcds;
+struct XcdSplit {
+    int64_t start[kXcds];
+    int64_t count[kXcds];
+};
+__device__ __forceinline__ int64_t split_region(const XcdSplit& sp, int64_t i) {
+    const int64_t x = i % kXcds, j = i / kXcds;
+    return j < sp.count[x] ? sp.start[x] + j : -1;
 }
 
 // Copy n elements: `head` scalar elements bring dst (and src, which has the
 // same alignment modulo W) to a W-byte boundary, then W-byte vectors, then
-// the scalar tail.  Workgroup `part` of `parts` takes its share of the
+// the scalar tail.  Region `region` of `regions` takes its share of the
 // vectors.  The burst copies lay their chunks out from `pre` vectors before
 // the vector body (the body's offset from dst's last 128 KB boundary), so
 // that every whole chunk, and every workgroup's four, sits on that grid.
 template <int W>
 __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, int64_t n,
-                                           int64_t head, int64_t pre, int64_t part, int64_t parts) {
+                                           int64_t head, int64_t pre, int64_t region,
+                                           int64_t regions) {
     typedef typename VecOf<W>::T V;
     constexpr int E = W / 2;
     const int64_t nb = (n - head) / E;
@@ -684,15 +703,15 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
     if constexpr (W >= 4) {
         // Register bursts: each wave loads kBurst vectors per lane (32 KB per
         // wave) before it stores any, so every wave alternates a read burst
-        // and a write burst; wave w of the launch takes chunks w, w + waves,
-        // ... (neighbouring waves, neighbouring chunks).  Chunk c covers body
+        // and a write burst; wave w of the regions' waves takes chunks w,
+        // w + waves, ... (neighbouring waves, neighbouring chunks).  Chunk c covers body
         // vectors [c * chunk - pre, (c + 1) * chunk - pre); the partial first
         // and last chunks go one guarded vector at a time.
         constexpr int kBurst = ZSMR_COPY_BURST_BYTES / W;
         constexpr int64_t chunk = (int64_t)kBurst * 64;
         const int64_t lane = threadIdx.x & 63u;
-        const int64_t waves = parts * (kThreads / 64);
-        const int64_t wid = xcd_region(part, parts) * (kThreads / 64) + (threadIdx.x >> 6);
+        const int64_t waves = regions * (kThreads / 64);
+        const int64_t wid = region * (kThreads / 64) + (threadIdx.x >> 6);
         const int64_t nv = nb;
         for (int64_t c = wid; c * chunk < nv + pre; c += waves) {
             const int64_t first = c * chunk - pre;   // the chunk's first body vector (may be < 0)
@@ -713,11 +732,11 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
         }
     } else {
         // 2-byte elements (source and destination an odd number of elements
-        // apart): one contiguous chunk per workgroup; kCopyUnroll consecutive
+        // apart): one contiguous chunk per region; kCopyUnroll consecutive
         // groups of kThreads elements are loaded before any is stored
         constexpr int64_t group = (int64_t)kThreads * kCopyUnroll;
-        const int64_t chunk = ((nb + parts - 1) / parts + group - 1) / group * group;
-        const int64_t lo = part * chunk;
+        const int64_t chunk = ((nb + regions - 1) / regions + group - 1) / group * group;
+        const int64_t lo = region * chunk;
         const int64_t hi = lo + chunk < nb ? lo + chunk : nb;
         for (int64_t i = lo + threadIdx.x; i < hi; i += group) {
             V tmp[kCopyUnroll];
@@ -729,7 +748,7 @@ __device__ __forceinline__ void copy_range(const uint16_t* src, uint16_t* dst, i
                 if (i + k * kThreads < hi) st(d + i + k * kThreads, tmp[k]);
         }
     }
-    if (part == 0) {
+    if (region == 0) {
         const int t = static_cast<int>(threadIdx.x);
         if (t < head) dst[t] = src[t];
         const int64_t tail = n - body_end;
@@ -775,8 +794,11 @@ __host__ __device__ inline int64_t pre_for(const void* dst, int w, int64_t head)
 
 template <int W>
 __global__ __launch_bounds__(kThreads) void copy16_kernel(const uint16_t* src, uint16_t* dst,
-                                                          int64_t n, int64_t head, int64_t pre) {
-    copy_range<W>(src, dst, n, head, pre, blockIdx.x, gridDim.x);
+                                                          int64_t n, int64_t head, int64_t pre,
+                                                          XcdSplit sp, int64_t regions) {
+    const int64_t r = split_region(sp, blockIdx.x);
+    if (r < 0) return;
+    copy_range<W>(src, dst, n, head, pre, r, regions);
 }
 
 // Block k of `count` (blockIdx.y): n elements from src + k * stride to
@@ -784,12 +806,15 @@ __global__ __launch_bounds__(kThreads) void copy16_kernel(const uint16_t* src, u
 // would have (the blocks' destinations need not share their alignment).
 template <int W>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const uint16_t* src, uint16_t* dst,
-                                                               int64_t n, int64_t stride) {
+                                                               int64_t n, int64_t stride,
+                                                               XcdSplit sp, int64_t regions) {
+    const int64_t r = split_region(sp, blockIdx.x);
+    if (r < 0) return;
     const int64_t k = blockIdx.y;
     const uint16_t* s = src + k * stride;
     uint16_t* d = dst + k * stride;
     const int64_t head = head_for(d, W, n);
-    copy_range<W>(s, d, n, head, pre_for(d, W, head), blockIdx.x, gridDim.x);
+    copy_range<W>(s, d, n, head, pre_for(d, W, head), r, regions);
 }
 
 constexpr int kMaxGather = 64;
@@ -802,10 +827,12 @@ struct GatherArgs {
 };
 
 template <int W>
-__global__ __launch_bounds__(kThreads) void gather16_kernel(GatherArgs g) {
+__global__ __launch_bounds__(kThreads) void gather16_kernel(GatherArgs g, XcdSplit sp,
+                                                            int64_t regions) {
+    const int64_t reg = split_region(sp, blockIdx.x);
+    if (reg < 0) return;
     const int r = blockIdx.y;
-    copy_range<W>(g.src[r], g.dst + (int64_t)r * g.each, g.each, g.head[r], g.pre[r], blockIdx.x,
-                  gridDim.x);
+    copy_range<W>(g.src[r], g.dst + (int64_t)r * g.each, g.each, g.head[r], g.pre[r], reg, regions);
 }
 
 // ------------------------------------------------------------------ host --
@@ -829,6 +856,29 @@ unsigned grid_for(int64_t work_items, int bpc) {
     if (bpc > 0 && blocks > (int64_t)cu_count() * bpc) blocks = (int64_t)cu_count() * bpc;
     if (blocks < 1) blocks = 1;
     return static_cast<unsigned>(blocks);
+}
+
+// `regions` split between the XCDs, each even one weighted
+// g_xcd_even_permille / 1000 against 1 for each odd one (floors, then the
+// remainder one region at a time from XCD 0 on); *grid receives the
+// workgroups that cover the largest share on every XCD.
+XcdSplit xcd_split(int64_t regions, unsigned* grid) {
+    XcdSplit sp{};
+    const int64_t we = g_xcd_even_permille, wo = 1000, wsum = (kXcds / 2) * (we + wo);
+    int64_t given = 0;
+    for (uint32_t x = 0; x < kXcds; ++x) {
+        sp.count[x] = regions * (x % 2 == 0 ? we : wo) / wsum;
+        given += sp.count[x];
+    }
+    for (uint32_t x = 0; given < regions; x = (x + 1) % kXcds, ++given) sp.count[x] += 1;
+    int64_t at = 0, most = 0;
+    for (uint32_t x = 0; x < kXcds; ++x) {
+        sp.start[x] = at;
+        at += sp.count[x];
+        most = sp.count[x] > most ? sp.count[x] : most;
+    }
+    *grid = static_cast<unsigned>(most * kXcds);
+    return sp;
 }
 
 inline bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -923,6 +973,8 @@ hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, bool vec, int dv, hipS
 }
 
 }  // namespace
+
+void set_xcd_balance(int32_t even_permille) { g_xcd_even_permille = even_permille; }
 
 void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                       int32_t defer_min_rows) {
@@ -1022,13 +1074,16 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     const int64_t head = head_for(dst, w, n);
     const int64_t pre = pre_for(dst, w, head);
     const int64_t vecs = (n - head) / (w / 2) + 1;
-    const dim3 grid(w >= 4 ? grid_for((vecs + pre) / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
-                           : grid_for(vecs, kNarrowCopyBpc));
+    const int64_t regions = w >= 4 ? grid_for((vecs + pre) / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
+                                   : grid_for(vecs, kNarrowCopyBpc);
+    unsigned gx = 0;
+    const XcdSplit sp = xcd_split(regions, &gx);
+    const dim3 grid(gx);
     switch (w) {
-        case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
-        case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
-        case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
-        default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre); break;
+        case 16: hipLaunchKernelGGL(copy16_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre, sp, regions); break;
+        case 8: hipLaunchKernelGGL(copy16_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre, sp, regions); break;
+        case 4: hipLaunchKernelGGL(copy16_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre, sp, regions); break;
+        default: hipLaunchKernelGGL(copy16_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, head, pre, sp, regions); break;
     }
     return hipGetLastError();
 }
@@ -1041,21 +1096,22 @@ hipError_t launch_copy_blocks(const uint16_t* src, uint16_t* dst, int64_t n, int
     const int64_t pre_max = w >= 4 ? int64_t(128 * 1024) / w : 0;   // a block's chunk-grid offset
     const int64_t per = n / (w / 2) + 1 + pre_max;
     const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
-    int64_t bx = (units + kThreads - 1) / kThreads;
-    if (w >= 4) bx = (bx + kXcds - 1) / kXcds * kXcds;   // each block's row starts on XCD 0
+    int64_t regions = (units + kThreads - 1) / kThreads;   // of each block
     const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
     if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all blocks
         const int64_t cap = (int64_t)cu_count() * bpc;
         const int64_t lim = cap / count > 0 ? cap / count : 1;
-        if (bx > lim) bx = lim;
+        if (regions > lim) regions = lim;
     }
-    if (bx < 1) bx = 1;
-    const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(count));
+    if (regions < 1) regions = 1;
+    unsigned gx = 0;   // a multiple of 8: each block's row starts on XCD 0
+    const XcdSplit sp = xcd_split(regions, &gx);
+    const dim3 grid(gx, static_cast<unsigned>(count));
     switch (w) {
-        case 16: hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
-        case 8: hipLaunchKernelGGL(copy_blocks_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
-        case 4: hipLaunchKernelGGL(copy_blocks_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
-        default: hipLaunchKernelGGL(copy_blocks_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, stride); break;
+        case 16: hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(kThreads), 0, s, src, dst, n, stride, sp, regions); break;
+        case 8: hipLaunchKernelGGL(copy_blocks_kernel<8>, grid, dim3(kThreads), 0, s, src, dst, n, stride, sp, regions); break;
+        case 4: hipLaunchKernelGGL(copy_blocks_kernel<4>, grid, dim3(kThreads), 0, s, src, dst, n, stride, sp, regions); break;
+        default: hipLaunchKernelGGL(copy_blocks_kernel<2>, grid, dim3(kThreads), 0, s, src, dst, n, stride, sp, regions); break;
     }
     return hipGetLastError();
 }
@@ -1083,21 +1139,22 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
         }
         const int64_t per = each / (w / 2) + 1 + pre_max;
         const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
-        int64_t bx = (units + kThreads - 1) / kThreads;
-        if (w >= 4) bx = (bx + kXcds - 1) / kXcds * kXcds;   // each source's row starts on XCD 0
+        int64_t regions = (units + kThreads - 1) / kThreads;   // of each source
         const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
         if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all sources
             const int64_t cap = (int64_t)cu_count() * bpc;
             const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
-            if (bx > lim) bx = lim;
+            if (regions > lim) regions = lim;
         }
-        if (bx < 1) bx = 1;
-        const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(cnt));
+        if (regions < 1) regions = 1;
+        unsigned gx = 0;   // a multiple of 8: each source's row starts on XCD 0
+        const XcdSplit sp = xcd_split(regions, &gx);
+        const dim3 grid(gx, static_cast<unsigned>(cnt));
         switch (w) {
-            case 16: hipLaunchKernelGGL(gather16_kernel<16>, grid, dim3(kThreads), 0, s, g); break;
-            case 8: hipLaunchKernelGGL(gather16_kernel<8>, grid, dim3(kThreads), 0, s, g); break;
-            case 4: hipLaunchKernelGGL(gather16_kernel<4>, grid, dim3(kThreads), 0, s, g); break;
-            default: hipLaunchKernelGGL(gather16_kernel<2>, grid, dim3(kThreads), 0, s, g); break;
+            case 16: hipLaunchKernelGGL(gather16_kernel<16>, grid, dim3(kThreads), 0, s, g, sp, regions); break;
+            case 8: hipLaunchKernelGGL(gather16_kernel<8>, grid, dim3(kThreads), 0, s, g, sp, regions); break;
+            case 4: hipLaunchKernelGGL(gather16_kernel<4>, grid, dim3(kThreads), 0, s, g, sp, regions); break;
+            default: hipLaunchKernelGGL(gather16_kernel<2>, grid, dim3(kThreads), 0, s, g, sp, regions); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -53,6 +53,8 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
                            uint16_t* dst, hipStream_t stream);
 void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                       int32_t defer_min_rows);
+// each even XCD's share of a copy's regions against an odd one's, in thousandths
+void set_xcd_balance(int32_t even_permille);
 // write windows of the fused step's deferred-write kernel (cycle_ns 0: none)
 void set_write_window(int64_t cycle_ns, int64_t write_ns, int64_t margin_ns, int64_t lead_ns);
 
