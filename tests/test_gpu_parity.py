@@ -675,3 +675,52 @@ def _copy_case(n, off):
     got = host16(D)
     assert np.array_equal(got[off:off + n], src[off:off + n])
     assert not got[:off].any() and not got[off + n:].any()
+
+
+@pytest.mark.parametrize("permille", [500, 1000, 2000])
+def test_copies_cover_every_region_at_any_xcd_weight(permille):
+    """However the copies weight the even XCDs against the odd ones, every
+    element is copied once: the receive, the block receive and the ZeRO-3
+    gather are byte-exact, nothing around them is written, and the counters
+    do not depend on the weight."""
+    say(f"[xcd balance] permille={permille}")
+    z.zsmr_set_xcd_balance(permille)
+    try:
+        rng = np.random.default_rng(permille)
+        for n, off in ((1, 0), (33, 3), (1_000_003, 0), (4_194_304 + 77, 5), (40_000_000, 8)):
+            src = rng.integers(1, 1 << 16, n + 64, dtype=np.uint64).astype(np.uint16)
+            S = dev16(src)
+            D = torch.zeros(n + 64, dtype=torch.int16, device="cuda")
+            ctx = z.zero_init_shards(64, 2, 2, "bf16")
+            z.zero_gather_copy(ctx, 1, S[off:], D[off:], n)
+            torch.cuda.synchronize()
+            got = host16(D)
+            assert np.array_equal(got[off:off + n], src[off:off + n]), n
+            assert not got[:off].any() and not got[off + n:].any(), n
+            assert z.zero_counters(ctx, 1)["ag_elems"] == n
+        n, count, stride = 100_003, 63, 117_003
+        span = (count - 1) * stride + n
+        src = rng.integers(1, 1 << 16, span, dtype=np.uint64).astype(np.uint16)
+        D = torch.zeros(span, dtype=torch.int16, device="cuda")
+        ctx = z.zero_init_shards(64, 2, 2, "bf16")
+        z.zero_gather_copy_blocks(ctx, 1, dev16(src), D, n, count, stride)
+        torch.cuda.synchronize()
+        want = np.zeros_like(src)
+        for k in range(count):
+            want[k * stride:k * stride + n] = src[k * stride:k * stride + n]
+        assert np.array_equal(host16(D), want)
+        units = [8 * 300_001, 8 * 5]
+        s3 = z.zero_init_shards(sum(units), 8, 3, "bf16", units=units)
+        for u, total in enumerate(units):
+            each = total // 8
+            shards = [dev16(rng.integers(1, 1 << 16, each, dtype=np.uint64).astype(np.uint16))
+                      for _ in range(8)]
+            buf = torch.zeros(total + 16, dtype=torch.int16, device="cuda")
+            z.zero_stage3_unit_gather(s3, u, shards, buf)
+            torch.cuda.synchronize()
+            got = host16(buf)
+            assert np.array_equal(got[:total], np.concatenate([host16(x) for x in shards]))
+            assert not got[total:].any()
+            z.zero_stage3_unit_release(s3, u)
+    finally:
+        z.zsmr_set_xcd_balance()
