@@ -36,3 +36,10 @@ def test_bench_prints_one_complete_json_line():
     for part in ("fused_step", "peer_receive", "step"):
         assert 0 < d["phased_bound"][part]["frac"] < 1.2
     assert d["copy_reference_GBps"] > 0 and d["runtime_d2d_copy_GBps"] > 0
+    bal = d["config"]["copy_xcd_balance"]                 # tuned on the device
+    assert 1000 <= bal["even_permille"] <= 1300 and bal["tuned_over"] == 6
+    win = d["config"]["fused_write_window_ns"]
+    assert win["tuned_over"] > 0 and win["write"] + win["margin"] < win["cycle"]
+    shapes = d["phased_bound"]
+    assert "bursts_balanced" in shapes["read_shapes_GBps"]
+    assert "bursts_plain_balanced" in shapes["write_shapes_GBps"]
