@@ -328,6 +328,31 @@ def bucketed_overlap(share, args, reps: int = 5) -> dict:
             "hidden_fraction_of_step": round((seq - buck) / (seq - fill), 4) if seq > fill else None}
 
 
+def untuned_step(share, args) -> dict:
+    """The same step at the library's default write window and XCD split
+    (what a caller gets without tuning), timed like the headline; the tuned
+    settings are restored afterwards."""
+    import torch
+    import zero_sharded_mixed_reduce_amd as z
+    stream = torch.cuda.current_stream()
+    z.zsmr_set_write_window()
+    z.zsmr_set_xcd_balance()
+    t0 = args.warmup + args.steps + 1
+    share.step(t0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        share.step(t0 + 1 + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    z.zsmr_set_write_window(*args.tuned["window"])
+    z.zsmr_set_xcd_balance(args.tuned["balance"])
+    return {"ms": round(e0.elapsed_time(e1) / args.steps, 4),
+            "write_window_ns": list(z.WRITE_WINDOW_DEFAULT),
+            "xcd_even_permille": z.XCD_BALANCE_DEFAULT}
+
+
 def unfused_step(share, args, reps: int = 10) -> dict:
     """The fused pass's work done by the three unfused calls (reduce to an
     fp32 gradient, Adam, cast), timed with HIP events on the launch stream:
@@ -381,6 +406,11 @@ def bench_share64(args, w):
         balance = tune_xcd_balance(share)
     else:
         z.zsmr_set_xcd_balance(args.xcd_balance)
+    # what the run tuned, restored after the untuned comparison
+    args.tuned = None
+    if window["tuned_over"] or balance["tuned_over"]:
+        args.tuned = {"window": (window["cycle"], window["write"], window["margin"], window["lead"]),
+                      "balance": balance["even_permille"]}
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()                    # the timed region starts with an idle device
     t0 = time.perf_counter()
@@ -396,6 +426,7 @@ def bench_share64(args, w):
     fused_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     recv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     ms_step = wall * 1e3 / args.steps
+    untuned = untuned_step(share, args) if args.tuned else None
 
     S, N = share.S, w.world
     bucketed = bucketed_overlap(share, args) if args.buckets else None
@@ -411,6 +442,10 @@ def bench_share64(args, w):
                          "frac": round(recv_bytes / recv_ms / 1e6 / PEAK_HBM_GBPS, 4)},
         "step_GBps": round((fused_bytes + recv_bytes) / ms_step / 1e6, 1),
     }
+    if untuned:
+        parts["step_at_library_defaults"] = dict(
+            untuned, GBps=round((fused_bytes + recv_bytes) / untuned["ms"] / 1e6, 1),
+            frac=round((fused_bytes + recv_bytes) / untuned["ms"] / 1e6 / PEAK_HBM_GBPS, 4))
     if bucketed:
         parts["bucketed_with_backward"] = bucketed
     if unfused:
@@ -440,23 +475,21 @@ def bench_share64(args, w):
         "fused_write_window_ns": window, "copy_xcd_balance": balance}
 
 
-def bench_world(args, w):
+def time_world(args, w, owner: bool = False, prefetch: bool = False):
     """Simulated-world workloads (all N ranks on the GPU): one step = N fused
-    launches (stages 1-2) or the ZeRO-3 unit schedule (stage 3)."""
+    launches (stages 1-2) or the ZeRO-3 unit schedule (stage 3), timed with
+    HIP events on the compute stream.  Returns (ms per step, algorithmic
+    bytes per step, (read bytes, write bytes) per step)."""
     import torch
     import workloads as wl
-    import zero_sharded_mixed_reduce_amd as z
 
-    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
-    z.zsmr_set_write_window(args.window_cycle_ns, args.window_write_ns, args.window_margin_ns,
-                            args.window_lead_ns)
-    z.zsmr_set_xcd_balance(args.xcd_balance if args.xcd_balance is not None else z.XCD_BALANCE_DEFAULT)
     stream = torch.cuda.current_stream()
     if w.stage == 3:
         # each unit size's gradients are made once, so that whole steps --
-        # gathers, fused launches and (with --prefetch) the overlap of the next
+        # gathers, fused launches and (with prefetch) the overlap of the next
         # gather -- are timed end to end on the compute stream
-        world = wl.Stage3World(w, prefetch=args.prefetch, fixed_grads=True, owner=args.owner)
+        world = wl.Stage3World(w, prefetch=prefetch, fixed_grads=True, owner=owner,
+                               owners=wl.LLAMA8B_OWNERS if owner and w.key == "llama8b" else None)
     else:
         world = wl.ShardedWorld(w)
         world.gen_grads(1)
@@ -468,24 +501,92 @@ def bench_world(args, w):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    del world
+    free_device()
     N = w.world
     byts = w.numel * (2 * N + 26) + (8 * w.numel if w.stage == 3 else 0)
+    gather = 4 * w.numel if w.stage == 3 else 0      # two gathers: 2 B read + 2 B written each
+    return ms_step, byts, (w.numel * (2 * N + 12) + gather, 14 * w.numel + gather)
+
+
+def free_device():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def fused_kernel_name(args, rows: int) -> str:
+    return "step_deferred_kernel" if args.defer_tiles > 0 and rows >= args.defer_min_rows \
+        else "step_vec8_kernel"
+
+
+def bench_world(args, w):
+    import zero_sharded_mixed_reduce_amd as z
+
+    z.zsmr_set_launch_shape(args.step_bpc, args.copy_bpc, args.defer_tiles, args.defer_min_rows)
+    z.zsmr_set_write_window(args.window_cycle_ns, args.window_write_ns, args.window_margin_ns,
+                            args.window_lead_ns)
+    z.zsmr_set_xcd_balance(args.xcd_balance if args.xcd_balance is not None else z.XCD_BALANCE_DEFAULT)
+    ms_step, byts, (rb, wb) = time_world(args, w, owner=args.owner, prefetch=args.prefetch)
+    N = w.world
     gbps = byts / ms_step / 1e6
-    kname = ("step_deferred_kernel" if args.defer_tiles > 0 and N >= args.defer_min_rows
-             else "step_vec8_kernel")
+    kname = fused_kernel_name(args, N)
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "traffic": read_traffic(kname, w.key, "hbm_bytes_per_step"),
             "kernel": kname, "algorithmic_bytes_per_step": byts,
             "note": "whole step (every rank's fused launch" + (", and the unit gathers" if w.stage == 3 else "")
                     + ") timed with HIP events on the compute stream"}
-    gather = 4 * w.numel if w.stage == 3 else 0      # two gathers: 2 B read + 2 B written each
-    rw = {"step": (w.numel * (2 * N + 12) + gather, 14 * w.numel + gather, ms_step)}
+    rw = {"step": (rb, wb, ms_step)}
     return w.numel / (ms_step / 1e3), ms_step, roof, None, {}, rw, {
         "workload": w.name, "numel": w.numel, "world": N, "stage": w.stage, "grad_dtype": w.dtype,
         "steps_T": w.steps, "lr": w.lr, "prefetch": bool(args.prefetch and w.stage == 3),
         "stage3_layout": ("owner_broadcast" if args.owner else "per_unit_split") if w.stage == 3 else None,
         "copy_xcd_balance": {"even_permille": args.xcd_balance or z.XCD_BALANCE_DEFAULT, "tuned_over": 0}}
+
+
+# The other workloads, timed after the headline in the same run: key ->
+# (workload, ZeRO-3 layout owner broadcast, prefetch)
+OTHER_CONFIGS = {
+    "psi65k_zero2": ("psi65k", False, False),
+    "gpt2s_zero2": ("gpt2s", False, False),
+    "gpt2xl_zero1": ("gpt2xl", False, False),
+    "llama8b_zero3_split": ("llama8b", False, False),
+    "llama8b_zero3_owner": ("llama8b", True, False),
+}
+
+
+def other_configs(args, pure) -> dict:
+    """Every other workload's whole step, at the library's default launch
+    shape and write window (the copies at the XCD split this run chose):
+    ms per step, parameters per second, GB/s of algorithmic bytes, its
+    fraction of 8 TB/s, and its fraction of the phased bound (the least time
+    its reads and writes could take at this run's pure read and write
+    rates).  psi65k (65,536 parameters) is latency-bound and reported for
+    completeness only."""
+    import ceiling
+    import workloads as wl
+    import zero_sharded_mixed_reduce_amd as z
+
+    z.zsmr_set_launch_shape()
+    z.zsmr_set_write_window()
+    out = {}
+    for name, (key, owner, prefetch) in OTHER_CONFIGS.items():
+        w = wl.WORKLOADS[key]
+        if key == "psi65k":
+            w = wl.Workload(w.key, w.name, w.numel, w.world, 2, w.dtype, w.grad_sigma, w.lr, w.steps)
+        ms, byts, (rb, wb) = time_world(args, w, owner=owner, prefetch=prefetch)
+        bound = ceiling.phased_bound(rb, wb, pure["read_GBps"], pure["write_GBps"])
+        gbps = byts / ms / 1e6
+        out[name] = {"workload": w.name, "ms_per_step": round(ms, 4),
+                     "params_per_s": round(w.numel / (ms / 1e3), 1),
+                     "algorithmic_bytes_per_step": byts, "GBps": round(gbps, 1),
+                     "frac_of_8TBps": round(gbps / PEAK_HBM_GBPS, 4),
+                     "phased_bound_ms": round(bound, 4), "frac_of_phased_bound": round(bound / ms, 4),
+                     "fused_kernel": fused_kernel_name(args, w.world)}
+    return out
 
 
 def main():
@@ -512,6 +613,8 @@ def main():
                     help="copies: each even XCD's share against an odd one's, in thousandths "
                          "(default: tuned on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="share64: skip timing the other workloads after the headline")
     ap.add_argument("--prefetch", action="store_true",
                     help="ZeRO-3 workload: gather the next unit while the current one is in use")
     ap.add_argument("--owner", action="store_true",
@@ -562,6 +665,8 @@ def main():
             parts["peer_receive"]["frac_of_copy_reference"] = round(
                 parts["peer_receive"]["GBps"] / ref["copy_GBps"], 4)
         line["phased_bound"] = phased(parts, rw, ref["pure"])
+    if args.workload == "share64" and not args.no_configs and rw:
+        line["other_configs"] = other_configs(args, ref["pure"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -135,10 +135,15 @@ typedef struct zsmr_counters {
     int64_t live_units, live_bytes, peak_live_bytes;
 } zsmr_counters;
 
-/* Name of a status code (static storage). */
+/* Name of a status code (static storage).  Library plumbing: the pages
+ * define no error codes; the conditions behind ZSMR_ERR_INDIVISIBLE and
+ * ZSMR_ERR_STATE are the prototype's divisibility assertion ("The four
+ * schemes", Base.__init__) and ZeRO-3's gather-before-use order ("The four
+ * schemes", where the third P comes from). */
 const char* zsmr_strerror(int32_t status);
 
-/* Text of the last HIP error seen by this thread, or "" (thread-local). */
+/* Text of the last HIP error seen by this thread, or "" (thread-local).
+ * Library plumbing, no passage of the pages. */
 const char* zsmr_last_hip_error(void);
 
 /* Build the partition of Psi = numel elements over `world` ranks (host only).
@@ -155,30 +160,50 @@ const char* zsmr_last_hip_error(void);
  * parallel rank "owns" [0, Psi).  Stage 4 keeps units whole and unpadded in
  * their natural order: unit u goes to the rank whose equal share
  * [r*Psi/N, (r+1)*Psi/N) holds the unit's midpoint (with U = k*N equal units
- * the pages' k consecutive units per rank); pad is ignored.  *out receives a
- * context to free with zero_destroy().  ZSMR_ERR_ARG if numel exceeds
+ * the pages' k consecutive units per rank -- for unequal units this default is
+ * a reading no passage fixes; zero_set_unit_owners() sets any other map);
+ * pad is ignored.  *out receives a context to free with zero_destroy().  ZSMR_ERR_ARG if numel exceeds
  * ZSMR_MAX_NUMEL, world ZSMR_MAX_WORLD or n_units ZSMR_MAX_UNITS, or if the
  * host allocation of the context fails; *out is then NULL. */
 int32_t zero_init_shards(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
                          int32_t grad_dtype, int32_t param_dtype, int32_t pad,
                          const int64_t* unit_numel, int32_t n_units);
 
-/* Free a context (NULL is ignored). */
+/* Free a context (NULL is ignored).  Library plumbing. */
 void zero_destroy(zsmr_ctx* ctx);
 
-/* Copy the partition's sizes into *out (host only). */
+/* Copy the partition's sizes into *out (host only): Psi, the padded length
+ * N*ceil(Psi/N) and the shard ceil(Psi/N) ("ZeRO and FSDP", ZeroAdam.__init__
+ * and _flatten), the largest unit ("ZeRO and FSDP", "ZeRO-3 and FSDP"). */
 int32_t zero_layout_info(const zsmr_ctx* ctx, zsmr_layout_info* out);
 
 /* Index map (host only): padded flat offset and length of what `rank` owns
  * in `unit` (stages 0-2: unit must be 0), and the offset of that piece inside
- * the rank's own concatenated shard.  Stage 4: the unit's start and length
+ * the rank's own concatenated shard.  The slice a rank keeps is
+ * [rank*S, rank*S + S) of the flat vector ("The four schemes", Base.__init__;
+ * "ZeRO and FSDP", ZeroAdam.__init__, lo = rank * shard); at stage 3 the same
+ * split is made within each unit ("ZeRO and FSDP", "ZeRO-3 and FSDP").  Stage 4: the unit's start and length
  * for its owner, length 0 for every other rank; the local offset is within
  * the owner's units.  Any output pointer may be NULL. */
 int32_t zero_layout(const zsmr_ctx* ctx, int32_t rank, int32_t unit,
                     int64_t* offset, int64_t* len, int64_t* local_offset);
 
-/* Stage 4: the rank owning `unit` (host only).  ZSMR_ERR_ARG at other stages. */
+/* Stage 4: the rank owning `unit` (host only).  ZSMR_ERR_ARG at other stages.
+ * ("One Poem Suffices: ZeRO" section 4.1.4; "ZeRO, annotated" section 7.) */
 int32_t zero_unit_owner(const zsmr_ctx* ctx, int32_t unit, int32_t* owner);
+
+/* Stage 4: give unit u to rank owners[u], for every unit (host only).  The
+ * pages fix owners only for equal partitions ("One Poem Suffices: ZeRO"
+ * section 4.1.4: 192 equal blocks, 3 consecutive ones per device of 64;
+ * "ZeRO, annotated" section 7: GPU i owns shard i); for any other unit list
+ * the caller chooses, here, which rank holds each unit's master, m and v and
+ * broadcasts it.  Offsets within each owner's concatenated units follow the
+ * natural unit order.  n_units must equal the context's unit count and every
+ * owner lie in [0, world), else ZSMR_ERR_ARG (also at stages 0-3).
+ * ZSMR_ERR_STATE if any unit is live or any counter or schedule count is
+ * non-zero: call it before the first step (or after zero_reset_counters()
+ * with no unit live); the context is then unchanged. */
+int32_t zero_set_unit_owners(zsmr_ctx* ctx, const int32_t* owners, int32_t n_units);
 
 /* Accounting for one rank (pure, host only).  gather_bytes: bytes per
  * gathered element of the stage-3 peak (0 = the 16-bit working copy's 2; the
@@ -191,18 +216,29 @@ int32_t zero_bytes_per_rank(const zsmr_ctx* ctx, int32_t gather_bytes, int32_t m
                             zsmr_bytes* out);
 
 /* The same accounting for a given rank (stage 4: ranks owning different
- * amounts hold and move different amounts). */
+ * amounts hold and move different amounts; "One Poem Suffices: ZeRO"
+ * section 4.1.4, the owner's shard plus one borrowed block). */
 int32_t zero_bytes_of_rank(const zsmr_ctx* ctx, int32_t rank, int32_t gather_bytes,
                            int32_t max_live, zsmr_bytes* out);
 
 /* Counters of `rank` accumulated by the calls below since creation or the
- * last zero_reset_counters() (host only). */
+ * last zero_reset_counters() (host only): the elements each simulated
+ * collective moved for that rank, in the same units as zero_bytes_per_rank
+ * ("The four schemes", bytes_comm_per_rank and the Comm calls of each
+ * scheme's step; "ZeRO, annotated" section 7, the all-gathers of the
+ * forward and backward passes and the reduce-scatter), and the ZeRO-3
+ * schedule's gathers, releases and live bytes ("The four schemes", where the
+ * third P comes from). */
 int32_t zero_counters(const zsmr_ctx* ctx, int32_t rank, zsmr_counters* out);
+/* Zero every counter of zero_counters() (live units stay live). */
 int32_t zero_reset_counters(zsmr_ctx* ctx);
 
 /* Device-side init of one (rank, unit) piece of length len = layout len:
  * master = theta0, m = v = 0, p16 = RNE16(theta0).  theta0 points at the
- * piece's initial values (fp32, len), p16 at where its 16-bit copy lives. */
+ * piece's initial values (fp32, len), p16 at where its 16-bit copy lives.
+ * ("The four schemes", Base.__init__: the fp32 master copied from theta0,
+ * zero moments, the 16-bit working copy cast from it; "ZeRO and FSDP",
+ * ZeroAdam.__init__: master = the rank's slice, m = v = 0.) */
 int32_t zero_init_state(const zsmr_ctx* ctx, int32_t rank, int32_t unit, const float* theta0,
                         float* master, float* m, float* v, void* p16, hipStream_t stream);
 
@@ -229,14 +265,23 @@ int32_t zero_adam_step(float* master, float* m, float* v, const float* g, int64_
 
 /* Cast only: p16_dst[j] = RNE16(master[j]) for the (rank, unit) piece -- the
  * all-gather side of stages 1-2 (into slot r of the working copy) and the
- * rank's own 16-bit shard at stage 3. */
+ * rank's own 16-bit shard at stage 3.  ("The four schemes", ZeRO1.step: the
+ * gathered masters cast to the 16-bit copy; "ZeRO and FSDP", ZeroAdam.step:
+ * all_gather_into_tensor of the updated slice into the full parameters;
+ * "Sharding the States.": the all-gather moves the 16-bit weights.)  At
+ * stages 1-2 it counts the all-gather that delivers this slot to the other
+ * ranks. */
 int32_t zero_gather_cast(zsmr_ctx* ctx, int32_t rank, int32_t unit, const float* master,
                          void* p16_dst, hipStream_t stream);
 
 /* The hot path: reduce + Adam + cast in one pass over the (rank, unit)
  * piece, reading each gradient row, master, m and v once and writing master,
  * m, v and the 16-bit copy once.  Bit-identical to zero_reduce_shard(mean=1)
- * + zero_adam_step + zero_gather_cast.  t >= 1 is the step number (the same
+ * + zero_adam_step + zero_gather_cast.  It is the middle of a sharded step as
+ * the pages give it: reduce-scatter the gradients, update the rank's own
+ * slice, all-gather it ("ZeRO and FSDP", ZeroAdam.step and the remark after
+ * the three-stage table; "The four schemes", ZeRO1.step and ZeRO3.step;
+ * "ZeRO, annotated" section 5.2).  t >= 1 is the step number (the same
  * for every rank and unit of a step). */
 int32_t zero_fused_step(zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* grads,
                         int64_t row_stride, int64_t base_elem, float* master, float* m,
@@ -251,7 +296,9 @@ int32_t zero_fused_step(zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* g
  * exactly as for zero_fused_step; the call touches only the sub-range.
  * Calls over disjoint sub-ranges that cover the piece, with the same t, give
  * the same bits as one zero_fused_step.  ZSMR_ERR_ARG if begin < 0, count < 0
- * or begin + count exceeds the piece.  Counts count elements of traffic. */
+ * or begin + count exceeds the piece, and at stage ZSMR_DP unless the range
+ * is the whole vector (a replica's all-reduce covers the whole vector and is
+ * counted once per step).  Counts count elements of traffic. */
 int32_t zero_fused_step_range(zsmr_ctx* ctx, int32_t rank, int32_t unit, int64_t begin,
                               int64_t count, const void* grads, int64_t row_stride,
                               int64_t base_elem, float* master, float* m, float* v,
@@ -259,7 +306,10 @@ int32_t zero_fused_step_range(zsmr_ctx* ctx, int32_t rank, int32_t unit, int64_t
 
 /* All-gather receive: copy n 16-bit elements src -> dst (peers' slices into
  * the working copy of recv_rank); counted as all-gather traffic received by
- * recv_rank.  Overlapping src and dst is not allowed. */
+ * recv_rank.  Overlapping src and dst is not allowed.  ("ZeRO and FSDP",
+ * ZeroAdam.step: all_gather_into_tensor assembles every rank's slice into
+ * the complete parameters; "Sharding the States.": the 16-bit all-gather of
+ * (N-1)/N of the weights.) */
 int32_t zero_gather_copy(zsmr_ctx* ctx, int32_t recv_rank, const void* src, void* dst,
                          int64_t n, hipStream_t stream);
 
@@ -299,14 +349,41 @@ int32_t zero_stage3_set_max_live(zsmr_ctx* ctx, int32_t max_live);
 int32_t zero_stage3_unit_gather(zsmr_ctx* ctx, int32_t unit, const void* const* shard_ptrs,
                                 void* unit_buf, hipStream_t stream);
 
-/* Release unit `unit` (host only).  ZSMR_ERR_STATE if it is not live. */
+/* Release unit `unit` (host only): the gathered copy is dropped and only
+ * the rank's own slice stays ("The four schemes", where the third P comes
+ * from: gather, use, release, gather again for backward; "ZeRO and FSDP",
+ * "ZeRO-3 and FSDP" steps 1-2).  ZSMR_ERR_STATE if it is not live. */
 int32_t zero_stage3_unit_release(zsmr_ctx* ctx, int32_t unit);
 
-/* Schedule state of one unit (host only); any output pointer may be NULL. */
+/* Schedule state of one unit (host only): live or not, gathers and releases
+ * so far ("The four schemes", where the third P comes from).  Any output
+ * pointer may be NULL. */
 int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
                                int64_t* gathers, int64_t* releases);
 
-/* Launch shape.  step_bpc, 0..64: the grid of the step kernels (reduce,
+/* Diagnostics: the kernel a call of zero_fused_step with these arguments
+ * runs, without running it (host only, but the write windows depend on the
+ * current device's clock rate).  The arguments are checked exactly as
+ * zero_fused_step checks them (the Adam constants aside), with the same
+ * errors.  A library query, no passage of the pages: it lets a caller (and
+ * the tests) confirm which of the equivalent kernels its buffers select. */
+#define ZSMR_KERNEL_SCALAR   0  /* one element per lane: an operand is not vector-aligned  */
+#define ZSMR_KERNEL_DIRECT   1  /* 8 elements per lane, results stored at once             */
+#define ZSMR_KERNEL_DEFERRED 2  /* 8 elements per lane, results kept in LDS, stored later  */
+typedef struct zsmr_plan {
+    int32_t kernel;       /* ZSMR_KERNEL_*                                               */
+    int32_t ring_tiles;   /* deferred: completed 512-element tiles each wave keeps in LDS */
+    int32_t windowed;     /* deferred: stores wait for chip-wide write windows            */
+    int32_t store_elems;  /* 16-bit elements per store of the working copy (4, 2, 1)      */
+    int32_t launches;     /* launches the piece is cut into (2^30 elements each at most)  */
+    int64_t head;         /* leading elements run one by one to reach a 128-byte line      */
+} zsmr_plan;
+int32_t zsmr_fused_step_plan(const zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* grads,
+                             int64_t row_stride, int64_t base_elem, float* master, float* m,
+                             float* v, void* p16_dst, zsmr_plan* out);
+
+/* Launch shape of the kernels behind the calls above.  No passage of the
+ * pages concerns it (they run NumPy and gloo on CPUs).  step_bpc, 0..64: the grid of the step kernels (reduce,
  * Adam, cast, and the fused step when it writes at once), where 0 (the
  * default) gives one 512-element wave tile per wave and as many workgroups
  * as the launch needs, and k > 0 a grid-stride grid of k workgroups per
@@ -323,7 +400,8 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* ctx, int32_t unit, int32_t* live,
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows);
 
-/* Write windows of the fused step's deferred writes.  Every cycle_ns, the
+/* Write windows of the fused step's deferred writes.  A speed knob of
+ * zero_fused_step; no passage of the pages concerns it.  Every cycle_ns, the
  * last write_ns form a window that all waves on the GPU take at the same
  * time, read from the chip's constant-rate clock: deferred results are
  * stored only inside windows, and no gradient loads are issued from
@@ -337,7 +415,7 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
  * full).
  * Otherwise 1,000 <= cycle_ns <= 10,000,000, write_ns >= 1, margin_ns >= 0,
  * write_ns + margin_ns < cycle_ns and 0 <= lead_ns < write_ns; ZSMR_ERR_ARG
- * if not.  Defaults: 74,000 / 12,000 / 1,000 / 2,000.  The best cycle follows
+ * if not.  Defaults: 72,000 / 11,000 / 1,000 / 4,000.  The best cycle follows
  * the device's read rate (it is the time the rings take to fill), so a
  * caller that can time the step may tune it.  Process-wide.  Affects speed
  * only, never results. */
@@ -345,7 +423,8 @@ int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin
                               int32_t lead_ns);
 
 /* Work split of the copies (zero_gather_copy, zero_gather_copy_blocks,
- * zero_stage3_unit_gather): the regions a copy is cut into go to the eight
+ * zero_stage3_unit_gather); a speed knob, no passage of the pages concerns
+ * it: the regions a copy is cut into go to the eight
  * XCDs in contiguous runs, each even-numbered XCD taking even_permille / 1000
  * times the regions of each odd one.  On MI355X the even XCDs move data
  * faster than the odd ones, so equal shares leave them idle at the end of a

@@ -31,8 +31,10 @@ arithmetic step and no fused multiply-add.  Every function is pinned by
 ``tests/test_oracle_*.py`` against values printed on the pages, closed forms,
 library routines (torch casts, ``torch.optim.Adam``) or brute force.
 
-Parity unpinned: which rank owns a unit of unequal size under owner
+Parity unpinned: the default owner of a unit of unequal size under owner
 broadcast (``layout.unit_owners`` on unequal units).  The pages show only
 equal partitions, where the rule is pinned; for unequal units it is a
-reading (the unit's midpoint decides) that no passage fixes.
+reading (the unit's midpoint decides) that no passage fixes.  An explicit
+owner map (``make_layout(..., owners=...)``) avoids the reading: the tests
+that run unequal units on the GPU pass one.
 """

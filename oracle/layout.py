@@ -17,10 +17,12 @@ Test infrastructure only (see the package header).
   GPU i owns shard i): every unit belongs whole to one rank, which sends it to
   the others when it is needed.  Nothing is padded; the vector keeps its
   natural order.  The pages only show equal partitions (each rank owning the
-  same number of equal blocks); the reading taken for any unit sizes is that
-  unit u goes to the rank whose equal share [r*Psi/N, (r+1)*Psi/N) holds the
-  unit's midpoint, which gives exactly the pages' contiguous k-blocks-per-rank
-  ownership when U = k*N equal units.
+  same number of equal blocks, k consecutive ones when U = k*N).  Any other
+  owner map is the caller's choice and is passed in as ``owners``; without
+  one, the default is a reading: unit u goes to the rank whose equal share
+  [r*Psi/N, (r+1)*Psi/N) holds the unit's midpoint, which gives exactly the
+  pages' contiguous k-blocks-per-rank ownership on equal partitions and is
+  parity unpinned on unequal units.
 """
 from __future__ import annotations
 
@@ -147,19 +149,41 @@ def unit_owners(units: Sequence[int], world: int) -> tuple:
     return tuple(owners)
 
 
+def pages_owners(n_units: int, world: int) -> tuple:
+    """The pages' owner map for U = k*N equal units: rank r owns the k
+    consecutive units [r*k, (r+1)*k) ("One Poem Suffices: ZeRO" section 4.1.4,
+    192 blocks on 64 devices, 3 each; "ZeRO, annotated" section 7, GPU i owns
+    shard i)."""
+    if n_units % world:
+        raise ValueError("the pages' partition needs a multiple of N units")
+    k = n_units // world
+    return tuple(u // k for u in range(n_units))
+
+
 def make_layout(numel: int, world: int, stage: int, units: Optional[Sequence[int]] = None,
-                pad: bool = False, owner_broadcast: bool = False) -> Layout:
+                pad: bool = False, owner_broadcast: bool = False,
+                owners: Optional[Sequence[int]] = None) -> Layout:
+    """``owners`` (owner broadcast only): the rank owning each unit; None
+    takes the midpoint reading of ``unit_owners``."""
     if numel < 1 or world < 1 or stage not in (0, 1, 2, 3):
         raise ValueError("bad numel/world/stage")
     if owner_broadcast and stage != 3:
         raise ValueError("owner broadcast is a stage-3 layout")
+    if owners is not None and not owner_broadcast:
+        raise ValueError("an owner map belongs to the owner-broadcast layout")
     unit_list: List[int] = list(units) if units else [numel]
     if any(u < 1 for u in unit_list) or sum(unit_list) != numel:
         raise ValueError("unit sizes must be positive and sum to numel")
     starts = [sum(unit_list[:i]) for i in range(len(unit_list))]
     if owner_broadcast:
+        if owners is None:
+            owner_map = unit_owners(unit_list, world)
+        else:
+            owner_map = tuple(int(o) for o in owners)
+            if len(owner_map) != len(unit_list) or any(not 0 <= o < world for o in owner_map):
+                raise ValueError("one owner in [0, N) per unit")
         return Layout(numel, world, 3, tuple(unit_list), pad, tuple(unit_list), tuple(starts),
-                      tuple(starts), unit_owners(unit_list, world))
+                      tuple(starts), owner_map)
     if stage == 0:
         shard_u = (numel,)
     elif stage in (1, 2):

@@ -428,11 +428,12 @@ SCHEMES = {0: DP, 1: ZeRO1, 2: ZeRO2, 3: ZeRO3}
 def run(stage: int, numel: int, world: int, theta0: np.ndarray,
         grads_per_step: Callable[[int], Sequence[np.ndarray]], steps: int, dtype16: str,
         lr: float, betas=(0.9, 0.999), eps: float = 1e-8, units=None, pad: bool = False,
-        owner_broadcast: bool = False, **kw):
+        owner_broadcast: bool = False, owners=None, **kw):
     """Build a scheme and run ``steps`` steps; ``grads_per_step(t)`` returns the
     N per-rank 16-bit gradient vectors of step t (t = 1..steps).  Stage 3 with
-    ``owner_broadcast`` runs ``ZeRO3Owner``."""
-    lay = make_layout(numel, world, stage, units, pad, owner_broadcast)
+    ``owner_broadcast`` runs ``ZeRO3Owner``, its units owned as ``owners``
+    says (None: the layout's default reading)."""
+    lay = make_layout(numel, world, stage, units, pad, owner_broadcast, owners)
     cls = ZeRO3Owner if owner_broadcast else SCHEMES[stage]
     sch = cls(lay, theta0, dtype16, lr, betas, eps, **kw)
     for t in range(1, steps + 1):

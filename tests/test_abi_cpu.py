@@ -134,6 +134,21 @@ def test_page_pins_through_the_c_library():
     assert b["res_master"] + b["res_m"] + b["res_v"] == 57636
 
 
+def test_unprinted_count_pins_through_the_c_library():
+    """"Sharding the States." Llama 3 70B on 64 devices: the parameter counts
+    at which the C library's per-device bytes round to 295.4 / 156.5 / 17.6
+    GB overlap, in the same interval the oracle finds."""
+    from decimal import Decimal
+    from tests import test_oracle_accounting as pa
+
+    def c_value(pin, psi):
+        ctx = z.zero_init_shards(psi, pin["world"], pin["stage"], "bf16", pad=pin["pad"])
+        return Decimal(z.zero_bytes_per_rank(ctx, pin["gather_bytes"])["resident"])
+    lo, hi = pa.solve_common_count(pa.SOLVED_PINS, c_value)
+    assert lo < hi
+    assert (lo, hi) == pa.solve_common_count(pa.SOLVED_PINS)
+
+
 def test_init_errors():
     with pytest.raises(z.ZsmrError) as e:
         z.zero_init_shards(1001, 4, 2, "bf16")
@@ -325,6 +340,71 @@ def test_owner_random_layouts_match_oracle():
         r = rnd.randrange(world)
         got = z.zero_bytes_of_rank(ctx, r, 2, rnd.randint(1, 3))
         assert got["resident"] == 16 * lay.own_numel(r)
+
+
+def test_explicit_owner_maps_match_oracle():
+    """Owners chosen by the caller (any map, not only the midpoint default):
+    the library's index map and per-rank accounting equal the oracle's for
+    the same map; the pages' own partition (k consecutive equal units per
+    rank) is one of them."""
+    from oracle.layout import pages_owners
+    rnd = random.Random(5)
+    cases = [(192_000, 64, [1000] * 192, list(pages_owners(192, 64))),
+             (6000, 5, [1000, 7, 2993, 1500, 500], [3, 0, 3, 1, 4]),
+             (8_030_261_248, 8, [1_050_677_248] + [218_112_000] * 32,
+              [0] + [1] * 5 + [2] * 5 + [3] * 5 + [4] * 5 + [5] * 4 + [6] * 4 + [7] * 4)]
+    for _ in range(200):
+        world = rnd.randint(1, 12)
+        units = [rnd.randint(1, 10 ** rnd.randint(1, 5)) for _ in range(rnd.randint(1, 15))]
+        cases.append((sum(units), world, units, [rnd.randrange(world) for _ in units]))
+    for numel, world, units, owners in cases:
+        ctx = z.zero_init_shards(numel, world, z.ZSMR_ZERO3_OWNER, "bf16", units=units)
+        z.zero_set_unit_owners(ctx, owners)
+        lay = make_layout(numel, world, 3, units, owner_broadcast=True, owners=owners)
+        assert ctx.info()["shard_numel"] == lay.shard_numel
+        for u in range(len(units)):
+            assert z.zero_unit_owner(ctx, u) == owners[u] == lay.owners[u]
+            for r in range(world):
+                off, ln, loc = z.zero_layout(ctx, r, u)
+                assert (off, ln) == lay.owned(r, u)
+                if ln:
+                    assert loc == lay.local_offset(u)
+        for ml in (1, 2):
+            for r in range(world):
+                got = z.zero_bytes_of_rank(ctx, r, 2, ml)
+                want = acc.bytes_per_rank(lay, max_live=ml, rank=r)
+                assert got == {k: getattr(want, k) for k in got}, (owners, r)
+            worst = z.zero_bytes_per_rank(ctx, 2, ml)
+            want = acc.bytes_per_rank(lay, max_live=ml)
+            assert worst == {k: getattr(want, k) for k in worst}
+
+
+def test_owner_map_errors():
+    ctx, _ = _owner_case(64, 4, [16] * 4)
+    for bad in ([0, 1, 2], [0, 1, 2, 4], [0, -1, 2, 3]):
+        with pytest.raises(z.ZsmrError) as e:
+            z.zero_set_unit_owners(ctx, bad)
+        assert e.value.code == z.ZSMR_ERR_ARG
+    split = z.zero_init_shards(64, 4, 3, "bf16", units=[32, 32])
+    with pytest.raises(z.ZsmrError) as e:
+        z.zero_set_unit_owners(split, [0, 1])
+    assert e.value.code == z.ZSMR_ERR_ARG
+    # a fresh context takes any map, and may be given another before its first use
+    # (a map is refused once a call has counted something: the host driver's check)
+    z.zero_set_unit_owners(ctx, [0, 0, 1, 1])
+    z.zero_set_unit_owners(ctx, [3, 2, 1, 0])
+    assert [z.zero_unit_owner(ctx, u) for u in range(4)] == [3, 2, 1, 0]
+
+
+def test_stage3_gather_refuses_a_short_pointer_list():
+    """The library reads N shard pointers at stage 3: the binding refuses a
+    shorter list before any call."""
+    ctx = z.zero_init_shards(64, 4, 3, "bf16", units=[32, 32])
+    with pytest.raises(ValueError, match="shard pointers"):
+        z.zero_stage3_unit_gather(ctx, 0, [1 << 20, 1 << 21], 1 << 22, stream=0)
+    own, _ = _owner_case(64, 4, [16] * 4)
+    with pytest.raises(ValueError, match="shard pointers"):
+        z.zero_stage3_unit_gather(own, 0, [], 1 << 22, stream=0)
 
 
 def test_owner_argument_errors():

@@ -182,25 +182,29 @@ def test_stage3_llama8b_full_size():
 def test_piece_larger_than_one_launch(defer):
     """A piece of 2^30 + 1,029 elements: the host cuts it into a launch of
     2^30 elements and one of the rest (a partial wave tile plus a ragged
-    tail); 9 rows, so that defer=5 runs the deferred-write kernel; checked
-    around the cut and at the ends."""
+    tail); 9 rows on 128-byte lines, so that defer=0 runs the direct kernel
+    and defer=5 the deferred-write kernel across the cut (the library's plan
+    says so); checked around the cut and at the ends."""
     import synth
     import synth.gpu as sgpu
     z.zsmr_set_launch_shape(0, 0, defer, 1)
     try:
         n, world, T, lr = (1 << 30) + 1029, 9, 2, 1e-3
-        say(f"[full] piece over 2^30: n={n} defer={defer}")
+        stride = (n + 63) // 64 * 64
+        say(f"[full] piece over 2^30: n={n} stride={stride} defer={defer}")
         ctx = z.zero_init_shards(n * world, world, 2, "bf16")
-        grads = torch.empty(world * n, dtype=torch.bfloat16, device="cuda")
+        grads = torch.empty(world * stride, dtype=torch.bfloat16, device="cuda")
         theta = torch.empty(n, dtype=torch.float32, device="cuda")
         sgpu.fill32(theta, n, 0, n, 0, synth.TAG_THETA, 0, 0, 0.02)
         master, m, v = torch.empty_like(theta), torch.empty_like(theta), torch.empty_like(theta)
         p16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        plan = z.zsmr_fused_step_plan(ctx, 0, 0, grads, stride, 0, master, m, v, p16)
+        assert plan["kernel"] == ("deferred" if defer else "direct") and plan["launches"] == 2, plan
         z.zero_init_state(ctx, 0, 0, theta, master, m, v, p16)
         del theta
         for t in range(1, T + 1):
-            sgpu.fill16(grads, world, n, n, 0, n, 0, synth.TAG_GRAD, 0, t, 1e-3, "bf16")
-            z.zero_fused_step(ctx, 0, 0, grads, n, 0, master, m, v, p16, t, lr)
+            sgpu.fill16(grads, world, stride, n, 0, n, 0, synth.TAG_GRAD, 0, t, 1e-3, "bf16")
+            z.zero_fused_step(ctx, 0, 0, grads, stride, 0, master, m, v, p16, t, lr)
         torch.cuda.synchronize()
         pos = windows([0, 1 << 30, n - 1, (1 << 30) - 512, n - 1029], 0, n, 1 << 14, seed=30)
         want = sampled.trajectory(pos, world, T, "bf16", 1e-3, lr)
@@ -318,23 +322,34 @@ def test_fused_ranges_with_ragged_unaligned_cuts():
 
 
 # ------------------------------------------------- owner-broadcast ZeRO-3 --
-def _owner_small():
-    units = (300_001, 1 << 17, 250_003, (1 << 17) - 1, 64, 200_000)
-    return wl.Workload("owner_small", "stage3_owner_small_6_units_n5_bf16", sum(units), 5, 3, "bf16",
-                       1e-2, 1e-3, 2, units=units)
+_OWNER_UNITS = (300_001, 1 << 17, 250_003, (1 << 17) - 1, 64, 200_000)
+OWNER_CASES = {
+    # uneven units, an odd world, owners chosen out of order (rank 2 owns
+    # nothing, rank 3 two units that are not neighbours): pieces start at any
+    # alignment
+    "explicit": (_OWNER_UNITS, 5, (3, 0, 3, 1, 4, 0)),
+    # the pages' partition: U = k*N equal units, k consecutive ones per rank
+    "pages": ((40_000,) * 15, 5, None),
+}
 
 
 @pytest.mark.parametrize("prefetch", [False, True])
-def test_owner_broadcast_matches_oracle(prefetch):
-    """Whole units owned by single ranks (odd world, uneven units, so one
-    rank owns nothing and pieces start at any alignment): every element
-    against the oracle's owner-broadcast scheme, every rank's counters against
-    the per-rank accounting, and gathered units against the owners' copies."""
+@pytest.mark.parametrize("case", list(OWNER_CASES))
+def test_owner_broadcast_matches_oracle(case, prefetch):
+    """Whole units owned by single ranks, owners given explicitly (the same
+    map to the library and to the oracle): every element against the
+    oracle's owner-broadcast scheme, every rank's counters against the
+    per-rank accounting, and gathered units against the owners' copies."""
     import synth
     from oracle import schemes as sc
-    w = _owner_small()
-    say(f"[owner] small prefetch={prefetch}")
-    s3 = wl.Stage3World(w, check_gathers=True, owner=True, prefetch=prefetch)
+    from oracle.layout import pages_owners
+    units, world, owners = OWNER_CASES[case]
+    if owners is None:
+        owners = pages_owners(len(units), world)
+    w = wl.Workload("owner_small", f"stage3_owner_small_{case}", sum(units), world, 3, "bf16", 1e-2,
+                    1e-3, 2, units=units)
+    say(f"[owner] {case} prefetch={prefetch} owners={owners}")
+    s3 = wl.Stage3World(w, check_gathers=True, owner=True, prefetch=prefetch, owners=owners)
     s3.run(w.steps)
     torch.cuda.synchronize()
     assert s3.gather_mismatch == 0
@@ -342,14 +357,14 @@ def test_owner_broadcast_matches_oracle(prefetch):
     theta = synth.theta0(w.seed, p, w.theta_sigma)
     g = lambda t: [synth.grad16(w.seed, r, t, p, w.grad_sigma, w.dtype) for r in range(w.world)]
     ref = sc.run(3, w.numel, w.world, theta, g, w.steps, w.dtype, w.lr, units=list(w.units),
-                 owner_broadcast=True)
+                 owner_broadcast=True, owners=owners)
     compare({"master": s3.master.cpu().numpy(), "m": s3.m.cpu().numpy(), "v": s3.v.cpu().numpy()},
             {"master": ref.full_master(), "m": ref.full_m(), "v": ref.full_v()},
-            host16(s3.p16), ref.working_copy(), "owner broadcast small")
+            host16(s3.p16), ref.working_copy(), f"owner broadcast {case}")
     assert np.array_equal(s3.master.cpu().numpy().view(np.uint32), ref.full_master().view(np.uint32))
     assert np.array_equal(host16(s3.p16), ref.working_copy())
-    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True)
-    assert [z.zero_unit_owner(s3.ctx, u) for u in range(lay.n_units)] == list(lay.owners)
+    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True, owners=owners)
+    assert [z.zero_unit_owner(s3.ctx, u) for u in range(lay.n_units)] == list(owners)
     ml = 2 if prefetch else 1
     for r in range(w.world):
         c = z.zero_counters(s3.ctx, r)
@@ -365,18 +380,20 @@ def test_owner_broadcast_matches_oracle(prefetch):
 
 
 def test_owner_broadcast_llama8b_full_size():
-    """The Llama-3-8B shape with whole units owned by ranks: sampled elements
-    against the oracle, the whole 16-bit copy against the cast of the master,
-    and the counters of every rank."""
+    """The Llama-3-8B shape with whole units owned by ranks (the explicit
+    map: embeddings and head alone on rank 0, the layers in contiguous runs
+    on ranks 1-7): sampled elements against the oracle, the whole 16-bit copy
+    against the cast of the master, and the counters of every rank."""
     base = wl.WORKLOADS["llama8b"]
     w = wl.Workload("llama8b_owner", "llama3_8b_shape_33_units_n8_zero3_owner_bf16", base.numel,
                     base.world, 3, base.dtype, base.grad_sigma, base.lr, base.steps, units=base.units)
     say(f"[full] llama8b owner broadcast: units={len(w.units)}")
-    s3 = wl.Stage3World(w, check_gathers=True, owner=True)
+    s3 = wl.Stage3World(w, check_gathers=True, owner=True, owners=wl.LLAMA8B_OWNERS)
     s3.run(w.steps)
     torch.cuda.synchronize()
     assert s3.gather_mismatch == 0
-    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True)
+    lay = make_layout(w.numel, w.world, 3, list(w.units), owner_broadcast=True,
+                      owners=wl.LLAMA8B_OWNERS)
     marks = []
     for u in range(lay.n_units):
         marks += [lay.unit_start[u], lay.unit_start[u] + lay.units[u] - 1]

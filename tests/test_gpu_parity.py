@@ -22,10 +22,10 @@ TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
 @pytest.fixture(params=[5, 0], ids=["deferred", "direct"])
 def fused_path(request):
-    """Run a test with the fused step's deferred-write kernel (default) and
-    with the kernel that writes at once; both must give the same bits.  The
-    deferred kernel runs only for more than 8 gradient rows; with fewer both
-    ids run the direct kernel."""
+    """Run a test with the fused step's deferred-write kernel (a ring of 5
+    tiles, from one gradient row on) and with the kernel that writes at once;
+    both must give the same bits.  Where an operand rules out the vector
+    path (unaligned rows or state) both ids run the one-element kernel."""
     z.zsmr_set_launch_shape(0, 0, request.param, 1)
     yield request.param
     z.zsmr_set_launch_shape()
@@ -390,6 +390,28 @@ def test_mixed_formats(gdt, pdt, fused_path):
             {"master": master, "m": m, "v": v}, host16(pb), p16, f"mixed {gdt}->{pdt}")
 
 
+def _padded_rows(rows: np.ndarray, stride: int) -> torch.Tensor:
+    """rows (N x n 16-bit) on the device, row r at r*stride."""
+    buf = np.zeros((rows.shape[0], stride), np.uint16)
+    buf[:, :rows.shape[1]] = rows
+    return dev16(buf.ravel())
+
+
+def _expect_kernel(ctx, grads, stride, master, m, v, p16, kernel, ring=None, windowed=None,
+                   store=None):
+    """Ask the library which kernel these buffers select and insist on it, so
+    that a test meant for one kernel cannot silently run another."""
+    plan = z.zsmr_fused_step_plan(ctx, 0, 0, grads, stride, 0, master, m, v, p16)
+    assert plan["kernel"] == kernel, plan
+    if ring is not None:
+        assert plan["ring_tiles"] == ring, plan
+    if windowed is not None:
+        assert bool(plan["windowed"]) == windowed, plan
+    if store is not None:
+        assert plan["store_elems"] == store, plan
+    return plan
+
+
 @pytest.mark.parametrize("tiles", [5, 3, 1])
 def test_deferred_kernel_many_rounds(tiles):
     """The deferred-write kernel with each wave's LDS ring filled several
@@ -398,6 +420,7 @@ def test_deferred_kernel_many_rounds(tiles):
     z.zsmr_set_launch_shape(0, 0, tiles, 1)
     try:
         n = 1024 * 10 * 512 + 3 * 512 + 77
+        stride = (n + 63) // 64 * 64                       # rows on 128-byte lines, n ragged
         world, T, lr = 9, 2, 1e-3
         ctx = z.zero_init_shards(n * world, world, 2, "bf16")
         steps_rows = {t: _piece_inputs(n, world, "bf16", step=t)[0] for t in range(1, T + 1)}
@@ -407,7 +430,11 @@ def test_deferred_kernel_many_rounds(tiles):
         pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
         z.zero_init_state(ctx, 0, 0, mb.clone(), mb, mm, vb, pb)
         for t in range(1, T + 1):
-            z.zero_fused_step(ctx, 0, 0, dev16(steps_rows[t].ravel()), n, 0, mb, mm, vb, pb, t, lr)
+            G = _padded_rows(steps_rows[t], stride)
+            # 9 rows: no windows, so a ring of at most 2 tiles
+            _expect_kernel(ctx, G, stride, mb, mm, vb, pb, "deferred", ring=min(tiles, 2),
+                           windowed=False)
+            z.zero_fused_step(ctx, 0, 0, G, stride, 0, mb, mm, vb, pb, t, lr)
         torch.cuda.synchronize()
         master, m, v, p16 = _oracle_piece(None, theta, "bf16", "bf16", T, lr, steps_rows)
         compare({"master": host32(mb), "m": host32(mm), "v": host32(vb)},
@@ -416,23 +443,30 @@ def test_deferred_kernel_many_rounds(tiles):
         z.zsmr_set_launch_shape()
 
 
-def _fused_run(n, rows, T, defer, window, guard=64):
+def _fused_run(n, rows, T, defer, window, guard=64, p16_shift=0, expect=None):
     """T fused steps on one n-element piece with rows gradient rows made by
-    the device generator; returns the outputs with `guard` untouched
-    elements on both sides of every buffer."""
+    the device generator (row stride n rounded up to 64 elements, so the
+    vector kernels run); returns the outputs with `guard` untouched elements
+    on both sides of every buffer.  p16_shift moves the 16-bit copy that many
+    elements off its 8-byte alignment (2: 32-bit stores, 1: 16-bit stores).
+    expect: the kernel the buffers must select (checked with the library's
+    plan query)."""
     import synth.gpu as sgpu
     z.zsmr_set_launch_shape(0, 0, defer, 1)
     z.zsmr_set_write_window(*window)
     try:
-        stride = n + 24
+        stride = (n + 63) // 64 * 64
         ctx = z.zero_init_shards(n * rows, rows, 2, "bf16")
         G = torch.empty(rows * stride, dtype=torch.int16, device="cuda")
         th = torch.empty(n, dtype=torch.float32, device="cuda")
         sgpu.fill32(th, n, 0, n, 7, synth.TAG_THETA, 0, 0, 0.02)
-        buf = lambda dt: torch.full((n + 2 * guard,), -3, dtype=dt, device="cuda")
+        buf = lambda dt, extra=0: torch.full((n + 2 * guard + extra,), -3, dtype=dt, device="cuda")
         mb, mm, vb = buf(torch.float32), buf(torch.float32), buf(torch.float32)
-        pb = buf(torch.int16)
+        pb_all = buf(torch.int16, 4)
+        pb = pb_all[p16_shift:p16_shift + n + 2 * guard]
         sl = slice(guard, guard + n)
+        if expect is not None:
+            _expect_kernel(ctx, G, stride, mb[sl], mm[sl], vb[sl], pb[sl], **expect)
         z.zero_init_state(ctx, 0, 0, th, mb[sl], mm[sl], vb[sl], pb[sl])
         for t in range(1, T + 1):
             sgpu.fill16(G, rows, stride, n, 0, n, 7, synth.TAG_GRAD, 0, t, 1e-2, "bf16")
@@ -454,18 +488,21 @@ WINDOWS = {
 
 
 @pytest.mark.parametrize("window", list(WINDOWS), ids=list(WINDOWS))
-@pytest.mark.parametrize("kd", [1, 2, 5])
+@pytest.mark.parametrize("kd", [1, 2, 3, 5])
 @pytest.mark.parametrize("rows", [1, 4, 5, 8, 9, 16, 33, 64])
 def test_deferred_windows_match_direct_bits(window, kd, rows):
     """Write windows and ring sizes change only when results are stored:
     the deferred kernel gives the direct kernel's bits, and writes nothing
     outside the piece.  With 4 rows or fewer a tile is one row batch (its
     first and last); windows apply from 16 rows, their cycle scaled to the
-    row count."""
+    row count (without windows the ring holds at most 2 tiles)."""
     n = 1024 * 6 * 512 + 2 * 512 + 131           # ~6 tiles per wave, a ragged tail
     say(f"[deferred] window={window} kd={kd} rows={rows} n={n}")
-    ref = _fused_run(n, rows, 2, 0, WINDOWS["off"])
-    got = _fused_run(n, rows, 2, kd, WINDOWS[window])
+    windowed = window != "off" and rows >= 16
+    ref = _fused_run(n, rows, 2, 0, WINDOWS["off"], expect={"kernel": "direct"})
+    got = _fused_run(n, rows, 2, kd, WINDOWS[window],
+                     expect={"kernel": "deferred", "windowed": windowed,
+                             "ring": kd if windowed else min(kd, 2)})
     for name, a, b in zip(("master", "m", "v", "p16"), ref, got):
         ai = a.view(torch.int32) if a.dtype == torch.float32 else a
         bi = b.view(torch.int32) if b.dtype == torch.float32 else b
@@ -479,13 +516,27 @@ def test_deferred_windows_match_direct_bits(window, kd, rows):
         assert torch.equal(bi[:g], fi) and torch.equal(bi[-g:], fi)
 
 
-def test_deferred_sampled_against_oracle():
-    """One windowed deferred run (64 rows, default windows) against the
-    oracle on every element of three whole tiles and the tail."""
-    n, rows, T = 1024 * 6 * 512 + 2 * 512 + 131, 64, 2
-    mb, mm, vb, pb = _fused_run(n, rows, T, 5, WINDOWS["default"])
+@pytest.mark.parametrize("rows,kd,p16_shift", [
+    (64, 5, 0), (64, 3, 0),
+    (64, 3, 2), (64, 3, 1),       # 16-bit copy 4-byte and 2-byte aligned (32- and 16-bit stores)
+    (16, 3, 2), (16, 3, 1),       # the fewest rows with windows
+    (24, 3, 0), (33, 3, 1),
+])
+def test_deferred_sampled_against_oracle(rows, kd, p16_shift):
+    """Windowed deferred runs (default windows, rings of 3 and 5 tiles, 16-bit
+    stores of every width) against the oracle on every element of three
+    whole tiles, a wave's later tiles and the tail."""
+    n, T = 1024 * 6 * 512 + 2 * 512 + 131, 2
+    say(f"[deferred sampled] rows={rows} kd={kd} p16_shift={p16_shift}")
+    store = {0: 4, 2: 2, 1: 1}[p16_shift]
+    mb, mm, vb, pb = _fused_run(n, rows, T, kd, WINDOWS["default"], p16_shift=p16_shift,
+                                expect={"kernel": "deferred", "ring": kd, "windowed": True,
+                                        "store": store})
     g = 64
+    # tiles 0, 1023-1024, a wave's second and third tiles (2,048 waves in the
+    # windowed grid of 2 workgroups per CU) and the tail
     pos = np.concatenate([np.arange(0, 512), np.arange(512 * 1023, 512 * 1025),
+                          np.arange(512 * 2048, 512 * 2049), np.arange(512 * 4096, 512 * 4097),
                           np.arange(n - 1200, n)])
     p = pos.astype(np.int64)
     theta = synth.theta0(7, p)
@@ -496,7 +547,8 @@ def test_deferred_sampled_against_oracle():
         master, m, v = nm.adam_update(master, m, v, gr, nm.adam_consts(1e-3, 0.9, 0.999, 1e-8, t))
     at = lambda x: host32(x)[g + pos] if x.dtype == torch.float32 else host16(x)[g + pos]
     compare({"master": at(mb), "m": at(mm), "v": at(vb)}, {"master": master, "m": m, "v": v},
-            at(pb), nm.cast16(master, "bf16"), "deferred windowed sampled")
+            at(pb), nm.cast16(master, "bf16"), f"deferred windowed sampled rows={rows} kd={kd} "
+            f"p16_shift={p16_shift}")
 
 
 @pytest.mark.parametrize("world", [16, 12, 64])     # the mean multiplies by 1/N for 16 and 64

@@ -94,6 +94,16 @@ void set_write_window(int64_t a, int64_t b, int64_t c, int64_t d) {
 }
 static int32_t g_balance;
 void set_xcd_balance(int32_t even_permille) { g_balance = even_permille; }
+static StepArgs g_described;
+void describe_step(int mode, const StepArgs& a, StepPlan* out) {
+    g_described = a;
+    out->kernel = mode;                 // echoed so that the driver can see the mode
+    out->ring_tiles = 3;
+    out->windowed = 1;
+    out->store_elems = 4;
+    out->launches = 1;
+    out->head = 5;
+}
 }  // namespace zsmr
 
 const char* hipGetErrorString(hipError_t) { return "launch refused by the stand-in"; }
@@ -337,6 +347,79 @@ static void launches() {
     CHECK(zero_fused_step(c, 0, 2, at<void>(G), 15, 0, at<float>(M), at<float>(MM), at<float>(V),
                           at<void>(P), 1, &hp, nullptr) == ZSMR_OK);
     CHECK(g_launch.size() == 1);                    // a rank that owns nothing of it: no launch
+    CHECK(zero_set_unit_owners(c, (const int32_t[]){0, 1, 2}, 3) == ZSMR_ERR_STATE);   // used
+    zero_destroy(c);
+
+    // owner broadcast with owners chosen by the caller
+    c = make(30, 3, 4, 0, {10, 5, 15}, &st);
+    const int32_t map[3] = {1, 1, 0}, out_of_range[3] = {1, 3, 0}, negative[3] = {1, -1, 0};
+    CHECK(zero_set_unit_owners(c, map, 2) == ZSMR_ERR_ARG);
+    CHECK(zero_set_unit_owners(c, out_of_range, 3) == ZSMR_ERR_ARG);
+    CHECK(zero_set_unit_owners(c, negative, 3) == ZSMR_ERR_ARG);
+    CHECK(zero_set_unit_owners(c, nullptr, 3) == ZSMR_ERR_ARG);
+    CHECK(zero_set_unit_owners(nullptr, map, 3) == ZSMR_ERR_ARG);
+    CHECK(zero_unit_owner(c, 0, &own) == ZSMR_OK && own == 0);   // unchanged by the refusals
+    CHECK(zero_set_unit_owners(c, map, 3) == ZSMR_OK);
+    for (int32_t u = 0; u < 3; ++u) CHECK(zero_unit_owner(c, u, &own) == ZSMR_OK && own == map[u]);
+    CHECK(zero_layout(c, 1, 1, &off, &len, &loc) == ZSMR_OK && off == 10 && len == 5 && loc == 10);
+    CHECK(zero_layout(c, 0, 2, &off, &len, &loc) == ZSMR_OK && off == 15 && len == 15 && loc == 0);
+    CHECK(zero_layout(c, 2, 0, &off, &len, &loc) == ZSMR_OK && len == 0);
+    zsmr_layout_info oi;
+    CHECK(zero_layout_info(c, &oi) == ZSMR_OK && oi.shard_numel == 15);
+    zsmr_bytes ob;
+    CHECK(zero_bytes_of_rank(c, 2, 0, 1, &ob) == ZSMR_OK && ob.resident == 0);
+    CHECK(ob.rs_elems == 30 && ob.ag_elems == 60 && ob.gathered == 2 * 15);
+    CHECK(zero_bytes_of_rank(c, 1, 0, 2, &ob) == ZSMR_OK && ob.resident == 16 * 15);
+    CHECK(ob.gathered == 2 * 15);                  // a borrowed pair: units 1 (own) and 2
+    g_launch.clear();
+    CHECK(zero_stage3_unit_gather(c, 0, one, at<void>(O), nullptr) == ZSMR_OK);
+    CHECK(zero_counters(c, 1, &k) == ZSMR_OK && k.ag_elems == 0 && k.live_bytes == 0);
+    CHECK(zero_counters(c, 0, &k) == ZSMR_OK && k.ag_elems == 10 && k.live_bytes == 20);
+    CHECK(zero_set_unit_owners(c, map, 3) == ZSMR_ERR_STATE);    // a unit is live
+    CHECK(zero_stage3_unit_release(c, 0) == ZSMR_OK);
+    CHECK(zero_set_unit_owners(c, map, 3) == ZSMR_ERR_STATE);    // counters moved
+    CHECK(zero_reset_counters(c) == ZSMR_OK);
+    const int32_t back[3] = {2, 2, 2};
+    CHECK(zero_set_unit_owners(c, back, 3) == ZSMR_OK);
+    CHECK(zero_layout_info(c, &oi) == ZSMR_OK && oi.shard_numel == 30);
+    CHECK(zero_layout(c, 2, 2, &off, &len, &loc) == ZSMR_OK && len == 15 && loc == 15);
+    zero_destroy(c);
+    c = make(16, 4, 3, 1, {10, 6}, &st);
+    CHECK(zero_set_unit_owners(c, map, 2) == ZSMR_ERR_ARG);     // not an owner-broadcast context
+    zero_destroy(c);
+
+    // data parallel: a replica's all-reduce covers the whole vector, so a
+    // fused range must be the whole vector (counted once per step)
+    c = make(8, 2, 0, 0, {}, &st);
+    g_launch.clear();
+    CHECK(zero_fused_step_range(c, 1, 0, 0, 4, at<void>(G), 8, 0, at<float>(M), at<float>(MM),
+                                at<float>(V), at<void>(P), 1, &hp, nullptr) == ZSMR_ERR_ARG);
+    CHECK(zero_fused_step_range(c, 1, 0, 0, 8, at<void>(G), 8, 0, at<float>(M), at<float>(MM),
+                                at<float>(V), at<void>(P), 1, &hp, nullptr) == ZSMR_OK);
+    CHECK(g_launch.size() == 1 && g_launch[0].a.n == 8);
+    CHECK(zero_counters(c, 1, &k) == ZSMR_OK && k.ar_elems == 2 * 1 * 4 && k.rs_elems == 0);
+    zero_destroy(c);
+
+    // the plan query: the fused step's checks, the first launch's arguments, no launch
+    c = make(16, 4, 3, 1, {10, 6}, &st);
+    g_launch.clear();
+    zsmr_plan pl;
+    CHECK(zsmr_fused_step_plan(c, 2, 1, at<void>(G), 8, 4, at<float>(M), at<float>(MM),
+                               at<float>(V), at<void>(P), &pl) == ZSMR_OK);
+    CHECK(pl.kernel == (zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST) && pl.ring_tiles == 3);
+    CHECK(pl.windowed == 1 && pl.store_elems == 4 && pl.launches == 1 && pl.head == 5);
+    CHECK(zsmr::g_described.grads == at<const uint16_t>(G) + 4 && zsmr::g_described.n == 2);
+    CHECK(zsmr::g_described.nrows == 4 && zsmr::g_described.p16 == at<uint16_t>(P));
+    CHECK(zsmr_fused_step_plan(c, 2, 1, at<void>(G + 1), 8, 4, at<float>(M), at<float>(MM),
+                               at<float>(V), at<void>(P), &pl) == ZSMR_ERR_ALIGN);
+    CHECK(zsmr_fused_step_plan(c, 2, 1, at<void>(G), 1, 4, at<float>(M), at<float>(MM),
+                               at<float>(V), at<void>(P), &pl) == ZSMR_ERR_ARG);
+    CHECK(zsmr_fused_step_plan(c, 2, 1, at<void>(G), 8, 4, at<float>(M), at<float>(MM),
+                               at<float>(V), at<void>(P), nullptr) == ZSMR_ERR_ARG);
+    CHECK(zsmr_fused_step_plan(c, 4, 1, at<void>(G), 8, 4, at<float>(M), at<float>(MM),
+                               at<float>(V), at<void>(P), &pl) == ZSMR_ERR_ARG);
+    CHECK(g_launch.empty());
+    CHECK(zero_counters(c, 2, &k) == ZSMR_OK && k.traffic_elems == 0);
     zero_destroy(c);
 
     // copies: the receive and the block receive

@@ -29,7 +29,8 @@ def load_pins():
             if not line or line.startswith("#"):
                 continue
             tok = shlex.split(line)
-            pins.append(dict(id=tok[0], numel=int(tok[1]), world=int(tok[2]),
+            pins.append(dict(id=tok[0], numel=None if tok[1] == "?" else int(tok[1]),
+                             world=int(tok[2]),
                              stage=int(tok[3].rstrip("o")), owner=tok[3].endswith("o"),
                              units=_units(tok[4]),
                              pad=bool(int(tok[5])), gather_bytes=int(tok[6]), quantity=tok[7],
@@ -63,14 +64,67 @@ def quantity(pin):
     raise KeyError(q)
 
 
-PINS = load_pins()
+ALL_PINS = load_pins()
+PINS = [p for p in ALL_PINS if p["numel"] is not None]
+SOLVED_PINS = [p for p in ALL_PINS if p["numel"] is None]
+
+
+def rounded(pin, value: Decimal) -> Decimal:
+    q = Decimal(1).scaleb(-pin["decimals"])
+    return (value / pin["scale"]).quantize(q, rounding=ROUND_HALF_UP)
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p["id"] for p in PINS])
 def test_page_printed_value(pin):
-    got = quantity(pin) / pin["scale"]
-    q = Decimal(1).scaleb(-pin["decimals"])
-    assert got.quantize(q, rounding=ROUND_HALF_UP) == pin["printed"].quantize(q), pin["source"]
+    assert rounded(pin, quantity(pin)) == pin["printed"].quantize(
+        Decimal(1).scaleb(-pin["decimals"])), pin["source"]
+
+
+def psi_interval(pin, value_of=None, hi=10 ** 13):
+    """[a, b): the parameter counts at which the pin's rounded value equals
+    the printed one.  The quantity never decreases as the count grows, so
+    the counts form one interval; found by bisection."""
+    value_of = value_of or (lambda psi: quantity(dict(pin, numel=psi)))
+    want = pin["printed"].quantize(Decimal(1).scaleb(-pin["decimals"]))
+
+    def first(pred):                     # smallest psi in [1, hi] with pred(psi), else hi
+        a, b = 1, hi
+        while a < b:
+            mid = (a + b) // 2
+            if pred(mid):
+                b = mid
+            else:
+                a = mid + 1
+        return a
+    lo = first(lambda psi: rounded(pin, value_of(psi)) >= want)
+    up = first(lambda psi: rounded(pin, value_of(psi)) > want)
+    return lo, up
+
+
+def solve_common_count(pins, value_of=None):
+    """The counts at which every pin of one model holds: [lo, hi)."""
+    lo, hi = 1, 10 ** 13
+    for pin in pins:
+        a, b = psi_interval(pin, value_of and (lambda psi, p=pin: value_of(p, psi)))
+        lo, hi = max(lo, a), min(hi, b)
+    return lo, hi
+
+
+def test_one_parameter_count_reproduces_the_unprinted_model():
+    # "Sharding the States.": Llama 3 70B's three per-device figures come from
+    # one parameter count, about 70.5e9 (each figure alone fixes it only to a
+    # band; the three bands must overlap)
+    groups = {}
+    for pin in SOLVED_PINS:
+        groups.setdefault(pin["id"][0], []).append(pin)
+    assert set(groups) == {"l"} and len(groups["l"]) == 3
+    for pins in groups.values():
+        lo, hi = solve_common_count(pins)
+        assert lo < hi, [p["source"] for p in pins]
+        assert 70.4e9 < lo < hi < 70.7e9
+        for psi in (lo, (lo + hi) // 2, hi - 1):
+            for pin in pins:
+                assert rounded(pin, quantity(dict(pin, numel=psi))) == pin["printed"], (psi, pin["id"])
 
 
 def test_sixteen_bytes_per_parameter():
@@ -162,6 +216,46 @@ def test_owner_rule_gives_the_pages_contiguous_partitions():
     assert make_layout(192, 64, 3, [1] * 192, owner_broadcast=True).owners == \
         tuple(u // 3 for u in range(192))
     assert make_layout(8, 4, 3, [2] * 4, owner_broadcast=True).owners == (0, 1, 2, 3)
+
+
+def test_pages_owner_map_and_explicit_maps():
+    # the pages' partition written out: 3 consecutive blocks per device of 64
+    from oracle.layout import pages_owners
+    assert pages_owners(192, 64) == tuple(u // 3 for u in range(192))
+    assert pages_owners(4, 4) == (0, 1, 2, 3)
+    lay = make_layout(192, 64, 3, [1] * 192, owner_broadcast=True, owners=pages_owners(192, 64))
+    assert lay.owners == make_layout(192, 64, 3, [1] * 192, owner_broadcast=True).owners
+    with pytest.raises(ValueError):
+        pages_owners(10, 4)
+    for bad in ((0, 1, 2), (0, 1, 2, 4), (0, -1, 2, 3)):
+        with pytest.raises(ValueError):
+            make_layout(64, 4, 3, [16] * 4, owner_broadcast=True, owners=bad)
+    with pytest.raises(ValueError):
+        make_layout(64, 4, 3, [16] * 4, owners=(0, 1, 2, 3))
+
+
+def test_owner_accounting_closed_forms_for_any_map():
+    # any owner map: a rank keeps 16 B per parameter it owns, receives every
+    # other parameter twice (forward and backward broadcasts), sends those
+    # gradients once, and its peak adds the largest borrowed unit(s) live
+    rnd = random.Random(12)
+    for _ in range(200):
+        world = rnd.randint(1, 9)
+        units = [rnd.randint(1, 100) for _ in range(rnd.randint(1, 12))]
+        owners = [rnd.randrange(world) for _ in units]
+        numel = sum(units)
+        lay = make_layout(numel, world, 3, units, owner_broadcast=True, owners=owners)
+        for r in range(world):
+            own = sum(n for n, o in zip(units, owners) if o == r)
+            assert lay.own_numel(r) == own
+            b = acc.bytes_per_rank(lay, rank=r)
+            assert b.resident == 16 * own
+            assert (b.rs_elems, b.ag_elems) == (numel - own, 2 * (numel - own))
+            borrowed = [0 if o == r else n for n, o in zip(units, owners)]
+            assert b.gathered == 2 * max(borrowed)
+            b2 = acc.bytes_per_rank(lay, rank=r, max_live=2)
+            pairs = [borrowed[i] + borrowed[i + 1] for i in range(len(units) - 1)] or borrowed
+            assert b2.gathered == 2 * max(pairs)
 
 
 def test_owner_peak_two_64ths_either_reading():

@@ -65,6 +65,8 @@ ACCOUNTING_PINS = [
     ("owner peak 2/64", pa.test_owner_peak_two_64ths_either_reading),
     ("owner = split when balanced", lambda: [pa.test_owner_balanced_equals_split_layout(w, k)
                                              for w, k in [(4, 1), (4, 3), (8, 4), (64, 3)]]),
+    ("owner forms for any map", pa.test_owner_accounting_closed_forms_for_any_map),
+    ("one count for Llama 3 70B", pa.test_one_parameter_count_reproduces_the_unprinted_model),
 ]
 
 SCHEME_PINS = [

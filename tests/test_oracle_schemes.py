@@ -257,6 +257,22 @@ def test_owner_broadcast_computes_the_same_model(numel, world, units):
     assert np.array_equal(own.working_copy(), dp.working_copy())
 
 
+@pytest.mark.parametrize("owners", [[3, 0, 3, 1, 4], [0, 0, 0, 0, 0], [4, 3, 2, 1, 0]])
+def test_owner_broadcast_with_any_owner_map_computes_the_same_model(owners):
+    # who owns a unit changes who stores and sends it, never the arithmetic
+    numel, world, units = 6000, 5, [1000, 7, 2993, 1500, 500]
+    theta = synth.theta0(0, np.arange(numel))
+    g = grads_fn(numel, world, "bf16", 1e-2)
+    own = sc.run(3, numel, world, theta, g, 2, "bf16", 1e-3, units=units, owner_broadcast=True,
+                 owners=owners)
+    dp = sc.run(0, numel, world, theta, g, 2, "bf16", 1e-3)
+    assert np.array_equal(bits(own.full_master()), bits(dp.full_master()))
+    assert np.array_equal(own.working_copy(), dp.working_copy())
+    for r in range(world):
+        b = acc.bytes_per_rank(own.lay, rank=r)
+        assert (own.rs_elems[r], own.ag_elems[r]) == (2 * b.rs_elems, 2 * b.ag_elems)
+
+
 def test_owner_broadcast_schedule_and_counters():
     numel, world, T = 6000, 5, 3
     units = [1000, 7, 2993, 1500, 500]

@@ -59,6 +59,11 @@ class Workload:
 
 
 LLAMA8B_UNITS = (1_050_677_248,) + (218_112_000,) * 32
+# Owner broadcast on the Llama-3-8B shape: the pages fix owners only for equal
+# partitions, so the owners are chosen here: embeddings + head + final norm
+# alone on rank 0, the 32 layers in contiguous runs of 5, 5, 5, 5, 4, 4, 4 on
+# ranks 1-7 (0.87e9-1.09e9 parameters per rank).
+LLAMA8B_OWNERS = (0,) + (1,) * 5 + (2,) * 5 + (3,) * 5 + (4,) * 5 + (5,) * 4 + (6,) * 4 + (7,) * 4
 
 WORKLOADS = {
     "psi65k": Workload("psi65k", "psi65536_n4_fp16_all_schemes", 65536, 4, 2, "fp16", 1e-2, 1e-2, 5,
@@ -290,10 +295,11 @@ class Stage3World:
     single ranks, natural order, no pad): unit u sits at its start Q_u, its
     owner alone initialises and updates it, a gather copies the owner's
     16-bit copy into the unit buffer, and a unit's gradients are N rows of
-    P_u."""
+    P_u.  ``owners`` gives each unit's owner (None: the library's default)."""
 
     def __init__(self, w: Workload, device="cuda", check_gathers: bool = False,
-                 prefetch: bool = False, fixed_grads: bool = False, owner: bool = False):
+                 prefetch: bool = False, fixed_grads: bool = False, owner: bool = False,
+                 owners=None):
         """prefetch: gather the next unit on a second stream while the current
         one is in use (two unit buffers, at most two units live).
         fixed_grads: generate each unit size's gradients once and reuse them
@@ -306,6 +312,8 @@ class Stage3World:
         stage = z.ZSMR_ZERO3_OWNER if owner else 3
         self.ctx = z.zero_init_shards(w.numel, w.world, stage, w.dtype, pad=w.pad,
                                       units=list(w.units) if w.units else None)
+        if owner and owners is not None:
+            z.zero_set_unit_owners(self.ctx, list(owners))
         if prefetch:
             z.zero_stage3_set_max_live(self.ctx, 2)
         info = self.ctx.info()

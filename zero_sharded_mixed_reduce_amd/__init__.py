@@ -52,6 +52,15 @@ class zsmr_bytes(ctypes.Structure):
                                     "ag_elems", "ar_elems", "traffic_elems", "traffic_bytes")]
 
 
+class zsmr_plan(ctypes.Structure):
+    _fields_ = [("kernel", _i32), ("ring_tiles", _i32), ("windowed", _i32), ("store_elems", _i32),
+                ("launches", _i32), ("head", _i64)]
+
+
+ZSMR_KERNEL_SCALAR, ZSMR_KERNEL_DIRECT, ZSMR_KERNEL_DEFERRED = 0, 1, 2
+KERNEL_NAMES = {0: "scalar", 1: "direct", 2: "deferred"}
+
+
 class zsmr_counters(ctypes.Structure):
     _fields_ = [(n, _i64) for n in ("rs_elems", "ag_elems", "ar_elems", "traffic_elems",
                                     "traffic_bytes", "stage3_gathers", "stage3_releases",
@@ -71,6 +80,7 @@ SIGNATURES = {
     "zero_bytes_per_rank": (_i32, [_vp, _i32, _i32, ctypes.POINTER(zsmr_bytes)]),
     "zero_bytes_of_rank": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(zsmr_bytes)]),
     "zero_unit_owner": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "zero_set_unit_owners": (_i32, [_vp, ctypes.POINTER(_i32), _i32]),
     "zero_counters": (_i32, [_vp, _i32, ctypes.POINTER(zsmr_counters)]),
     "zero_reset_counters": (_i32, [_vp]),
     "zero_init_state": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -81,6 +91,8 @@ SIGNATURES = {
                                ctypes.POINTER(zsmr_adam), _vp]),
     "zero_fused_step_range": (_i32, [_vp, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _i32, ctypes.POINTER(zsmr_adam), _vp]),
+    "zsmr_fused_step_plan": (_i32, [_vp, _i32, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                    ctypes.POINTER(zsmr_plan)]),
     "zero_gather_copy": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
     "zero_gather_copy_blocks": (_i32, [_vp, _i32, _vp, _vp, _i64, _i32, _i64, _vp]),
     "zero_stage3_set_max_live": (_i32, [_vp, _i32]),
@@ -289,6 +301,11 @@ def zero_unit_owner(ctx: Ctx, unit: int) -> int:
     return o.value
 
 
+def zero_set_unit_owners(ctx: Ctx, owners: Sequence[int]) -> None:
+    arr = (_i32 * max(len(owners), 1))(*[int(o) for o in owners])
+    _check(_lib().zero_set_unit_owners(ctx.handle, arr, len(owners)), "zero_set_unit_owners")
+
+
 def zero_counters(ctx: Ctx, rank: int) -> dict:
     out = zsmr_counters()
     _check(_lib().zero_counters(ctx.handle, rank, ctypes.byref(out)), "zero_counters")
@@ -349,6 +366,20 @@ def zero_fused_step(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base
                                   int(t), ctypes.byref(hp), _stream(stream)), "zero_fused_step")
 
 
+def zsmr_fused_step_plan(ctx: Ctx, rank: int, unit: int, grads, row_stride: int, base_elem: int,
+                         master, m, v, p16_dst) -> dict:
+    """Which kernel ``zero_fused_step`` with these arguments runs (nothing is
+    launched): kernel ("scalar", "direct" or "deferred"), ring_tiles,
+    windowed, store_elems, launches, head."""
+    out = zsmr_plan()
+    _check(_lib().zsmr_fused_step_plan(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
+                                       int(base_elem), _ptr(master), _ptr(m), _ptr(v),
+                                       _ptr(p16_dst), ctypes.byref(out)), "zsmr_fused_step_plan")
+    d = {n: getattr(out, n) for n, _ in out._fields_}
+    d["kernel"] = KERNEL_NAMES[d["kernel"]]
+    return d
+
+
 def zero_fused_step_range(ctx: Ctx, rank: int, unit: int, begin: int, count: int, grads,
                           row_stride: int, base_elem: int, master, m, v, p16_dst, t: int,
                           lr: float, betas=(0.9, 0.999), eps: float = 1e-8, stream=None):
@@ -395,6 +426,10 @@ def zero_stage3_unit_gather(ctx: Ctx, unit: int, shard_ptrs: Sequence, unit_buf,
         else:
             each = _piece_len(ctx, 0, unit)
             nsrc = info["world"]
+        if len(shard_ptrs) < nsrc:
+            # the library reads nsrc pointers from the array
+            raise ValueError(f"zero_stage3_unit_gather: {len(shard_ptrs)} shard pointers, "
+                             f"unit {unit} needs {nsrc}")
         for r, p in enumerate(list(shard_ptrs)[:nsrc]):
             _fits(p, each, 2, f"shard {r}")
         _fits(unit_buf, nsrc * each, 2, "unit_buf")
@@ -420,7 +455,7 @@ def zsmr_set_launch_shape(step_bpc: int = 0, copy_bpc: int = 0, defer_tiles: int
                                         int(defer_min_rows)), "zsmr_set_launch_shape")
 
 
-WRITE_WINDOW_DEFAULT = (74000, 12000, 1000, 2000)
+WRITE_WINDOW_DEFAULT = (72000, 11000, 1000, 4000)     # the library's own defaults
 
 
 def zsmr_set_write_window(cycle_ns: int = WRITE_WINDOW_DEFAULT[0],

@@ -130,6 +130,19 @@ int32_t midpoint_owner(int64_t start, int64_t size, int64_t numel, int32_t world
     return r < world - 1 ? (int32_t)r : world - 1;
 }
 
+// Stage 4: each unit's offset within its owner's concatenated units, what
+// every rank owns, and the most any rank owns, from c->owners (no
+// allocation: the vectors are sized when the context is built).
+void assign_owners(zsmr_ctx* c) {
+    std::fill(c->own.begin(), c->own.end(), 0);
+    for (size_t u = 0; u < c->units.size(); ++u) {
+        const int32_t o = c->owners[u];
+        c->local_off[u] = c->own[o];
+        c->own[o] += c->units[u];
+    }
+    c->shard_total = *std::max_element(c->own.begin(), c->own.end());
+}
+
 // Counting of one cast of (rank, unit): at stages 1-2 the all-gather delivers
 // the rank's slot to every other rank; DP and stage 3 cast locally.
 void count_cast(zsmr_ctx* c, int32_t rank, int64_t len) {
@@ -171,20 +184,19 @@ int32_t build_ctx(zsmr_ctx** out, int64_t numel, int32_t world, int32_t stage,
         c->padded = numel;
         c->shard_total = numel;
     } else if (stage == ZSMR_ZERO3_OWNER) {
-        // whole units, natural order, no padding
+        // whole units, natural order, no padding; owners by default from the
+        // midpoint rule, replaceable by zero_set_unit_owners()
         int64_t start = 0;
-        c->own.assign(world, 0);
         for (int64_t u : units) {
-            const int32_t o = midpoint_owner(start, u, numel, world);
             c->shard_u.push_back(u);
             c->unit_pstart.push_back(start);
-            c->local_off.push_back(c->own[o]);
-            c->owners.push_back(o);
-            c->own[o] += u;
+            c->owners.push_back(midpoint_owner(start, u, numel, world));
             start += u;
         }
+        c->local_off.assign(units.size(), 0);
+        c->own.assign(world, 0);
+        assign_owners(c.get());
         c->padded = numel;
-        c->shard_total = *std::max_element(c->own.begin(), c->own.end());
     } else if (stage != ZSMR_ZERO3) {
         if (numel % world && !pad) {
             return ZSMR_ERR_INDIVISIBLE;
@@ -530,10 +542,13 @@ int32_t zero_gather_cast(zsmr_ctx* c, int32_t rank, int32_t unit, const float* m
     return ZSMR_OK;
 }
 
-static int32_t fused_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begin, int64_t count,
-                           bool whole, const void* grads, int64_t row_stride, int64_t base,
-                           float* master, float* m, float* v, void* p16_dst, int32_t t,
-                           const zsmr_adam* hp, hipStream_t stream) {
+// The arguments of the fused step over [begin, begin + count) of the
+// (rank, unit) piece (whole: the piece), checked as every fused call checks
+// them.  *empty is set when there is nothing to launch.
+static int32_t fused_args(const zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begin,
+                          int64_t count, bool whole, const void* grads, int64_t row_stride,
+                          int64_t base, float* master, float* m, float* v, void* p16_dst,
+                          int32_t t, const zsmr_adam* hp, zsmr::StepArgs* a) {
     int32_t st = check_piece(c, rank, unit);
     if (st) return st;
     int64_t len = 0;
@@ -543,29 +558,43 @@ static int32_t fused_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begi
         count = len;
     }
     if (begin < 0 || count < 0 || begin > len - count) return ZSMR_ERR_ARG;
+    // a data-parallel replica's all-reduce covers the whole vector: it is
+    // counted once per step, so a range must be the whole vector too
+    if (c->stage == ZSMR_DP && count != len) return ZSMR_ERR_ARG;
     if ((st = check_grads(c, grads, row_stride, base, len))) return st;
     zsmr::AdamK k{};
     if ((st = check_adam(hp, t, &k))) return st;
     if (!master || !m || !v || !p16_dst) return ZSMR_ERR_ARG;
     if (!al(master, 4) || !al(m, 4) || !al(v, 4) || !al(p16_dst, 2)) return ZSMR_ERR_ALIGN;
-    if (count == 0) return ZSMR_OK;
+    *a = zsmr::StepArgs{};
+    a->grads = static_cast<const uint16_t*>(grads) + base + begin;
+    a->row_stride = row_stride;
+    a->nrows = c->world;
+    a->mean = 1;
+    set_mean_divisor(*a, c->world);
+    a->master = master + begin;
+    a->m = m + begin;
+    a->v = v + begin;
+    a->p16 = static_cast<uint16_t*>(p16_dst) + begin;
+    a->n = count;
+    a->k = k;
+    return ZSMR_OK;
+}
+
+static int32_t fused_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t begin, int64_t count,
+                           bool whole, const void* grads, int64_t row_stride, int64_t base,
+                           float* master, float* m, float* v, void* p16_dst, int32_t t,
+                           const zsmr_adam* hp, hipStream_t stream) {
     zsmr::StepArgs a{};
-    a.grads = static_cast<const uint16_t*>(grads) + base + begin;
-    a.row_stride = row_stride;
-    a.nrows = c->world;
-    a.mean = 1;
-    set_mean_divisor(a, c->world);
-    a.master = master + begin;
-    a.m = m + begin;
-    a.v = v + begin;
-    a.p16 = static_cast<uint16_t*>(p16_dst) + begin;
-    a.n = count;
-    a.k = k;
+    const int32_t st = fused_args(c, rank, unit, begin, count, whole, grads, row_stride, base,
+                                  master, m, v, p16_dst, t, hp, &a);
+    if (st) return st;
+    if (a.n == 0) return ZSMR_OK;
     const hipError_t e =
         zsmr::launch_step(zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST, c->gdt, c->pdt, a, stream);
     if (e != hipSuccess) return hip_fail(e);
-    count_reduce(c, rank, count);
-    count_cast(c, rank, count);
+    count_reduce(c, rank, a.n);
+    count_cast(c, rank, a.n);
     return ZSMR_OK;
 }
 
@@ -582,6 +611,26 @@ int32_t zero_fused_step_range(zsmr_ctx* c, int32_t rank, int32_t unit, int64_t b
                               int32_t t, const zsmr_adam* hp, hipStream_t stream) {
     return fused_range(c, rank, unit, begin, count, false, grads, row_stride, base, master, m, v,
                        p16_dst, t, hp, stream);
+}
+
+int32_t zsmr_fused_step_plan(const zsmr_ctx* c, int32_t rank, int32_t unit, const void* grads,
+                             int64_t row_stride, int64_t base, float* master, float* m, float* v,
+                             void* p16_dst, zsmr_plan* out) {
+    if (!out) return ZSMR_ERR_ARG;
+    const zsmr_adam hp{1e-3, 0.9, 0.999, 1e-8};
+    zsmr::StepArgs a{};
+    const int32_t st = fused_args(c, rank, unit, 0, 0, true, grads, row_stride, base, master, m, v,
+                                  p16_dst, 1, &hp, &a);
+    if (st) return st;
+    zsmr::StepPlan p{};
+    zsmr::describe_step(zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST, a, &p);
+    out->kernel = p.kernel;
+    out->ring_tiles = p.ring_tiles;
+    out->windowed = p.windowed;
+    out->store_elems = p.store_elems;
+    out->launches = p.launches;
+    out->head = p.head;
+    return ZSMR_OK;
 }
 
 int32_t zero_gather_copy(zsmr_ctx* c, int32_t recv_rank, const void* src, void* dst, int64_t n,
@@ -685,6 +734,23 @@ int32_t zero_stage3_unit_state(const zsmr_ctx* c, int32_t unit, int32_t* live, i
     if (live) *live = c->live[unit];
     if (gathers) *gathers = c->gathers[unit];
     if (releases) *releases = c->releases[unit];
+    return ZSMR_OK;
+}
+
+int32_t zero_set_unit_owners(zsmr_ctx* c, const int32_t* owners, int32_t n_units) {
+    if (!c || !owners || c->stage != ZSMR_ZERO3_OWNER || n_units != (int32_t)c->units.size())
+        return ZSMR_ERR_ARG;
+    for (int32_t u = 0; u < n_units; ++u)
+        if (owners[u] < 0 || owners[u] >= c->world) return ZSMR_ERR_ARG;
+    // only on a context no call has used yet (or whose counters were reset
+    // with no unit live): counters and schedule state follow the owners
+    bool used = c->live_units != 0;
+    for (int32_t r = 0; r < c->world; ++r)
+        used = used || c->rs[r] || c->ag[r] || c->ar[r] || c->live_bytes[r] || c->peak_live_bytes[r];
+    for (size_t u = 0; u < c->units.size(); ++u) used = used || c->gathers[u] || c->releases[u];
+    if (used) return ZSMR_ERR_STATE;
+    std::copy(owners, owners + n_units, c->owners.begin());
+    assign_owners(c);
     return ZSMR_OK;
 }
 

@@ -106,12 +106,13 @@ constexpr int kRingWithoutWindows = 2;
 // The read phase, ~63 us, is about the time two waves per SIMD take to fill
 // their 3-tile rings: a longer cycle idles until its window, a shorter one
 // pays the window more often; +-4 us cost 3-5%.  The best window follows
-// the device's read rate (72 / 12 / 1 / 4 won by 1.7% on one box and lost by
-// 4% on another), so callers that can time the step should tune it.
-int64_t g_window_cycle_ns = 74000;
-int64_t g_window_write_ns = 12000;
+// the device's read rate, so callers that can time the step may tune it;
+// the default is the window a tuning over 31 candidates picked on three
+// boxes of three (72 / 11 / 1 / 4 us, 2.70-2.72 ms per step).
+int64_t g_window_cycle_ns = 72000;
+int64_t g_window_write_ns = 11000;
 int64_t g_window_margin_ns = 1000;
-int64_t g_window_lead_ns = 2000;
+int64_t g_window_lead_ns = 4000;
 // The cycle as set is the one for 64 rows of 16-bit gradients.  A wave's
 // ring fills in a time proportional to the bytes its tiles move per element
 // (2 * rows + 26: the gradient rows, master, m and v read and written, the
@@ -474,7 +475,9 @@ __global__ __launch_bounds__(kThreads, KD <= kRingTwoPerCu ? 2 : 1) void step_de
     // the ring: tiles [flushed, done) of this wave are in LDS, not yet stored
     uint32_t done = 0, flushed = 0;
     auto flush = [&]() {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");   // the ring holds other lanes' values
+        // the ring holds other lanes' values: release this lane's ring stores
+        // (consume) and acquire the other lanes' before reading them back
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         for (uint32_t j = flushed; j < done; ++j) {
             const uint32_t k = j % KD, e0 = tile_of(j) + lane * 4u;
             float w[8], m[8], v[8];
@@ -921,10 +924,20 @@ Window window_ticks(int32_t rows) {
     return w;
 }
 
+// Which kernel a launch runs, and its shape (every launch of one call runs
+// the same plan: the host's cuts keep every operand's alignment).
+enum : int { K_SCALAR = 0, K_DIRECT = 1, K_DEFERRED = 2 };
+struct Plan {
+    int kernel;   // K_*
+    int dv;       // 16-bit elements per store of the 16-bit output (4, 2 or 1)
+    int kd;       // K_DEFERRED: tiles in each wave's LDS ring
+    Window win;   // K_DEFERRED: write windows (cycle 0: none)
+};
+
 template <int GDT, int PDT, int DV>
-hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
-    const Window w = a.nrows >= kWindowMinRows ? window_ticks(a.nrows) : Window{0, 0, 0, 0};
-    const int kd = w.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
+hipError_t launch_deferred(const StepArgs& a, const Plan& p, hipStream_t s) {
+    const Window w = p.win;
+    const int kd = p.kd;
     const int bpc = w.cycle && kd <= kRingTwoPerCu ? 2 : 1;
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, bpc));   // one wave per tile at most
     switch (kd) {
@@ -938,24 +951,23 @@ hipError_t launch_deferred(const StepArgs& a, hipStream_t s) {
 }
 
 template <int GDT, int PDT, int MODE>
-hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
+hipError_t launch_mode(const StepArgs& a, const Plan& p, hipStream_t s) {
     if constexpr (MODE == (M_REDUCE | M_ADAM | M_CAST)) {
-        if (vec && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows && al(a.grads, 16) &&
-            a.row_stride % 8 == 0) {
-            switch (dv) {
-                case 4: return launch_deferred<GDT, PDT, 4>(a, s);
-                case 2: return launch_deferred<GDT, PDT, 2>(a, s);
-                default: return launch_deferred<GDT, PDT, 1>(a, s);
+        if (p.kernel == K_DEFERRED) {
+            switch (p.dv) {
+                case 4: return launch_deferred<GDT, PDT, 4>(a, p, s);
+                case 2: return launch_deferred<GDT, PDT, 2>(a, p, s);
+                default: return launch_deferred<GDT, PDT, 1>(a, p, s);
             }
         }
     }
-    if (!vec) {
+    if (p.kernel == K_SCALAR) {
         hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n, g_step_bpc)), dim3(kThreads),
                            0, s, a);
         return hipGetLastError();
     }
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc));
-    switch (dv) {
+    switch (p.dv) {
         case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
         case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
         default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
@@ -964,12 +976,12 @@ hipError_t launch_mode(const StepArgs& a, bool vec, int dv, hipStream_t s) {
 }
 
 template <int MODE>
-hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, bool vec, int dv, hipStream_t s) {
+hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, const Plan& p, hipStream_t s) {
     const bool gb = gdt == ZSMR_BF16, pb = pdt == ZSMR_BF16;
-    if (gb && pb) return launch_mode<ZSMR_BF16, ZSMR_BF16, MODE>(a, vec, dv, s);
-    if (gb) return launch_mode<ZSMR_BF16, ZSMR_FP16, MODE>(a, vec, dv, s);
-    if (pb) return launch_mode<ZSMR_FP16, ZSMR_BF16, MODE>(a, vec, dv, s);
-    return launch_mode<ZSMR_FP16, ZSMR_FP16, MODE>(a, vec, dv, s);
+    if (gb && pb) return launch_mode<ZSMR_BF16, ZSMR_BF16, MODE>(a, p, s);
+    if (gb) return launch_mode<ZSMR_BF16, ZSMR_FP16, MODE>(a, p, s);
+    if (pb) return launch_mode<ZSMR_FP16, ZSMR_BF16, MODE>(a, p, s);
+    return launch_mode<ZSMR_FP16, ZSMR_FP16, MODE>(a, p, s);
 }
 
 }  // namespace
@@ -1039,16 +1051,35 @@ int64_t line_head(int mode, const StepArgs& a) {
     return vec_ok(mode, advanced(a, h, a.n - h, 0)) ? h : 0;
 }
 
+// The kernel a launch of `mode` over a's operands runs: the one-element
+// kernel unless every operand allows the vector path; for the fused step the
+// deferred-write kernel when it is on, the step has at least
+// g_defer_min_rows rows and its rows are 16-byte aligned (one 16-byte load
+// per row per lane), else the direct kernel.
+Plan plan_for(int mode, const StepArgs& a) {
+    Plan p{K_DIRECT, (mode & M_CAST) ? dst_vec(a.p16) : 4, 0, Window{0, 0, 0, 0}};
+    if (!vec_ok(mode, a)) {
+        p.kernel = K_SCALAR;
+        return p;
+    }
+    if (mode == (M_REDUCE | M_ADAM | M_CAST) && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows &&
+        al(a.grads, 16) && a.row_stride % 8 == 0) {
+        p.kernel = K_DEFERRED;
+        p.win = a.nrows >= kWindowMinRows ? window_ticks(a.nrows) : Window{0, 0, 0, 0};
+        p.kd = p.win.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
+    }
+    return p;
+}
+
 hipError_t launch_step_one(int mode, int gdt, int pdt, const StepArgs& a, hipStream_t s) {
-    const bool vec = vec_ok(mode, a);
-    if (!vec && a.head) return hipErrorInvalidValue;   // the host gives a head to vector launches only
-    const int dv = (mode & M_CAST) ? dst_vec(a.p16) : 4;   // (no 16-bit output: unused)
+    const Plan p = plan_for(mode, a);
+    if (p.kernel == K_SCALAR && a.head) return hipErrorInvalidValue;   // the host gives a head to vector launches only
     switch (mode) {
-        case M_REDUCE | M_ADAM | M_CAST: return launch_dt<M_REDUCE | M_ADAM | M_CAST>(gdt, pdt, a, vec, dv, s);
-        case M_REDUCE | M_GOUT: return launch_dt<M_REDUCE | M_GOUT>(gdt, ZSMR_BF16, a, vec, dv, s);
-        case M_ADAM: return launch_mode<ZSMR_BF16, ZSMR_BF16, M_ADAM>(a, vec, dv, s);
-        case M_CAST: return launch_dt<M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
-        case M_INIT | M_CAST: return launch_dt<M_INIT | M_CAST>(ZSMR_BF16, pdt, a, vec, dv, s);
+        case M_REDUCE | M_ADAM | M_CAST: return launch_dt<M_REDUCE | M_ADAM | M_CAST>(gdt, pdt, a, p, s);
+        case M_REDUCE | M_GOUT: return launch_dt<M_REDUCE | M_GOUT>(gdt, ZSMR_BF16, a, p, s);
+        case M_ADAM: return launch_mode<ZSMR_BF16, ZSMR_BF16, M_ADAM>(a, p, s);
+        case M_CAST: return launch_dt<M_CAST>(ZSMR_BF16, pdt, a, p, s);
+        case M_INIT | M_CAST: return launch_dt<M_INIT | M_CAST>(ZSMR_BF16, pdt, a, p, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1066,6 +1097,19 @@ hipError_t launch_step(int mode, int gdt, int pdt, const StepArgs& a0, hipStream
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+void describe_step(int mode, const StepArgs& a0, StepPlan* out) {
+    constexpr int64_t kMaxLaunch = int64_t(1) << 30;
+    const int64_t h = line_head(mode, a0);
+    const int64_t n = a0.n - h < kMaxLaunch ? a0.n - h : kMaxLaunch;
+    const Plan p = plan_for(mode, advanced(a0, h, n, (int32_t)h));
+    out->kernel = p.kernel;
+    out->ring_tiles = p.kernel == K_DEFERRED ? p.kd : 0;
+    out->windowed = p.win.cycle != 0;
+    out->store_elems = p.dv;
+    out->launches = a0.n > h ? (int32_t)((a0.n - h + kMaxLaunch - 1) / kMaxLaunch) : 0;
+    out->head = h;
 }
 
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t s) {

@@ -44,6 +44,13 @@ struct StepArgs {
 
 hipError_t launch_step(int mode, int grad_dtype, int param_dtype, const StepArgs& a,
                        hipStream_t stream);
+// what launch_step(mode, ..., a) would launch (no launch; the write windows
+// need the current device's clock rate)
+struct StepPlan {
+    int32_t kernel, ring_tiles, windowed, store_elems, launches;
+    int64_t head;
+};
+void describe_step(int mode, const StepArgs& a, StepPlan* out);
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t stream);
 // dst[k*stride + j] = src[k*stride + j], j < n, k < count (count <= 65535)
 hipError_t launch_copy_blocks(const uint16_t* src, uint16_t* dst, int64_t n, int32_t count,
