@@ -376,6 +376,7 @@ typedef struct zsmr_plan {
     int32_t windowed;     /* deferred: stores wait for chip-wide write windows            */
     int32_t store_elems;  /* 16-bit elements per store of the working copy (4, 2, 1)      */
     int32_t launches;     /* launches the piece is cut into (2^30 elements each at most)  */
+    int32_t row_batch;    /* direct: gradient rows loaded per batch (8 or 12)              */
     int64_t head;         /* leading elements run one by one to reach a 128-byte line      */
 } zsmr_plan;
 int32_t zsmr_fused_step_plan(const zsmr_ctx* ctx, int32_t rank, int32_t unit, const void* grads,

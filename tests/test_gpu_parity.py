@@ -551,6 +551,37 @@ def test_deferred_sampled_against_oracle(rows, kd, p16_shift):
             f"p16_shift={p16_shift}")
 
 
+@pytest.mark.parametrize("rows", [8, 9, 12, 13, 14, 16, 17, 20, 23])
+def test_direct_kernel_row_batches_against_oracle(rows):
+    """The direct kernel loads 12 gradient rows per batch at 9-13 and 16-23
+    rows and 8 otherwise (the library's plan says which): every element
+    against the oracle, two steps, a ragged tail."""
+    n, T, lr = 512 * 40 + 77, 2, 1e-3
+    z.zsmr_set_launch_shape(0, 0, 0, 24)            # no deferred kernel: the direct one at any rows
+    try:
+        ctx = z.zero_init_shards(n * rows, rows, 2, "bf16")
+        stride = (n + 63) // 64 * 64
+        steps_rows = {t: _piece_inputs(n, rows, "bf16", step=t, seed=4)[0] for t in range(1, T + 1)}
+        theta = synth.theta0(4, np.arange(n))
+        mb = torch.from_numpy(theta.copy()).cuda()
+        mm, vb = torch.empty_like(mb), torch.empty_like(mb)
+        pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        z.zero_init_state(ctx, 0, 0, mb.clone(), mb, mm, vb, pb)
+        want_rb = 12 if 9 <= rows <= 13 or 16 <= rows <= 23 else 8
+        for t in range(1, T + 1):
+            G = _padded_rows(steps_rows[t], stride)
+            plan = _expect_kernel(ctx, G, stride, mb, mm, vb, pb, "direct")
+            assert plan["row_batch"] == want_rb, plan
+            z.zero_fused_step(ctx, 0, 0, G, stride, 0, mb, mm, vb, pb, t, lr)
+        torch.cuda.synchronize()
+    finally:
+        z.zsmr_set_launch_shape()
+    theta = synth.theta0(4, np.arange(n))
+    master, m, v, p16 = _oracle_piece(None, theta, "bf16", "bf16", T, lr, steps_rows)
+    compare({"master": host32(mb), "m": host32(mm), "v": host32(vb)},
+            {"master": master, "m": m, "v": v}, host16(pb), p16, f"direct rows={rows}")
+
+
 @pytest.mark.parametrize("world", [16, 12, 64])     # the mean multiplies by 1/N for 16 and 64
 @pytest.mark.parametrize("gdt", ["bf16", "fp16"])
 def test_reduce_sum_and_mean(gdt, world):

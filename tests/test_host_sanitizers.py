@@ -102,6 +102,7 @@ void describe_step(int mode, const StepArgs& a, StepPlan* out) {
     out->windowed = 1;
     out->store_elems = 4;
     out->launches = 1;
+    out->row_batch = 12;
     out->head = 5;
 }
 }  // namespace zsmr
@@ -408,6 +409,7 @@ static void launches() {
                                at<float>(V), at<void>(P), &pl) == ZSMR_OK);
     CHECK(pl.kernel == (zsmr::M_REDUCE | zsmr::M_ADAM | zsmr::M_CAST) && pl.ring_tiles == 3);
     CHECK(pl.windowed == 1 && pl.store_elems == 4 && pl.launches == 1 && pl.head == 5);
+    CHECK(pl.row_batch == 12);
     CHECK(zsmr::g_described.grads == at<const uint16_t>(G) + 4 && zsmr::g_described.n == 2);
     CHECK(zsmr::g_described.nrows == 4 && zsmr::g_described.p16 == at<uint16_t>(P));
     CHECK(zsmr_fused_step_plan(c, 2, 1, at<void>(G + 1), 8, 4, at<float>(M), at<float>(MM),

@@ -54,7 +54,7 @@ class zsmr_bytes(ctypes.Structure):
 
 class zsmr_plan(ctypes.Structure):
     _fields_ = [("kernel", _i32), ("ring_tiles", _i32), ("windowed", _i32), ("store_elems", _i32),
-                ("launches", _i32), ("head", _i64)]
+                ("launches", _i32), ("row_batch", _i32), ("head", _i64)]
 
 
 ZSMR_KERNEL_SCALAR, ZSMR_KERNEL_DIRECT, ZSMR_KERNEL_DEFERRED = 0, 1, 2
@@ -370,7 +370,7 @@ def zsmr_fused_step_plan(ctx: Ctx, rank: int, unit: int, grads, row_stride: int,
                          master, m, v, p16_dst) -> dict:
     """Which kernel ``zero_fused_step`` with these arguments runs (nothing is
     launched): kernel ("scalar", "direct" or "deferred"), ring_tiles,
-    windowed, store_elems, launches, head."""
+    windowed, store_elems, launches, row_batch, head."""
     out = zsmr_plan()
     _check(_lib().zsmr_fused_step_plan(ctx.handle, rank, unit, _ptr(grads), int(row_stride),
                                        int(base_elem), _ptr(master), _ptr(m), _ptr(v),

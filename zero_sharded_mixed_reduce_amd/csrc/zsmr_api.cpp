@@ -629,6 +629,7 @@ int32_t zsmr_fused_step_plan(const zsmr_ctx* c, int32_t rank, int32_t unit, cons
     out->windowed = p.windowed;
     out->store_elems = p.store_elems;
     out->launches = p.launches;
+    out->row_batch = p.row_batch;
     out->head = p.head;
     return ZSMR_OK;
 }

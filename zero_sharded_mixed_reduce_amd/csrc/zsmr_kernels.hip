@@ -36,10 +36,10 @@
 // Gradient rows per double-buffered load batch.  Measured on MI355X,
 // alternating processes on one box: the deferred-write kernel on share64
 // (tuned windows) 2.694-2.730 ms with 4 against 2.742-2.769 with 8 (154
-// against 184 VGPRs); the direct kernel with 12 instead of 8: 97M-element
-// pieces at 8 and 16 rows +3%, but GPT-2 small's 15.5M-element shard -3%.
+// against 184 VGPRs).  The direct kernel takes 8 or 12 by row count (the
+// measurements are beside direct_row_batch below).
 #ifndef ZSMR_ROW_BATCH
-#define ZSMR_ROW_BATCH 8        // direct kernel
+#define ZSMR_ROW_BATCH 8        // direct kernel's default batch
 #endif
 #ifndef ZSMR_DEFER_BATCH
 #define ZSMR_DEFER_BATCH 4      // deferred-write kernel
@@ -60,6 +60,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRowBatch = ZSMR_ROW_BATCH;
+constexpr int kRowBatchWide = 12;
 constexpr int kDeferBatch = ZSMR_DEFER_BATCH;
 constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // Grids.  0 = one unit of work per thread (a wave tile per wave for the step
@@ -264,21 +265,22 @@ struct Groups {
     }
 };
 
+template <int RB>
 __device__ __forceinline__ void load_rows(const StepArgs& a, int r, uint32_t e0, uint32_t e1, u32x4* buf) {
     // rows past the last one are clamped to it: every load is issued
     // unconditionally (so the compiler can count them) and the re-read row
     // comes from cache; add_rows() skips it
 #pragma unroll
-    for (int k = 0; k < kRowBatch; ++k) {
+    for (int k = 0; k < RB; ++k) {
         const int rr = r + k < a.nrows ? r + k : a.nrows - 1;
         buf[k] = Groups::load16raw(a.grads + (int64_t)rr * a.row_stride, e0, e1);
     }
 }
 
-template <int GDT>
+template <int GDT, int RB>
 __device__ __forceinline__ void add_rows(const StepArgs& a, int r, const u32x4* buf, float* g) {
 #pragma unroll
-    for (int k = 0; k < kRowBatch; ++k) {
+    for (int k = 0; k < RB; ++k) {
         if (r + k < a.nrows) {
             float t[8];
             unpack8<GDT>(buf[k], t);
@@ -288,8 +290,9 @@ __device__ __forceinline__ void add_rows(const StepArgs& a, int r, const u32x4* 
     }
 }
 
-// One lane's 8 elements (groups at e0 and e1) of the launch's MODE.
-template <int GDT, int PDT, int MODE, int DV>
+// One lane's 8 elements (groups at e0 and e1) of the launch's MODE; RB
+// gradient rows per load batch.
+template <int GDT, int PDT, int MODE, int DV, int RB>
 __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e1) {
     typedef Groups G;
     float g[8];
@@ -298,26 +301,26 @@ __device__ __forceinline__ void body8(const StepArgs& a, uint32_t e0, uint32_t e
         // rows 1..N-1 in batches, double-buffered so that one batch is in
         // flight while the previous one is added; the sum itself runs
         // strictly in rank order 0, 1, ..., N-1
-        u32x4 bufA[kRowBatch], bufB[kRowBatch];
+        u32x4 bufA[RB], bufB[RB];
         const u32x4 row0 = G::load16raw(a.grads, e0, e1);
         int r = 1;
-        if (a.nrows > 1) load_rows(a, r, e0, e1, bufA);
+        if (a.nrows > 1) load_rows<RB>(a, r, e0, e1, bufA);
         unpack8<GDT>(row0, g);
         while (r < a.nrows) {
-            if (r + kRowBatch >= a.nrows) {
-                add_rows<GDT>(a, r, bufA, g);
+            if (r + RB >= a.nrows) {
+                add_rows<GDT, RB>(a, r, bufA, g);
                 break;
             }
-            load_rows(a, r + kRowBatch, e0, e1, bufB);
-            add_rows<GDT>(a, r, bufA, g);
-            r += kRowBatch;
-            if (r + kRowBatch >= a.nrows) {
-                add_rows<GDT>(a, r, bufB, g);
+            load_rows<RB>(a, r + RB, e0, e1, bufB);
+            add_rows<GDT, RB>(a, r, bufA, g);
+            r += RB;
+            if (r + RB >= a.nrows) {
+                add_rows<GDT, RB>(a, r, bufB, g);
                 break;
             }
-            load_rows(a, r + kRowBatch, e0, e1, bufA);
-            add_rows<GDT>(a, r, bufB, g);
-            r += kRowBatch;
+            load_rows<RB>(a, r + RB, e0, e1, bufA);
+            add_rows<GDT, RB>(a, r, bufB, g);
+            r += RB;
         }
         if (a.mean) {
 #pragma unroll
@@ -403,7 +406,7 @@ __device__ __forceinline__ void edges1(const StepArgs& a) {
 
 // Aligned path over vector index i (8 elements each, grid-stride); the
 // elements outside whole tiles go one per lane to workgroup 0.
-template <int GDT, int PDT, int MODE, int DV>
+template <int GDT, int PDT, int MODE, int DV, int RB>
 __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
     // a launch covers fewer than 2^31 elements (the host splits larger
     // pieces), so in-launch offsets are 32-bit
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void step_vec8_kernel(StepArgs a) {
     const uint32_t stride = gridDim.x * kThreads;
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
         const uint32_t e0 = (i >> 6) * 512u + (i & 63u) * 4u;   // wave tile, lane group
-        body8<GDT, PDT, MODE, DV>(a, e0, e0 + 256u);
+        body8<GDT, PDT, MODE, DV, RB>(a, e0, e0 + 256u);
     }
     edges1<GDT, PDT, MODE>(a);
 }
@@ -932,6 +935,7 @@ struct Plan {
     int dv;       // 16-bit elements per store of the 16-bit output (4, 2 or 1)
     int kd;       // K_DEFERRED: tiles in each wave's LDS ring
     Window win;   // K_DEFERRED: write windows (cycle 0: none)
+    int rb;       // K_DIRECT, launches that reduce: gradient rows per load batch
 };
 
 template <int GDT, int PDT, int DV>
@@ -967,10 +971,20 @@ hipError_t launch_mode(const StepArgs& a, const Plan& p, hipStream_t s) {
         return hipGetLastError();
     }
     const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc));
+    if constexpr ((MODE & M_REDUCE) != 0) {
+        if (p.rb == kRowBatchWide) {
+            switch (p.dv) {
+                case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4, kRowBatchWide>), grid, dim3(kThreads), 0, s, a); break;
+                case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2, kRowBatchWide>), grid, dim3(kThreads), 0, s, a); break;
+                default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1, kRowBatchWide>), grid, dim3(kThreads), 0, s, a); break;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (p.dv) {
-        case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 4, kRowBatch>), grid, dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 2, kRowBatch>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_vec8_kernel<GDT, PDT, MODE, 1, kRowBatch>), grid, dim3(kThreads), 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -1056,8 +1070,21 @@ int64_t line_head(int mode, const StepArgs& a) {
 // deferred-write kernel when it is on, the step has at least
 // g_defer_min_rows rows and its rows are 16-byte aligned (one 16-byte load
 // per row per lane), else the direct kernel.
+// Gradient rows per load batch of the direct kernel for a step of `rows`
+// rows: 12 where one batch of 12 holds rows 1..N-1 (9-13 rows) or the
+// batches stay mostly full (16-23 rows), else 8.  Measured on MI355X, one
+// launch of 60M elements, ms with 12 / 8 rows per batch: 9 rows 0.434 /
+// 0.458, 10 0.446 / 0.465, 11 0.466 / 0.480, 12 0.490 / 0.499, 14 0.567 /
+// 0.548, 16 (97M elements) 0.953 / 0.980, 18 0.624 / 0.624, 20 0.668 /
+// 0.679; the 1.558e9-element 16-rank world 15.37 / 15.92 ms per step; 8 rows
+// (GPT-2 small, Llama-3-8B shape) within 1% either way, 8 kept.
+int direct_row_batch(int rows) {
+    return (rows >= 9 && rows <= 13) || (rows >= 16 && rows <= 23) ? kRowBatchWide : kRowBatch;
+}
+
 Plan plan_for(int mode, const StepArgs& a) {
-    Plan p{K_DIRECT, (mode & M_CAST) ? dst_vec(a.p16) : 4, 0, Window{0, 0, 0, 0}};
+    Plan p{K_DIRECT, (mode & M_CAST) ? dst_vec(a.p16) : 4, 0, Window{0, 0, 0, 0},
+           (mode & M_REDUCE) ? direct_row_batch(a.nrows) : kRowBatch};
     if (!vec_ok(mode, a)) {
         p.kernel = K_SCALAR;
         return p;
@@ -1110,6 +1137,7 @@ void describe_step(int mode, const StepArgs& a0, StepPlan* out) {
     out->store_elems = p.dv;
     out->launches = a0.n > h ? (int32_t)((a0.n - h + kMaxLaunch - 1) / kMaxLaunch) : 0;
     out->head = h;
+    out->row_batch = p.kernel == K_DIRECT && (mode & M_REDUCE) ? p.rb : 0;
 }
 
 hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStream_t s) {

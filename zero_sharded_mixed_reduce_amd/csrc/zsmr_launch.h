@@ -47,7 +47,7 @@ hipError_t launch_step(int mode, int grad_dtype, int param_dtype, const StepArgs
 // what launch_step(mode, ..., a) would launch (no launch; the write windows
 // need the current device's clock rate)
 struct StepPlan {
-    int32_t kernel, ring_tiles, windowed, store_elems, launches;
+    int32_t kernel, ring_tiles, windowed, store_elems, launches, row_batch;
     int64_t head;
 };
 void describe_step(int mode, const StepArgs& a, StepPlan* out);
