@@ -43,3 +43,14 @@ def test_bench_prints_one_complete_json_line():
     shapes = d["phased_bound"]
     assert "bursts_balanced" in shapes["read_shapes_GBps"]
     assert "bursts_plain_balanced" in shapes["write_shapes_GBps"]
+    # the same step at the library's untuned defaults, beside the tuned one
+    untuned = d["parts"]["step_at_library_defaults"]
+    assert untuned["ms"] > 0 and 0 < untuned["frac"] < 1
+    # every other workload, timed in the same run
+    oc = d["other_configs"]
+    assert set(oc) == {"psi65k_zero2", "gpt2s_zero2", "gpt2xl_zero1", "llama8b_zero3_split",
+                       "llama8b_zero3_owner"}
+    for name, v in oc.items():
+        assert v["ms_per_step"] > 0 and v["params_per_s"] > 0, name
+        assert 0 < v["frac_of_8TBps"] < 1 and 0 < v["frac_of_phased_bound"] < 1.2, name
+        assert abs(v["GBps"] - v["algorithmic_bytes_per_step"] / v["ms_per_step"] / 1e6) < 1, name
