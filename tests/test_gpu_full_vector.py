@@ -1,18 +1,25 @@
 """Whole-vector parity against the oracle: every element of master, m, v and
 the 16-bit working copy, compared after every step.
 
-* The GPT-2-small workload (124,439,808 parameters, 8 ranks, ZeRO-2, bf16,
-  10 steps), as "ZeRO and FSDP"'s zero_check.py compares every parameter of
-  the sharded run with the unsharded one.
+* Every workload at its full size, as "ZeRO and FSDP"'s zero_check.py
+  compares every parameter of the sharded run with the unsharded one:
+  GPT-2 small (124,439,808 parameters, 8 ranks, ZeRO-2, 10 steps) and GPT-2
+  1.5B (1,558,000,000, 16 ranks, ZeRO-1, outliers, 3 steps) after every
+  step; one rank's share of the 7.5e9 / 64-rank world (117,187,500 owned
+  elements, 64 rows; ranks 0 and 63) after every step; the Llama-3-8B
+  shape (8,030,261,248 parameters in 33 units, ZeRO-3) after its 2 steps,
+  unit by unit.
 * The bucketed share step (gradients arriving bucket by bucket during a
   simulated backward, each bucket updated and received as it lands; 1, 3 and
   16 buckets, and sub-ranges cut at ragged, unaligned places) on a
   2,000,003-element share of a 64-rank world.
 * The ZeRO-3 split layout with the next unit prefetched on a second stream.
 
-The oracle's initial parameters come from the generator's CPU definition.
-Its gradients are the device fill's, read back after each step: at these
-sizes the CPU generator would take minutes per step.  The device fill is the
+The oracle's initial parameters come from the generator's CPU definition
+(at 10^9 elements and more from the device fill, checked against the CPU
+definition on a sample).  Its gradients are the device fill's, read back
+after each step: at these sizes the CPU generator would take minutes per
+step.  The largest vectors are read back and checked range by range.  The device fill is the
 generator itself (``tests/test_gpu_synth.py`` pins it to the CPU definition
 bit for bit), and each step's read-back is checked against the CPU
 definition again on a random sample of every row.  The oracle runs on
@@ -86,6 +93,20 @@ class OracleState:
         with cf.ThreadPoolExecutor(THREADS) as ex:
             list(ex.map(run, _chunks(self.master.size)))
 
+    def step_range(self, t, lo, rows16):
+        """One step on parameters [lo, lo + rows16.shape[1]) only."""
+        k = nm.adam_consts(self.lr, self.betas[0], self.betas[1], self.eps, t)
+        n = rows16.shape[1]
+
+        def run(span):
+            a, b = span
+            g = nm.reduce_rank_order([nm.widen16(r[a:b], self.dtype) for r in rows16])
+            sl = slice(lo + a, lo + b)
+            self.master[sl], self.m[sl], self.v[sl] = nm.adam_update(
+                self.master[sl], self.m[sl], self.v[sl], g, k)
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            list(ex.map(run, _chunks(n)))
+
     def cast(self):
         out = np.empty(self.master.size, np.uint16)
 
@@ -112,6 +133,53 @@ def check_generator_sample(rows16, seed, step, p0, sigma, dtype, outlier=0, rng_
     for r in range(rows16.shape[0]):
         want = synth.grad16(seed, r, step, p0 + k, sigma, dtype, outlier)
         assert np.array_equal(rows16[r, k], want), f"device fill differs from the generator: row {r}"
+
+
+def rows_range(grads: torch.Tensor, rows: int, stride: int, lo: int, hi: int) -> np.ndarray:
+    """rows x (hi - lo) 16-bit patterns, columns [lo, hi) of a device buffer
+    of rows x stride."""
+    v = grads.view(torch.int16)[:rows * stride].view(rows, stride)[:, lo:hi]
+    return v.contiguous().cpu().numpy().view(np.uint16)
+
+
+def theta_device_checked(n, p0, seed, sigma=0.02):
+    """theta0 of parameters [p0, p0 + n) from the device fill, checked against
+    the generator's CPU definition on a sample."""
+    import synth.gpu as sgpu
+    th = torch.empty(n, dtype=torch.float32, device="cuda")
+    sgpu.fill32(th, n, p0, n, seed, synth.TAG_THETA, 0, 0, sigma)
+    host = th.cpu().numpy()
+    del th
+    rng = np.random.default_rng(p0 % 1000)
+    k = np.unique(np.concatenate([rng.integers(0, n, SAMPLE), [0, n - 1]]))
+    assert np.array_equal(host[k].view(np.uint32), synth.theta0(seed, p0 + k, sigma).view(np.uint32))
+    return host
+
+
+class RangeCounts:
+    """Differing-element counts accumulated over ranges of a vector, with the
+    acceptance bar checked on every range."""
+
+    def __init__(self, what):
+        self.what = what
+        self.counts = {"master": 0, "m": 0, "v": 0, "p16": 0}
+        self.n = 0
+
+    def add(self, got, want, got16, want16):
+        diff = {k: np.flatnonzero(got[k].view(np.uint32) != want[k].view(np.uint32)) for k in want}
+        d16 = np.flatnonzero(got16 != want16)
+        idx = np.unique(np.concatenate([*diff.values(), d16, [0]]))
+        compare({k: got[k][idx] for k in want}, {k: want[k][idx] for k in want}, got16[idx],
+                want16[idx], self.what + " (differing elements of a range)")
+        for k, v in diff.items():
+            self.counts[k] += int(v.size)
+        self.counts["p16"] += int(d16.size)
+        self.n += got16.size
+
+    def report(self):
+        say(f"[full vector] {self.what}: {self.n} elements, differing " +
+            ", ".join(f"{k}={v}" for k, v in self.counts.items()))
+        return self.counts
 
 
 def compare_all(got, want, got16, want16, what):
@@ -288,4 +356,130 @@ def test_stage3_split_layout_against_oracle(prefetch):
     c = z.zero_counters(s3.ctx, 0)
     assert c["stage3_gathers"] == 2 * lay.n_units * w.steps == c["stage3_releases"]
     del s3, g, oracle
+    free()
+
+
+# ------------------------------------------------------------ GPT-2 1.5B ---
+RANGE = 1 << 27                 # parameters read back and checked at once
+
+
+@pytest.mark.timeout(1800)
+def test_gpt2xl_every_element_every_step():
+    """GPT-2 1.5B: 1,558,000,000 parameters, 16 ranks, ZeRO-1, bf16 with one
+    entry in a hundred scaled by 100, 3 steps: every element after every
+    step, range by range."""
+    w = wl.WORKLOADS["gpt2xl"]
+    say(f"[full vector] gpt2xl: numel={w.numel} world={w.world} T={w.steps}")
+    world = wl.ShardedWorld(w)
+    n, P = w.numel, world.P
+    assert P == n
+    oracle = OracleState(theta_device_checked(n, 0, w.seed, w.theta_sigma), w.dtype, w.lr, w.betas,
+                         w.eps)
+    total = 0
+    for t in range(1, w.steps + 1):
+        world.gen_grads(t)
+        for lo in range(0, n, RANGE):
+            hi = min(n, lo + RANGE)
+            rows16 = rows_range(world.grads, w.world, P, lo, hi)
+            if lo == 0:
+                check_generator_sample(rows16, w.seed, t, 0, w.grad_sigma, w.dtype,
+                                       w.outlier_permyriad)
+            oracle.step_range(t, lo, rows16)
+            del rows16
+        world.step(t)
+        torch.cuda.synchronize()
+        rc = RangeCounts(f"gpt2xl step {t}")
+        for lo in range(0, n, RANGE):
+            hi = min(n, lo + RANGE)
+            got = {"master": world.master[lo:hi].cpu().numpy(), "m": world.m[lo:hi].cpu().numpy(),
+                   "v": world.v[lo:hi].cpu().numpy()}
+            want = {"master": oracle.master[lo:hi], "m": oracle.m[lo:hi], "v": oracle.v[lo:hi]}
+            rc.add(got, want, host16(world.wc[lo:hi]), nm.cast16(oracle.master[lo:hi], w.dtype))
+        total += sum(rc.report().values())
+    say(f"[full vector] gpt2xl: differing elements over all steps: {total}")
+    del world, oracle
+    free()
+
+
+# ------------------------------------------ one rank's share, 64 ranks ---
+@pytest.mark.timeout(1800)
+@pytest.mark.parametrize("rank", [0, 63])
+def test_share64_every_owned_element_every_step(rank):
+    """One rank of the 7.5e9-parameter, 64-rank world: every one of its
+    117,187,500 owned elements after each of the 3 steps (64 bf16
+    contributions each); the 63 peer slots equal the staged values."""
+    w = wl.WORKLOADS["share64"]
+    say(f"[full vector] share64 rank={rank}")
+    share = wl.RankShare(w, rank=rank)
+    S, off = share.S, share.off
+    oracle = OracleState(theta_host(w.seed, off, S), w.dtype, w.lr, w.betas, w.eps)
+    total = 0
+    for t in range(1, w.steps + 1):
+        share.gen_grads(t)
+        for lo in range(0, S, RANGE // 4):
+            hi = min(S, lo + RANGE // 4)
+            rows16 = rows_range(share.grads, w.world, share.row_stride, lo, hi)
+            if lo == 0:
+                check_generator_sample(rows16, w.seed, t, off, w.grad_sigma, w.dtype)
+            oracle.step_range(t, lo, rows16)
+            del rows16
+        share.step(t)
+        torch.cuda.synchronize()
+        rc = RangeCounts(f"share64 rank {rank} step {t}")
+        got = {"master": share.master.cpu().numpy(), "m": share.m.cpu().numpy(), "v": share.v.cpu().numpy()}
+        rc.add(got, {"master": oracle.master, "m": oracle.m, "v": oracle.v},
+               host16(share.wc[off:off + S]), oracle.cast())
+        total += sum(rc.report().values())
+    for lo, hi in ((0, off), (off + S, share.P)):
+        for c in range(lo, hi, 1 << 28):
+            e = min(hi, c + (1 << 28))
+            assert torch.equal(share.wc[c:e].view(torch.int16), share.staged[c:e].view(torch.int16))
+    say(f"[full vector] share64 rank {rank}: differing elements over all steps: {total}")
+    del share, oracle
+    free()
+
+
+# --------------------------------------------------- Llama-3-8B shape ---
+@pytest.mark.timeout(1800)
+@pytest.mark.parametrize("part", [0, 1, 2])
+def test_llama8b_every_element_after_the_run(part):
+    """The Llama-3-8B shape (33 units, 8 ranks, ZeRO-3 per-unit split, 2
+    steps): after the run, every element of the units u with u % 3 == part
+    against the oracle, unit by unit (each unit's trajectory depends on its
+    own inputs alone; the three parts together cover all 33 units)."""
+    import synth.gpu as sgpu
+    w = wl.WORKLOADS["llama8b"]
+    say(f"[full vector] llama8b: units={len(w.units)} numel={w.numel} part={part}")
+    s3 = wl.Stage3World(w, check_gathers=True)
+    s3.run(w.steps)
+    torch.cuda.synchronize()
+    assert s3.gather_mismatch == 0
+    rc = RangeCounts(f"llama8b after 2 steps, units {part}, {part + 3}, ...")
+    for u in range(part, s3.U, 3):
+        p0, size, width, q0 = s3.P_start[u], s3.P_size[u], s3.width[u], s3.Q_u[u]
+        assert width == size                        # every unit divides by 8: no pad
+        oracle = OracleState(theta_device_checked(size, p0, w.seed, w.theta_sigma), w.dtype, w.lr,
+                             w.betas, w.eps)
+        for t in range(1, w.steps + 1):
+            # the unit's gradients of step t, drawn again exactly as the run drew them
+            sgpu.fill16(s3.grads, w.world, width, width, p0, size, w.seed, synth.TAG_GRAD, 0, t,
+                        w.grad_sigma, w.dtype, w.outlier_permyriad)
+            torch.cuda.synchronize()
+            for lo in range(0, size, RANGE):
+                hi = min(size, lo + RANGE)
+                rows16 = rows_range(s3.grads, w.world, width, lo, hi)
+                if lo == 0 and u in (0, 1, 2, s3.U - 1):
+                    check_generator_sample(rows16, w.seed, t, p0, w.grad_sigma, w.dtype)
+                oracle.step_range(t, lo, rows16)
+                del rows16
+        for lo in range(0, size, RANGE):
+            hi = min(size, lo + RANGE)
+            a, b = q0 + lo, q0 + hi
+            got = {"master": s3.master[a:b].cpu().numpy(), "m": s3.m[a:b].cpu().numpy(),
+                   "v": s3.v[a:b].cpu().numpy()}
+            want = {"master": oracle.master[lo:hi], "m": oracle.m[lo:hi], "v": oracle.v[lo:hi]}
+            rc.add(got, want, host16(s3.p16[a:b]), nm.cast16(oracle.master[lo:hi], w.dtype))
+        del oracle
+    rc.report()
+    del s3
     free()
