@@ -396,6 +396,17 @@ def test_owner_map_errors():
     assert [z.zero_unit_owner(ctx, u) for u in range(4)] == [3, 2, 1, 0]
 
 
+def test_integer_arrays_that_do_not_fit_their_c_type_are_refused():
+    """Unit sizes (int64) and owners (int32) are checked before the call:
+    ctypes would store 2**32 + 1 in an int32 array as 1, a valid owner."""
+    ctx, _ = _owner_case(64, 4, [16] * 4)
+    with pytest.raises(ValueError, match="owners"):
+        z.zero_set_unit_owners(ctx, [0, 1, 2, (1 << 32) + 1])
+    assert [z.zero_unit_owner(ctx, u) for u in range(4)] == [0, 1, 2, 3]   # unchanged
+    with pytest.raises(ValueError, match="units"):
+        z.zero_init_shards(64, 4, 3, "bf16", units=[(1 << 64) + 32, 32])
+
+
 def test_stage3_gather_refuses_a_short_pointer_list():
     """The library reads N shard pointers at stage 3: the binding refuses a
     shorter list before any call."""

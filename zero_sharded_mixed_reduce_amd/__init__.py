@@ -129,6 +129,17 @@ class CheckedFunction:
         return self.fn(*args)
 
 
+def int_array(ctype, values, what: str):
+    """A ctypes array of integers, each checked to fit ``ctype`` (ctypes would
+    truncate silently: 2**32 + 1 stored in an int32_t array arrives as 1)."""
+    lo, hi = _INT_RANGE[ctype]
+    vals = [int(x) for x in values]
+    for i, x in enumerate(vals):
+        if not lo <= x <= hi:
+            raise ValueError(f"{what}[{i}] = {x} is outside [{lo}, {hi}]")
+    return (ctype * max(len(vals), 1))(*vals)
+
+
 def checked_library(path: str, signatures: dict):
     """Load a shared library and give it the (restype, argtypes) of each
     named function; returns a namespace of CheckedFunction."""
@@ -255,7 +266,7 @@ def zero_init_shards(numel: int, world: int, stage: int, grad_dtype: str = "bf16
     arr = None
     n_units = 0
     if units:
-        arr = (_i64 * len(units))(*[int(u) for u in units])
+        arr = int_array(_i64, units, "units")
         n_units = len(units)
     code = _lib().zero_init_shards(ctypes.byref(h), int(numel), int(world), int(stage),
                                    DTYPES[grad_dtype], DTYPES[param_dtype or grad_dtype],
@@ -302,7 +313,7 @@ def zero_unit_owner(ctx: Ctx, unit: int) -> int:
 
 
 def zero_set_unit_owners(ctx: Ctx, owners: Sequence[int]) -> None:
-    arr = (_i32 * max(len(owners), 1))(*[int(o) for o in owners])
+    arr = int_array(_i32, owners, "owners")
     _check(_lib().zero_set_unit_owners(ctx.handle, arr, len(owners)), "zero_set_unit_owners")
 
 
