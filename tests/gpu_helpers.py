@@ -1,20 +1,14 @@
 """Shared helpers of the GPU tests (not collected by pytest)."""
 from __future__ import annotations
 
-import sys
-
 import numpy as np
 import torch
 
 import zero_sharded_mixed_reduce_amd as z
+from tests.progress import say  # noqa: F401  (the GPU tests import it from here)
 
 REL_TOL = 1e-5      # fp32 master/m/v: max relative error against the oracle
 ULP_TOL = 1         # 16-bit working copy: max distance in units in the last place
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
 
 
 def dev16(bits: np.ndarray) -> torch.Tensor:

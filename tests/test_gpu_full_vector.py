@@ -386,6 +386,7 @@ def test_gpt2xl_every_element_every_step():
                                        w.outlier_permyriad)
             oracle.step_range(t, lo, rows16)
             del rows16
+        say(f"[full vector] gpt2xl step {t}: oracle stepped")
         world.step(t)
         torch.cuda.synchronize()
         rc = RangeCounts(f"gpt2xl step {t}")
@@ -423,6 +424,7 @@ def test_share64_every_owned_element_every_step(rank):
                 check_generator_sample(rows16, w.seed, t, off, w.grad_sigma, w.dtype)
             oracle.step_range(t, lo, rows16)
             del rows16
+        say(f"[full vector] share64 rank {rank} step {t}: oracle stepped")
         share.step(t)
         torch.cuda.synchronize()
         rc = RangeCounts(f"share64 rank {rank} step {t}")
