@@ -585,3 +585,42 @@ def test_size_limits_of_a_context():
     with pytest.raises(z.ZsmrError) as e:
         z.zero_bytes_per_rank(ctx, gather_bytes=9)
     assert e.value.code == z.ZSMR_ERR_ARG
+
+
+def test_peak_over_every_window_length_matches_oracle():
+    """The gathered peak with max_live units live at once, for every
+    max_live from 1 to past the unit count, split (stage 3) and owner
+    (stage 4) layouts on random units and owner maps: the library equals the
+    oracle's window-by-window sums."""
+    rnd = random.Random(17)
+    for _ in range(60):
+        world = rnd.randint(1, 9)
+        units = [world * rnd.randint(1, 10 ** rnd.randint(1, 4)) for _ in range(rnd.randint(1, 12))]
+        numel = sum(units)
+        split = z.zero_init_shards(numel, world, 3, "bf16", units=units)
+        lay3 = make_layout(numel, world, 3, units)
+        owners = [rnd.randrange(world) for _ in units]
+        own = z.zero_init_shards(numel, world, z.ZSMR_ZERO3_OWNER, "bf16", units=units)
+        z.zero_set_unit_owners(own, owners)
+        lay4 = make_layout(numel, world, 3, units, owner_broadcast=True, owners=owners)
+        for ml in range(1, len(units) + 3):
+            got = z.zero_bytes_per_rank(split, 2, ml)
+            want = acc.bytes_per_rank(lay3, max_live=ml)
+            assert got == {k: getattr(want, k) for k in got}, (units, ml)
+            for r in range(world):
+                got = z.zero_bytes_of_rank(own, r, 4, ml)
+                want = acc.bytes_per_rank(lay4, gather_bytes=4, max_live=ml, rank=r)
+                assert got == {k: getattr(want, k) for k in got}, (units, owners, r, ml)
+
+
+def test_peak_of_many_units_is_one_pass():
+    """2^20 units (the most a context takes) with half of them live at once:
+    the accounting is one pass over the units, not one per window."""
+    import time
+    n_units = 1 << 20
+    units = [1 + (u % 7) for u in range(n_units)]
+    ctx = z.zero_init_shards(sum(units), 2, z.ZSMR_ZERO3_OWNER, "bf16", units=units)
+    t0 = time.perf_counter()
+    b = z.zero_bytes_per_rank(ctx, 2, n_units // 2)
+    assert time.perf_counter() - t0 < 5.0
+    assert b["gathered"] > 0

@@ -143,6 +143,22 @@ void assign_owners(zsmr_ctx* c) {
     c->shard_total = *std::max_element(c->own.begin(), c->own.end());
 }
 
+// The largest sum of size(u) over max_live consecutive units (all of them if
+// there are fewer): the most a rank holds gathered at once when units are
+// gathered in order and at most max_live are live.  One pass, a running sum
+// over the window.
+template <typename F>
+int64_t most_in_window(int64_t n_units, int64_t max_live, F size) {
+    const int64_t k = max_live < n_units ? max_live : n_units;
+    int64_t best = 0, sum = 0;
+    for (int64_t j = 0; j < n_units; ++j) {
+        sum += size(j);
+        if (j >= k) sum -= size(j - k);
+        if (j >= k - 1 && sum > best) best = sum;
+    }
+    return best;
+}
+
 // Counting of one cast of (rank, unit): at stages 1-2 the all-gather delivers
 // the rank's slot to every other rank; DP and stage 3 cast locally.
 void count_cast(zsmr_ctx* c, int32_t rank, int64_t len) {
@@ -324,13 +340,9 @@ void owner_bytes(const zsmr_ctx* c, int32_t rank, int64_t gather_bytes, int64_t 
     o->res_v = 4 * own;
     o->resident = 16 * own;
     const int64_t nu = (int64_t)c->units.size();
-    const int64_t k = max_live < nu ? max_live : nu;
-    int64_t best = 0, widest = 0;
-    for (int64_t i = 0; i + k <= nu; ++i) {
-        int64_t sum = 0;
-        for (int64_t j = i; j < i + k; ++j) sum += c->owners[j] == rank ? 0 : c->units[j];
-        best = sum > best ? sum : best;
-    }
+    auto borrowed = [&](int64_t u) { return c->owners[u] == rank ? int64_t(0) : c->units[u]; };
+    const int64_t best = most_in_window(nu, max_live, borrowed);
+    int64_t widest = 0;
     for (int64_t u : c->units) widest = u > widest ? u : widest;
     o->gathered = gather_bytes * best;
     o->unit_grad = 2 * widest;
@@ -359,13 +371,8 @@ void even_bytes(const zsmr_ctx* c, int64_t gather_bytes, int64_t max_live, zsmr_
     o->resident = o->res_p16 + o->res_grad + o->res_master + o->res_m + o->res_v;
     if (c->stage == ZSMR_ZERO3) {
         const int64_t nu = (int64_t)c->shard_u.size();
-        const int64_t k = max_live < nu ? max_live : nu;
-        int64_t best = 0, widest = 0;
-        for (int64_t i = 0; i + k <= nu; ++i) {
-            int64_t sum = 0;
-            for (int64_t j = i; j < i + k; ++j) sum += w * c->shard_u[j];
-            best = sum > best ? sum : best;
-        }
+        const int64_t best = most_in_window(nu, max_live, [&](int64_t u) { return w * c->shard_u[u]; });
+        int64_t widest = 0;
         for (int64_t su : c->shard_u) widest = w * su > widest ? w * su : widest;
         o->gathered = gather_bytes * best;
         o->unit_grad = 2 * widest;
