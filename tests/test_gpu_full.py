@@ -121,6 +121,53 @@ def test_rank_share_full_size(rank):
     free()
 
 
+# The corners of the space bench.py's window tuner searches (cycle, write,
+# margin, lead in ns): cycles 62-82 us, write windows 9-11 us, leads 2-4 us.
+TUNER_CORNERS = [(62000, 9000, 1000, 2000), (62000, 11000, 1000, 4000),
+                 (82000, 9000, 1000, 4000), (82000, 11000, 1000, 2000)]
+
+
+def test_share64_tuner_windows_give_the_default_bits():
+    """The full share64 fused step (117,187,500 elements, 64 rows, about 38
+    write windows) at the corners of the tuner's search space stores the
+    same bits as at the library's default window, which the full-vector
+    test checks against the oracle on every element: the window the bench
+    picks on a device changes only when results are stored."""
+    w = wl.WORKLOADS["share64"]
+    say("[full] share64 fused step at the tuner's corner windows")
+    share = wl.RankShare(w, rank=5)
+    start = [x.clone() for x in (share.master, share.m, share.v)]
+    own = share.wc[share.off:share.off + share.S]
+    share.gen_grads(1)
+
+    def run(window):
+        for x, x0 in zip((share.master, share.m, share.v), start):
+            x.copy_(x0)
+        own.zero_()
+        z.zsmr_set_write_window(*window)
+        try:
+            plan = z.zsmr_fused_step_plan(share.ctx, share.rank, 0, share.grads, share.row_stride, 0,
+                                          share.master, share.m, share.v, own)
+            assert plan["kernel"] == "deferred" and plan["windowed"], plan
+            share.fused(1)
+            torch.cuda.synchronize()
+        finally:
+            z.zsmr_set_write_window()
+        return [x.clone() for x in (share.master, share.m, share.v, own)]
+
+    ref = run(z.WRITE_WINDOW_DEFAULT)
+    for window in TUNER_CORNERS:
+        got = run(window)
+        for name, a, b in zip(("master", "m", "v", "p16"), ref, got):
+            ai = a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16)
+            bi = b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16)
+            assert torch.equal(ai, bi), f"window {window}: {name} differs"
+        say(f"[full] window {window}: same bits as the default")
+        del got
+    del share, start, ref, own
+    free()
+
+
 @pytest.mark.parametrize("rank", [0, 63])
 def test_bucketed_step_full_size(rank):
     """The share64 step as ``bench.py --buckets 8`` runs it (each bucket's
