@@ -397,7 +397,9 @@ int32_t zsmr_fused_step_plan(const zsmr_ctx* ctx, int32_t rank, int32_t unit, co
  * 16 rows or with windows off, at most 2; with windows and at most 3, two
  * workgroups run per CU).  defer_min_rows >= 1 (default 24): the fewest
  * gradient rows for which the fused step defers its writes.
- * Process-wide.  Affects speed only, never results. */
+ * Process-wide; safe to call while other threads launch (each value is read
+ * atomically, and a launch that overlaps the call may take some values old
+ * and some new).  Affects speed only, never results. */
 int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                               int32_t defer_min_rows);
 
@@ -418,8 +420,9 @@ int32_t zsmr_set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_
  * write_ns + margin_ns < cycle_ns and 0 <= lead_ns < write_ns; ZSMR_ERR_ARG
  * if not.  Defaults: 72,000 / 11,000 / 1,000 / 4,000.  The best cycle follows
  * the device's read rate (it is the time the rings take to fill), so a
- * caller that can time the step may tune it.  Process-wide.  Affects speed
- * only, never results. */
+ * caller that can time the step may tune it.  Process-wide; safe to call
+ * while other threads launch, and a launch sees either all four old values
+ * or all four new ones.  Affects speed only, never results. */
 int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin_ns,
                               int32_t lead_ns);
 
@@ -431,8 +434,8 @@ int32_t zsmr_set_write_window(int32_t cycle_ns, int32_t write_ns, int32_t margin
  * faster than the odd ones, so equal shares leave them idle at the end of a
  * copy.  500 <= even_permille <= 2000 (1000: equal shares), else
  * ZSMR_ERR_ARG.  Default 1200, the best measured for the 14.77 GB receive of
- * one rank's share of a 64-rank world.  Process-wide.  Affects speed only,
- * never results. */
+ * one rank's share of a 64-rank world.  Process-wide; safe to call while
+ * other threads launch.  Affects speed only, never results. */
 int32_t zsmr_set_xcd_balance(int32_t even_permille);
 
 #ifdef __cplusplus

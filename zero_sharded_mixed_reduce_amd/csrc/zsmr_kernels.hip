@@ -20,6 +20,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "zsmr.h"
 #include "zsmr_launch.h"
 
@@ -72,16 +75,16 @@ constexpr int kCopyUnroll = ZSMR_COPY_UNROLL;
 // tile per wave against 2 per CU grid-stride: 4 rows 5.89 against 5.28
 // TB/s, 8 rows 5.87-5.91 against 5.53, 12 rows 6.14-6.19 against 5.45;
 // GPT-2 small's 15.5M-element shard at 8 rows 6.05-6.09 against 5.62-5.69.
-int g_step_bpc = 0;
+std::atomic<int> g_step_bpc{0};
 constexpr int kNarrowCopyBpc = 4;   // the 2-byte copies: 4 per CU
 // The burst copies (receive and ZeRO-3 gather), measured the same way: a
 // 14.77 GB copy between fresh buffers, one burst per wave 6.22 TB/s against
 // 6.07 grid-stride at 1 per CU; the share64 receive 6.00-6.03 against
 // 5.82-5.84 (2 per CU 5.84-5.86, 4 per CU 5.94-5.96).
-int g_copy_bpc = 0;
+std::atomic<int> g_copy_bpc{0};
 // The copies' share of regions for each even-numbered XCD against each odd
 // one, in thousandths (the measurements are beside XcdSplit below).
-int g_xcd_even_permille = 1200;
+std::atomic<int> g_xcd_even_permille{1200};
 // the fused step's deferred-write kernel: tiles kept in LDS per wave with
 // write windows (0 = write at once with step_vec8_kernel).  With windows and
 // a ring of at most 3 tiles (72 KB per workgroup), two workgroups run per CU
@@ -89,7 +92,7 @@ int g_xcd_even_permille = 1200;
 // its Adam tail.  Measured on MI355X, share64, per step: 3 tiles x 2
 // workgroups 2.78 ms, 2 x 2 2.85 ms, 5 x 1 3.07 ms; without windows one
 // workgroup per CU is 5% faster (16-24 rows).
-int g_defer_tiles = 3;
+std::atomic<int> g_defer_tiles{3};
 constexpr int kRingTwoPerCu = 3;
 // ... used when a step reduces at least this many rows.  Measured on MI355X,
 // one box, 97,375,000 elements, against the direct kernel with one tile per
@@ -97,7 +100,7 @@ constexpr int kRingTwoPerCu = 3;
 // 5.90-5.99, 24 rows 5.99-6.09 against 5.66-5.69, 32 rows 6.12-6.15 against
 // 5.48-5.50, 64 rows 6.05 against 5.29; the 1.558e9-element, 16-rank world
 // 16.94 against 15.96-15.99 ms per step.
-int g_defer_min_rows = 24;
+std::atomic<int> g_defer_min_rows{24};
 // without windows the ring holds at most this many tiles: smaller bursts at
 // ring-full beat larger ones (8-24 rows: 2 tiles up to 5% faster than 5)
 constexpr int kRingWithoutWindows = 2;
@@ -110,10 +113,13 @@ constexpr int kRingWithoutWindows = 2;
 // the device's read rate, so callers that can time the step may tune it;
 // the default is the window a tuning over 31 candidates picked on three
 // boxes of three (72 / 11 / 1 / 4 us, 2.70-2.72 ms per step).
-int64_t g_window_cycle_ns = 72000;
-int64_t g_window_write_ns = 11000;
-int64_t g_window_margin_ns = 1000;
-int64_t g_window_lead_ns = 4000;
+struct WindowNs {
+    int64_t cycle, write, margin, lead;
+};
+WindowNs g_window_ns{72000, 11000, 1000, 4000};
+// the four values change together: a launch reads them under this lock, so
+// it never sees half of a new window
+std::mutex g_window_lock;
 // The cycle as set is the one for 64 rows of 16-bit gradients.  A wave's
 // ring fills in a time proportional to the bytes its tiles move per element
 // (2 * rows + 26: the gradient rows, master, m and v read and written, the
@@ -852,15 +858,16 @@ __global__ __launch_bounds__(kThreads) void gather16_kernel(GatherArgs g, XcdSpl
 
 // ------------------------------------------------------------------ host --
 int cu_count() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+    if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed))
+        return cache[dev].load(std::memory_order_relaxed);
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
@@ -879,7 +886,7 @@ unsigned grid_for(int64_t work_items, int bpc) {
 // workgroups that cover the largest share on every XCD.
 XcdSplit xcd_split(int64_t regions, unsigned* grid) {
     XcdSplit sp{};
-    const int64_t we = g_xcd_even_permille, wo = 1000, wsum = (kXcds / 2) * (we + wo);
+    const int64_t we = g_xcd_even_permille.load(std::memory_order_relaxed), wo = 1000, wsum = (kXcds / 2) * (we + wo);
     int64_t given = 0;
     for (uint32_t x = 0; x < kXcds; ++x) {
         sp.count[x] = regions * (x % 2 == 0 ? we : wo) / wsum;
@@ -909,14 +916,17 @@ int dst_vec(const void* p) {
 // ticks of the s_memrealtime clock per second on the current device (0 if
 // the runtime does not say: then no windows)
 int64_t clock_hz() {
-    static int64_t cache[64] = {0};
+    static std::atomic<int64_t> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] > 0 ? cache[dev] : 0;
+    if (dev >= 0 && dev < 64) {
+        const int64_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c) return c > 0 ? c : 0;
+    }
     int khz = 0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) khz = 0;
     const int64_t hz = khz > 0 ? (int64_t)khz * 1000 : -1;
-    if (dev >= 0 && dev < 64) cache[dev] = hz;
+    if (dev >= 0 && dev < 64) cache[dev].store(hz, std::memory_order_relaxed);
     return hz > 0 ? hz : 0;
 }
 
@@ -924,14 +934,19 @@ int64_t clock_hz() {
 // per element, at most 2^30 ticks)
 Window window_ticks(int32_t rows) {
     Window w{0, 0, 0, 0};
+    WindowNs ns;
+    {
+        std::lock_guard<std::mutex> hold(g_window_lock);
+        ns = g_window_ns;
+    }
     const int64_t hz = clock_hz();
-    if (!g_window_cycle_ns || !hz || rows < 1) return w;
-    auto ticks = [&](int64_t ns) { return static_cast<uint32_t>(ns * hz / 1000000000); };
-    const int64_t cycle = int64_t(ticks(g_window_cycle_ns)) * (2 * int64_t(rows) + 26) / kWindowRefBytes;
+    if (!ns.cycle || !hz || rows < 1) return w;
+    auto ticks = [&](int64_t t) { return static_cast<uint32_t>(t * hz / 1000000000); };
+    const int64_t cycle = int64_t(ticks(ns.cycle)) * (2 * int64_t(rows) + 26) / kWindowRefBytes;
     w.cycle = static_cast<uint32_t>(cycle < kMaxCycleTicks ? cycle : kMaxCycleTicks);
-    w.write = ticks(g_window_write_ns);
-    w.margin = ticks(g_window_margin_ns);
-    w.lead = ticks(g_window_lead_ns);
+    w.write = ticks(ns.write);
+    w.margin = ticks(ns.margin);
+    w.lead = ticks(ns.lead);
     if (w.write < 1 || w.write + w.margin >= w.cycle || w.lead >= w.write) w = Window{0, 0, 0, 0};
     return w;
 }
@@ -975,11 +990,11 @@ hipError_t launch_mode(const StepArgs& a, const Plan& p, hipStream_t s) {
         }
     }
     if (p.kernel == K_SCALAR) {
-        hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n, g_step_bpc)), dim3(kThreads),
+        hipLaunchKernelGGL((step_scalar_kernel<GDT, PDT, MODE>), dim3(grid_for(a.n, g_step_bpc.load(std::memory_order_relaxed))), dim3(kThreads),
                            0, s, a);
         return hipGetLastError();
     }
-    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc));
+    const dim3 grid(grid_for(vec_elems(a.n) >> 3, g_step_bpc.load(std::memory_order_relaxed)));
     if constexpr ((MODE & M_REDUCE) != 0) {
         if (p.rb == kRowBatchWide) {
             switch (p.dv) {
@@ -1009,21 +1024,19 @@ hipError_t launch_dt(int gdt, int pdt, const StepArgs& a, const Plan& p, hipStre
 
 }  // namespace
 
-void set_xcd_balance(int32_t even_permille) { g_xcd_even_permille = even_permille; }
+void set_xcd_balance(int32_t even_permille) { g_xcd_even_permille.store(even_permille, std::memory_order_relaxed); }
 
 void set_launch_shape(int32_t step_bpc, int32_t copy_bpc, int32_t defer_tiles,
                       int32_t defer_min_rows) {
-    g_step_bpc = step_bpc;
-    g_copy_bpc = copy_bpc;
-    g_defer_tiles = defer_tiles;
-    g_defer_min_rows = defer_min_rows;
+    g_step_bpc.store(step_bpc, std::memory_order_relaxed);
+    g_copy_bpc.store(copy_bpc, std::memory_order_relaxed);
+    g_defer_tiles.store(defer_tiles, std::memory_order_relaxed);
+    g_defer_min_rows.store(defer_min_rows, std::memory_order_relaxed);
 }
 
 void set_write_window(int64_t cycle_ns, int64_t write_ns, int64_t margin_ns, int64_t lead_ns) {
-    g_window_cycle_ns = cycle_ns;
-    g_window_write_ns = write_ns;
-    g_window_margin_ns = margin_ns;
-    g_window_lead_ns = lead_ns;
+    std::lock_guard<std::mutex> hold(g_window_lock);
+    g_window_ns = WindowNs{cycle_ns, write_ns, margin_ns, lead_ns};
 }
 
 namespace {
@@ -1098,11 +1111,13 @@ Plan plan_for(int mode, const StepArgs& a) {
         p.kernel = K_SCALAR;
         return p;
     }
-    if (mode == (M_REDUCE | M_ADAM | M_CAST) && g_defer_tiles > 0 && a.nrows >= g_defer_min_rows &&
-        al(a.grads, 16) && a.row_stride % 8 == 0) {
+    const int tiles = g_defer_tiles.load(std::memory_order_relaxed);
+    if (mode == (M_REDUCE | M_ADAM | M_CAST) && tiles > 0 &&
+        a.nrows >= g_defer_min_rows.load(std::memory_order_relaxed) && al(a.grads, 16) &&
+        a.row_stride % 8 == 0) {
         p.kernel = K_DEFERRED;
         p.win = a.nrows >= kWindowMinRows ? window_ticks(a.nrows) : Window{0, 0, 0, 0};
-        p.kd = p.win.cycle || g_defer_tiles < kRingWithoutWindows ? g_defer_tiles : kRingWithoutWindows;
+        p.kd = p.win.cycle || tiles < kRingWithoutWindows ? tiles : kRingWithoutWindows;
     }
     return p;
 }
@@ -1155,7 +1170,7 @@ hipError_t launch_copy16(const uint16_t* src, uint16_t* dst, int64_t n, hipStrea
     const int64_t head = head_for(dst, w, n);
     const int64_t pre = pre_for(dst, w, head);
     const int64_t vecs = (n - head) / (w / 2) + 1;
-    const int64_t regions = w >= 4 ? grid_for((vecs + pre) / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc)
+    const int64_t regions = w >= 4 ? grid_for((vecs + pre) / (ZSMR_COPY_BURST_BYTES / w) + 1, g_copy_bpc.load(std::memory_order_relaxed))
                                    : grid_for(vecs, kNarrowCopyBpc);
     unsigned gx = 0;
     const XcdSplit sp = xcd_split(regions, &gx);
@@ -1178,7 +1193,7 @@ hipError_t launch_copy_blocks(const uint16_t* src, uint16_t* dst, int64_t n, int
     const int64_t per = n / (w / 2) + 1 + pre_max;
     const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
     int64_t regions = (units + kThreads - 1) / kThreads;   // of each block
-    const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
+    const int bpc = w >= 4 ? g_copy_bpc.load(std::memory_order_relaxed) : kNarrowCopyBpc;
     if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all blocks
         const int64_t cap = (int64_t)cu_count() * bpc;
         const int64_t lim = cap / count > 0 ? cap / count : 1;
@@ -1221,7 +1236,7 @@ hipError_t launch_gather16(const uint16_t* const* srcs, int32_t nsrc, int64_t ea
         const int64_t per = each / (w / 2) + 1 + pre_max;
         const int64_t units = w >= 4 ? per / (ZSMR_COPY_BURST_BYTES / w) + 1 : per;   // lanes' work
         int64_t regions = (units + kThreads - 1) / kThreads;   // of each source
-        const int bpc = w >= 4 ? g_copy_bpc : kNarrowCopyBpc;
+        const int bpc = w >= 4 ? g_copy_bpc.load(std::memory_order_relaxed) : kNarrowCopyBpc;
         if (bpc > 0) {   // a grid-stride grid: bpc workgroups per CU over all sources
             const int64_t cap = (int64_t)cu_count() * bpc;
             const int64_t lim = cap / cnt > 0 ? cap / cnt : 1;
