@@ -214,8 +214,7 @@ def _rows_fit(ctx, grads, row_stride: int, base: int, end: int, what: str) -> No
     """The N gradient rows: row r covers [base + r*row_stride, ... + end)."""
     if grads is None or isinstance(grads, int) or end <= 0:
         return
-    world = zero_layout_info(ctx)["world"]
-    _fits(grads, int(base) + (world - 1) * max(int(row_stride), 0) + end, 2, what)
+    _fits(grads, int(base) + (ctx.world - 1) * max(int(row_stride), 0) + end, 2, what)
 
 
 def _stream(stream) -> Optional[int]:
@@ -236,6 +235,14 @@ class Ctx:
 
     def __init__(self, handle: int):
         self.handle = handle
+        self._world = None
+
+    @property
+    def world(self) -> int:
+        """N, fixed when the context is made (read once, then kept)."""
+        if self._world is None:
+            self._world = zero_layout_info(self)["world"]
+        return self._world
 
     def close(self):
         if self.handle:
