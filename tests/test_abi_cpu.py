@@ -284,6 +284,21 @@ def test_write_window_arguments():
     z.zsmr_set_write_window()                 # back to the defaults
 
 
+def test_context_world_is_kept():
+    """The binding reads N once per context and keeps it for its row-size
+    checks; it equals what the library reports, and a short gradient
+    buffer is still refused before any call."""
+    import torch
+    for world in (1, 4, 64):
+        ctx = z.zero_init_shards(64 * world, world, 2, "bf16")
+        assert ctx.world == z.zero_layout_info(ctx)["world"] == world
+        g = torch.empty(64 * world, dtype=torch.bfloat16)
+        if world > 1:
+            with pytest.raises(ValueError):
+                z._rows_fit(ctx, g, 64 * world, 0, 64, "grads")   # rows of stride Psi overrun the buffer
+        z._rows_fit(ctx, g, 64, 0, 64, "grads")                   # N rows of stride 64 fit
+
+
 def test_xcd_balance_arguments():
     for bad in (0, 499, 2001, -1000):
         with pytest.raises(z.ZsmrError) as e:
